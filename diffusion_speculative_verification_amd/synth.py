@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the speculative verification step.
+
+This module only draws random numbers and lays them out; it holds none of the
+verification arithmetic (no RoPE, no mask, no attention, no acceptance).  Both
+the CPU oracle's tests and the GPU path draw their inputs from here.
+
+Workloads follow the block-diffusion verification setting of SimSD
+("SimSD: Simple Speculative Decoding in Diffusion Language Models",
+sections "数据-掩码配对布局" and "投机拒绝采样"): a cached prompt of P tokens,
+a response block of B data slots D followed by B mask slots, a permutation tau
+of step labels, and per-slot target logits / draft distributions over a vocab.
+
+Recipe (per sequence b, tensor id t, case seed s; generator =
+numpy default_rng(SeedSequence([s, t, b]))):
+  t=0 Q      [2B][Hq][d]   iid N(0,1)          (pre-RoPE)
+  t=1 K_new  [2B][Hkv][d]  iid N(0,1)          (pre-RoPE)
+  t=2 V_new  [2B][Hkv][d]  iid N(0,1)
+  t=3 K_cache[Hkv][P][d]   iid N(0,1)          (taken as already rotated: an
+      orthogonal rotation of an iid standard normal vector is again iid
+      standard normal, so this has the law of rotated raw keys)
+  t=4 V_cache[Hkv][P][d]   iid N(0,1)
+  t=5 tau    [B]           uniform permutation of 1..B (identity for every
+      `identity_every`-th sequence, 0-based b % k == k-1)
+  t=6 target logits [B][V] N(0, var_t)
+  t=7 draft logits  [B][V] iid model: N(0, var_d) independent of the target;
+      perturb model: target + N(0, 1)
+  t=8 draft sampling uniforms [B]
+  t=9 acceptance/resample uniforms [gamma+1]  U[0,1) fp32
+bf16 cases round Q/K/V and the caches to bf16 (round-to-nearest-even) and keep
+them as float32 arrays holding exactly bf16-representable values.
+
+The synthetic drafter: p_phi = softmax(draft logits) computed in float64 and
+stored as float32; each draft token is drawn from the float64 p_phi by
+inverse CDF with its own uniform.  This is input synthesis (the drafter is not
+part of the verification step).
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = ["Case", "CONFIGS", "make_inputs", "round_bf16", "config_by_name"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Case:
+    name: str
+    batch: int
+    prefix_len: int
+    block: int
+    gamma: int
+    n_qh: int
+    n_kvh: int
+    head_dim: int
+    vocab: int
+    dtype: str  # "f32" or "bf16"
+    theta: float
+    logit_model: str  # "iid" or "perturb"
+    target_var: float
+    draft_var: float = 1.0
+    identity_every: int = 0
+    seed: int = 0
+
+    @property
+    def rows(self) -> int:
+        return 2 * self.block
+
+    def with_(self, **kw) -> "Case":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the verification step (block sizes, prefix lengths,
+# head counts and vocab of the block-diffusion setting; sizes as stated).
+CONFIGS = [
+    Case("tiny", 1, 32, 8, 8, 4, 4, 64, 512, "f32", 1e4, "iid", 2.0, 2.0, 0, seed=0),
+    Case("small", 8, 512, 16, 16, 32, 8, 128, 151936, "bf16", 1e6, "perturb", 3.0, 1.0, 0, seed=1),
+    Case("headline", 32, 2048, 32, 32, 32, 8, 128, 151936, "bf16", 1e6, "perturb", 3.0, 1.0, 0, seed=2),
+    Case("longprefix", 4, 16384, 32, 32, 32, 8, 128, 151936, "bf16", 1e6, "perturb", 3.0, 1.0, 0, seed=3),
+    Case("wide", 64, 4096, 64, 64, 64, 8, 128, 151936, "bf16", 1e6, "perturb", 3.0, 1.0, 8, seed=4),
+]
+
+
+def config_by_name(name: str) -> Case:
+    for c in CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def _rng(case: Case, tensor_id: int, b: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([case.seed, tensor_id, b]))
+
+
+def _normal(case: Case, tensor_id: int, b: int, shape) -> np.ndarray:
+    x = _rng(case, tensor_id, b).standard_normal(shape, dtype=np.float32)
+    return round_bf16(x) if case.dtype == "bf16" else x
+
+
+def _tau(case: Case, b: int) -> np.ndarray:
+    if case.identity_every and (b % case.identity_every) == case.identity_every - 1:
+        return np.arange(1, case.block + 1, dtype=np.int32)
+    return (_rng(case, 5, b).permutation(case.block) + 1).astype(np.int32)
+
+
+def _logits_and_draft(case: Case, b: int, want_logits: bool = True):
+    B, V = case.block, case.vocab
+    tgt = _rng(case, 6, b).standard_normal((B, V), dtype=np.float64) * np.sqrt(case.target_var)
+    noise = _rng(case, 7, b).standard_normal((B, V), dtype=np.float64)
+    if case.logit_model == "perturb":
+        drf = tgt + noise * np.sqrt(case.draft_var)
+    else:
+        drf = noise * np.sqrt(case.draft_var)
+    tgt32 = tgt.astype(np.float32)
+    # synthetic drafter: its distribution and its sampled tokens
+    drf -= drf.max(axis=1, keepdims=True)
+    np.exp(drf, out=drf)
+    drf /= drf.sum(axis=1, keepdims=True)
+    probs32 = drf.astype(np.float32)
+    u = _rng(case, 8, b).random(B)
+    np.cumsum(drf, axis=1, out=drf)
+    tok = np.empty(B, dtype=np.int32)
+    for k in range(B):
+        t = int(np.searchsorted(drf[k], u[k] * drf[k, -1], side="right"))
+        tok[k] = min(t, V - 1)
+    return tgt32, probs32, tok
+
+
+def _uniforms(case: Case, b: int) -> np.ndarray:
+    return _rng(case, 9, b).random(case.gamma + 1, dtype=np.float32)
+
+
+def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | None = None) -> dict:
+    """Generate the inputs of `case` for sequences `seqs` (default: all).
+
+    Returns a dict of float32/int32 numpy arrays with a leading batch axis:
+    q [n][2B][Hq][d], k_new/v_new [n][2B][Hkv][d], k_cache/v_cache
+    [n][Hkv][P][d], tau [n][B], target_logits/draft_probs [n][B][V],
+    draft_tokens [n][B], uniforms [n][gamma+1].
+    """
+    seqs = list(range(case.batch)) if seqs is None else list(seqs)
+    n = len(seqs)
+    B, R, P, d = case.block, case.rows, case.prefix_len, case.head_dim
+    out = {"tau": np.stack([_tau(case, b) for b in seqs]) if n else np.zeros((0, B), np.int32)}
+    if threads is None:
+        threads = max(1, min(8, os.cpu_count() or 1))
+    if "attn" in parts:
+        out["q"] = np.empty((n, R, case.n_qh, d), np.float32)
+        out["k_new"] = np.empty((n, R, case.n_kvh, d), np.float32)
+        out["v_new"] = np.empty((n, R, case.n_kvh, d), np.float32)
+        out["k_cache"] = np.empty((n, case.n_kvh, P, d), np.float32)
+        out["v_cache"] = np.empty((n, case.n_kvh, P, d), np.float32)
+
+        def fill_attn(i):
+            b = seqs[i]
+            out["q"][i] = _normal(case, 0, b, (R, case.n_qh, d))
+            out["k_new"][i] = _normal(case, 1, b, (R, case.n_kvh, d))
+            out["v_new"][i] = _normal(case, 2, b, (R, case.n_kvh, d))
+            out["k_cache"][i] = _normal(case, 3, b, (case.n_kvh, P, d))
+            out["v_cache"][i] = _normal(case, 4, b, (case.n_kvh, P, d))
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill_attn, range(n)))
+    if "accept" in parts:
+        V = case.vocab
+        out["target_logits"] = np.empty((n, B, V), np.float32)
+        out["draft_probs"] = np.empty((n, B, V), np.float32)
+        out["draft_tokens"] = np.empty((n, B), np.int32)
+        out["uniforms"] = np.empty((n, case.gamma + 1), np.float32)
+
+        def fill_acc(i):
+            b = seqs[i]
+            t, p, k = _logits_and_draft(case, b)
+            out["target_logits"][i] = t
+            out["draft_probs"][i] = p
+            out["draft_tokens"][i] = k
+            out["uniforms"][i] = _uniforms(case, b)
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill_acc, range(n)))
+    return out

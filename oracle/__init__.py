@@ -1,0 +1,186 @@
+"""CPU oracle for the speculative verification step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check (``__graft_entry__.smoke``) and
+the benchmark's ``cpu_baseline`` leg may import this package.  The product
+path (the HIP library and its Python binding) never imports, links or runs
+anything here, and nothing here imports the product package.
+
+Thin ctypes wrapper over ``svo.c`` (plain C, float64, OpenMP over independent
+rows).  Every C function cites the passage it follows.  Parity is pinned by
+``tests/test_oracle_*.py`` against facts the pages and mathematics fix
+(invariants, closed forms, brute force on tiny inputs, special cases, hand
+fixtures under ``tests/golden/``); ``tests/test_oracle_mutants.py`` plants
+plausible mistakes in copies of ``svo.c`` and checks that a pin fails for each.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "svo.c")
+LIB = os.path.join(_HERE, "libsvo.so")
+_lock = threading.Lock()
+_default = None
+
+
+def gcc_cmd(src: str, out: str) -> list:
+    return ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+            "-shared", "-fPIC", src, "-o", out, "-lm"]
+
+
+def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
+    """Compile svo.c (or another copy) into a shared library with gcc."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.run(gcc_cmd(src, tmp), check=True)
+        os.replace(tmp, out)
+    return out
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def _check(rc):
+    if rc == -1:
+        raise OracleError("tau is not a permutation of 1..B")
+    if rc:
+        raise OracleError(f"oracle rejected the arguments (code {rc})")
+
+
+class Oracle:
+    """ctypes handle on one build of svo.c (the default build, or another
+    library path, e.g. a deliberately broken copy built by a test)."""
+
+    def __init__(self, path: str | None = None):
+        if path is None:
+            build(force=False)
+            path = LIB
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.svo_mask.argtypes = [i32, i32, P, P]
+        lib.svo_rope.argtypes = [P, i64, i32, i32, P, dbl]
+        lib.svo_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, dbl, dbl, P]
+        lib.svo_softmax.argtypes = [P, i64, P, P, P]
+        lib.svo_residual.argtypes = [P, P, i64, dbl, P, P, P]
+        lib.svo_residual.restype = i64
+        lib.svo_accept.argtypes = [P, P, P, P, P, i32, i32, i32, i64, P, P, P, P]
+        lib.svo_set_threads.argtypes = [i32]
+        self.lib = lib
+
+    def set_threads(self, n: int) -> None:
+        self.lib.svo_set_threads(int(n))
+
+    def max_threads(self) -> int:
+        return int(self.lib.svo_max_threads())
+
+    def mask(self, tau, P: int) -> np.ndarray:
+        """Temporal-causal mask A (SimSD 关键设计 2): uint8 [2B][P+2B]."""
+        tau = _c(tau, np.int32)
+        B = tau.shape[0]
+        M = np.empty((2 * B, P + 2 * B), np.uint8)
+        _check(self.lib.svo_mask(B, P, _p(tau), _p(M)))
+        return M
+
+    def rope(self, x, pos, theta: float) -> np.ndarray:
+        """Rotate-half RoPE (SimSD 关键设计 3) of x[n][heads][d] (or [n][d]) at pos[n]."""
+        x = np.array(x, dtype=np.float64, copy=True)
+        shp = x.shape
+        if x.ndim == 2:
+            x = x[:, None, :]
+        n, h, d = x.shape
+        pos = _c(pos, np.float64)
+        assert pos.shape == (n,)
+        self.lib.svo_rope(_p(x), n, h, d, _p(pos), float(theta))
+        return x.reshape(shp)
+
+    def attention(self, q, k_new, v_new, k_cache, v_cache, tau, theta: float,
+                  scale: float = 0.0) -> np.ndarray:
+        """Masked attention of one sequence's 2B response rows -> float64 [2B][Hq][d].
+
+        q [2B][Hq][d], k_new/v_new [2B][Hkv][d] (pre-RoPE when theta > 0),
+        k_cache/v_cache [Hkv][P][d] (prompt keys already rotated), tau [B].
+        """
+        q, k_new, v_new = _c(q, np.float32), _c(k_new, np.float32), _c(v_new, np.float32)
+        k_cache, v_cache, tau = _c(k_cache, np.float32), _c(v_cache, np.float32), _c(tau, np.int32)
+        R, Hq, d = q.shape
+        B = tau.shape[0]
+        assert R == 2 * B
+        Hkv, P = k_cache.shape[0], k_cache.shape[1]
+        assert k_new.shape == (R, Hkv, d) and v_new.shape == (R, Hkv, d)
+        assert k_cache.shape == (Hkv, P, d) and v_cache.shape == (Hkv, P, d)
+        out = np.empty((R, Hq, d), np.float64)
+        _check(self.lib.svo_attn(_p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(tau),
+                                 B, P, Hq, Hkv, d, float(theta), float(scale), _p(out)))
+        return out
+
+    def softmax(self, l):
+        """Float64 softmax of one logits row -> (p, m, s)."""
+        l = _c(l, np.float32)
+        p = np.empty(l.shape[0], np.float64)
+        m = np.zeros(1, np.float64)
+        s = np.zeros(1, np.float64)
+        self.lib.svo_softmax(_p(l), l.shape[0], _p(p), _p(m), _p(s))
+        return p, float(m[0]), float(s[0])
+
+    def residual(self, l, pphi, u: float):
+        """Residual resample of one slot -> (token, cdf[V], total mass, used_target)."""
+        l, pphi = _c(l, np.float32), _c(pphi, np.float32)
+        V = l.shape[0]
+        cdf = np.empty(V, np.float64)
+        Z = np.zeros(1, np.float64)
+        ut = np.zeros(1, np.int32)
+        tok = self.lib.svo_residual(_p(l), _p(pphi), V, float(u), _p(cdf), _p(Z), _p(ut))
+        return int(tok), cdf, float(Z[0]), bool(ut[0])
+
+    def accept(self, logits, probs, tokens, tau, u, gamma: int):
+        """Acceptance + resample for a batch (SimSD 关键设计 4).
+
+        logits/probs [n][B][V], tokens/tau [n][B], u [n][gamma+1].
+        Returns (accept_len[n], out_tokens[n][B], alpha[n][gamma] float64,
+        resample_slot[n]).
+        """
+        logits, probs = _c(logits, np.float32), _c(probs, np.float32)
+        tokens, tau, u = _c(tokens, np.int32), _c(tau, np.int32), _c(u, np.float32)
+        n, B, V = logits.shape
+        assert probs.shape == (n, B, V) and tokens.shape == (n, B) and tau.shape == (n, B)
+        assert u.shape == (n, gamma + 1)
+        L = np.empty(n, np.int32)
+        ot = np.empty((n, B), np.int32)
+        al = np.empty((n, gamma), np.float64)
+        rs = np.empty(n, np.int32)
+        _check(self.lib.svo_accept(_p(logits), _p(probs), _p(tokens), _p(tau), _p(u), n, B, gamma,
+                                   V, _p(L), _p(ot), _p(al), _p(rs)))
+        return L, ot, al, rs
+
+
+def default() -> Oracle:
+    global _default
+    with _lock:
+        if _default is None:
+            _default = Oracle()
+    return _default
+
+
+def set_threads(n): return default().set_threads(n)
+def max_threads(): return default().max_threads()
+def mask(tau, P): return default().mask(tau, P)
+def rope(x, pos, theta): return default().rope(x, pos, theta)
+def attention(*a, **k): return default().attention(*a, **k)
+def softmax(l): return default().softmax(l)
+def residual(l, pphi, u): return default().residual(l, pphi, u)
+def accept(*a, **k): return default().accept(*a, **k)

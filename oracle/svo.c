@@ -1,0 +1,336 @@
+/*
+ * svo.c -- CPU oracle for the single-forward speculative verification step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header or constant
+ * with the GPU library.
+ *
+ * Plain, slow and direct: dense mask matrix, two-pass softmax per row over
+ * the visible keys, full per-slot softmax, serial scans.  All arithmetic is
+ * float64; inputs arrive as float32 (bf16 inputs are upcast exactly by the
+ * caller).  Sources followed (page title, then section / equation):
+ *   - "SimSD: Simple Speculative Decoding in Diffusion Language Models"
+ *     (papernotes.org): 关键设计 1 (paired data/mask layout), 关键设计 2
+ *     (temporal mask A_ij, the four-case equation), 关键设计 3 (RoPE copy
+ *     alignment), 关键设计 4 (acceptance alpha_r in draft order, longest
+ *     accepted prefix, in-place resample at the first rejection).
+ *   - "S2D2: Fast Decoding for Diffusion LLMs via Training-Free
+ *     Self-Speculation": 前置知识 "推测解码" (accept with min(1, q/p), resample
+ *     at the first rejection from the residual) and 方法步骤 (5) (residual
+ *     distribution (P_ver - P_draft)^+).
+ *   - The Portuguese SimSD summary (gist.science), sections 1-4, which
+ *     restate the layout, mask and RoPE rule.
+ * Readings where the pages are silent (each is listed in the design doc):
+ *   prompt carries step label 0 and counts as data; D~_k shares tau(k) with
+ *   D_k; positions are 0..P-1 for the prompt and P+k for both D_k and D~_k;
+ *   rotate-half RoPE with inv_freq_i = theta^(-2i/d); scale 1/sqrt(d) by
+ *   default; q-head h reads kv-head h / (Hq/Hkv); accept iff u < alpha
+ *   (strict); alpha = 1 when the draft probability of the proposed token is
+ *   zero; inverse-CDF resampling in ascending token order with u[gamma];
+ *   Z = 0 falls back to the target distribution; a full accept emits no extra
+ *   token.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define SVO_OK 0
+#define SVO_BAD_TAU -1
+#define SVO_BAD_ARG -2
+
+int svo_version(void) { return 1; }
+
+void svo_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int svo_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* tau must be a permutation of 1..B.  Returns 1 if so. */
+static int tau_is_permutation(const int32_t *tau, int B) {
+    int ok = 1;
+    char *seen = (char *)calloc((size_t)B + 1, 1);
+    for (int k = 0; k < B; ++k) {
+        int t = tau[k];
+        if (t < 1 || t > B || seen[t]) { ok = 0; break; }
+        seen[t] = 1;
+    }
+    free(seen);
+    return ok;
+}
+
+/*
+ * Temporal-causal mask (SimSD 关键设计 2, equation A_ij).
+ * Key/row order: [prompt 0..P-1 | D_1..D_B | D~_1..D~_B].  M is [2B][P+2B],
+ * row i = response row (i < B: D_{i+1}; i >= B: D~_{i-B+1}).
+ * Every position carries a kind (data or mask) and a step label: the prompt
+ * is data with label 0, D_k and D~_k both carry tau(k).  A row sees a column
+ * exactly when one of the equation's four cases holds.
+ */
+int svo_mask(int B, int P, const int32_t *tau, uint8_t *M) {
+    if (B < 1 || P < 0) return SVO_BAD_ARG;
+    if (!tau_is_permutation(tau, B)) return SVO_BAD_TAU;
+    const int ncol = P + 2 * B;
+    for (int i = 0; i < 2 * B; ++i) {
+        const int row_is_data = i < B;
+        const int ti = tau[i % B];
+        for (int j = 0; j < ncol; ++j) {
+            int col_is_data, tj;
+            if (j < P) { col_is_data = 1; tj = 0; }
+            else { const int c = j - P; col_is_data = c < B; tj = tau[c % B]; }
+            int vis = 0;
+            if (row_is_data && col_is_data && tj <= ti) vis = 1;          /* i,j in D      */
+            else if (row_is_data && !col_is_data && tj > ti) vis = 1;     /* i in D, j in D~ */
+            else if (!row_is_data && col_is_data && tj < ti) vis = 1;     /* i in D~, j in D */
+            else if (!row_is_data && !col_is_data && tj >= ti) vis = 1;   /* i,j in D~     */
+            M[(size_t)i * ncol + j] = (uint8_t)vis;
+        }
+    }
+    return SVO_OK;
+}
+
+/*
+ * Rotary position embedding, rotate-half convention, in place on
+ * x[n][heads][d] (float64); row r is rotated at position pos[r].
+ * Pair (i, i + d/2) turns by angle pos * theta^(-2i/d).
+ */
+void svo_rope(double *x, int64_t n, int heads, int d, const double *pos, double theta) {
+    const int half = d / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int h = 0; h < heads; ++h) {
+            double *v = x + ((size_t)r * heads + h) * d;
+            for (int i = 0; i < half; ++i) {
+                const double w = pow(theta, -2.0 * i / d);
+                const double phi = pos[r] * w;
+                const double c = cos(phi), s = sin(phi);
+                const double a = v[i], b = v[i + half];
+                v[i] = a * c - b * s;
+                v[i + half] = a * s + b * c;
+            }
+        }
+    }
+}
+
+/*
+ * Masked attention of the 2B response rows of ONE sequence.
+ *   q      [2B][Hq][d]   (pre-RoPE if theta > 0)
+ *   k_new  [2B][Hkv][d]  (pre-RoPE if theta > 0), v_new [2B][Hkv][d]
+ *   k_cache, v_cache [Hkv][P][d] (prompt keys already rotated)
+ *   tau    [B], out [2B][Hq][d] float64.
+ * Response row r (D_{r+1} or D~_{r-B+1}) sits at position P + (r mod B)
+ * (SimSD 关键设计 3: the mask slot reuses its data slot's index).  With
+ * theta <= 0 the inputs are taken as already rotated.  scale <= 0 means
+ * 1/sqrt(d).  Keys: prompt, then the 2B response keys, masked by svo_mask.
+ */
+int svo_attn(const float *q, const float *k_new, const float *v_new,
+             const float *k_cache, const float *v_cache, const int32_t *tau,
+             int B, int P, int Hq, int Hkv, int d, double theta, double scale,
+             double *out) {
+    if (B < 1 || P < 0 || Hq < 1 || Hkv < 1 || d < 2 || (d & 1) || Hq % Hkv) return SVO_BAD_ARG;
+    const int R = 2 * B, ncol = P + 2 * B, g = Hq / Hkv;
+    uint8_t *M = (uint8_t *)malloc((size_t)R * ncol);
+    int rc = svo_mask(B, P, tau, M);
+    if (rc) { free(M); return rc; }
+    double *qd = (double *)malloc(sizeof(double) * (size_t)R * Hq * d);
+    double *kd = (double *)malloc(sizeof(double) * (size_t)R * Hkv * d);
+    double *pos = (double *)malloc(sizeof(double) * (size_t)R);
+    for (size_t t = 0; t < (size_t)R * Hq * d; ++t) qd[t] = q[t];
+    for (size_t t = 0; t < (size_t)R * Hkv * d; ++t) kd[t] = k_new[t];
+    for (int r = 0; r < R; ++r) pos[r] = (double)P + (double)(r % B);
+    if (theta > 0) {
+        svo_rope(qd, R, Hq, d, pos, theta);
+        svo_rope(kd, R, Hkv, d, pos, theta);
+    }
+    if (scale <= 0) scale = 1.0 / sqrt((double)d);
+
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)ncol);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int h = 0; h < Hq; ++h) {
+            for (int i = 0; i < R; ++i) {
+                const int kvh = h / g;
+                const double *qi = qd + ((size_t)i * Hq + h) * d;
+                const uint8_t *Mi = M + (size_t)i * ncol;
+                double mx = -INFINITY;
+                for (int j = 0; j < ncol; ++j) {
+                    if (!Mi[j]) continue;
+                    double dot = 0.0;
+                    if (j < P) {
+                        const float *kj = k_cache + ((size_t)kvh * P + j) * d;
+                        for (int e = 0; e < d; ++e) dot += qi[e] * (double)kj[e];
+                    } else {
+                        const double *kj = kd + ((size_t)(j - P) * Hkv + kvh) * d;
+                        for (int e = 0; e < d; ++e) dot += qi[e] * kj[e];
+                    }
+                    sc[j] = scale * dot;
+                    if (sc[j] > mx) mx = sc[j];
+                }
+                double den = 0.0;
+                for (int j = 0; j < ncol; ++j) {
+                    if (!Mi[j]) continue;
+                    sc[j] = exp(sc[j] - mx);
+                    den += sc[j];
+                }
+                double *oi = out + ((size_t)i * Hq + h) * d;
+                for (int e = 0; e < d; ++e) oi[e] = 0.0;
+                for (int j = 0; j < ncol; ++j) {
+                    if (!Mi[j]) continue;
+                    const double w = sc[j] / den;
+                    if (j < P) {
+                        const float *vj = v_cache + ((size_t)kvh * P + j) * d;
+                        for (int e = 0; e < d; ++e) oi[e] += w * (double)vj[e];
+                    } else {
+                        const float *vj = v_new + ((size_t)(j - P) * Hkv + kvh) * d;
+                        for (int e = 0; e < d; ++e) oi[e] += w * (double)vj[e];
+                    }
+                }
+            }
+        }
+        free(sc);
+    }
+    free(M); free(qd); free(kd); free(pos);
+    return SVO_OK;
+}
+
+/* Softmax of one logits row in float64: p[v] = exp(l[v] - m) / s with
+ * m = max l and s = sum_v exp(l[v] - m).  p may be NULL (only m, s). */
+void svo_softmax(const float *l, int64_t V, double *p, double *m_out, double *s_out) {
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) if ((double)l[v] > m) m = l[v];
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v) s += exp((double)l[v] - m);
+    if (p) for (int64_t v = 0; v < V; ++v) p[v] = exp((double)l[v] - m) / s;
+    if (m_out) *m_out = m;
+    if (s_out) *s_out = s;
+}
+
+/*
+ * Residual resample at the first rejected slot (S2D2 方法步骤 (5): the
+ * residual (P_target - P_draft)^+; SimSD 关键设计 4: the target resamples the
+ * rejected position in place).  r(v) = max(0, p_theta(v) - p_phi(v)),
+ * Z = sum r.  The token is the smallest v whose running sum (ascending token
+ * order) exceeds u * Z.  If Z == 0 the target distribution p_theta is used
+ * instead.  If rounding leaves no running sum above u * Z, the last token
+ * with positive mass is taken.  Optional outputs: cdf[V] (running sums of the
+ * distribution actually used), *Z_out, *used_target (1 if Z == 0).
+ */
+int64_t svo_residual(const float *l, const float *pphi, int64_t V, double u,
+                     double *cdf, double *Z_out, int *used_target) {
+    double m, s;
+    svo_softmax(l, V, NULL, &m, &s);
+    double Z = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        const double pt = exp((double)l[v] - m) / s;
+        const double r = pt - (double)pphi[v];
+        if (r > 0) Z += r;
+    }
+    const int use_t = !(Z > 0.0);
+    double tot = 0.0;
+    if (use_t) for (int64_t v = 0; v < V; ++v) tot += exp((double)l[v] - m) / s;
+    else tot = Z;
+    const double thr = u * tot;
+    double run = 0.0;
+    int64_t pick = -1, last_pos = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        const double pt = exp((double)l[v] - m) / s;
+        double mass = use_t ? pt : pt - (double)pphi[v];
+        if (mass < 0) mass = 0;
+        run += mass;
+        if (cdf) cdf[v] = run;
+        if (mass > 0) last_pos = v;
+        if (pick < 0 && run > thr) pick = v;
+    }
+    if (pick < 0) pick = last_pos;
+    if (Z_out) *Z_out = tot;
+    if (used_target) *used_target = use_t;
+    return pick;
+}
+
+/*
+ * Acceptance for `batch` sequences (SimSD 关键设计 4).
+ *   logits, probs [batch][B][V] indexed by slot (the slot's D~ row);
+ *   tokens [batch][B] draft token per slot; tau [batch][B];
+ *   u [batch][gamma+1]: u[r-1] tests draft step r, u[gamma] drives the resample.
+ * Draft step r (1..gamma) verifies slot o_r with tau(o_r) = r:
+ *   alpha_r = min(1, p_theta(x) / p_phi(x)), x = tokens[o_r], accept iff
+ *   u[r-1] < alpha_r.  L = number of leading accepted steps.
+ * Outputs: accept_len[batch] = L; out_tokens[batch][B]: the draft token where
+ *   tau <= L, the resampled token where tau == L+1 (only if L < gamma), -1
+ *   elsewhere; alpha[batch][gamma] (float64, every step, draft order);
+ *   resample_slot[batch] (-1 if none) -- may be NULL.
+ * Returns 0, or a negative code for the first bad sequence.
+ */
+int svo_accept(const float *logits, const float *probs, const int32_t *tokens,
+               const int32_t *tau, const float *u, int batch, int B, int gamma,
+               int64_t V, int32_t *accept_len, int32_t *out_tokens, double *alpha,
+               int32_t *resample_slot) {
+    if (batch < 0 || B < 1 || gamma < 1 || gamma > B || V < 1) return SVO_BAD_ARG;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *tb = tau + (size_t)b * B;
+        const int32_t *xb = tokens + (size_t)b * B;
+        const float *ub = u + (size_t)b * (gamma + 1);
+        int32_t *ob = out_tokens + (size_t)b * B;
+        if (!tau_is_permutation(tb, B)) {
+#pragma omp critical
+            err = SVO_BAD_TAU;
+            continue;
+        }
+        int bad = 0;
+        for (int k = 0; k < B; ++k) if (xb[k] < 0 || xb[k] >= V) bad = 1;
+        if (bad) {
+#pragma omp critical
+            err = SVO_BAD_ARG;
+            continue;
+        }
+        int order[64 + 1];
+        int *o = (B <= 64) ? order : (int *)malloc(sizeof(int) * ((size_t)B + 1));
+        for (int k = 0; k < B; ++k) o[tb[k]] = k;   /* o[r] = slot decoded at step r */
+        int L = -1;
+        for (int r = 1; r <= gamma; ++r) {
+            const int k = o[r];
+            const float *lk = logits + ((size_t)b * B + k) * V;
+            const float *pk = probs + ((size_t)b * B + k) * V;
+            double m, s;
+            svo_softmax(lk, V, NULL, &m, &s);
+            const int x = xb[k];
+            const double pt = exp((double)lk[x] - m) / s;
+            const double pd = (double)pk[x];
+            double a = (pd > 0.0) ? pt / pd : 1.0;
+            if (a > 1.0) a = 1.0;
+            if (alpha) alpha[(size_t)b * gamma + (r - 1)] = a;
+            if (L < 0 && !((double)ub[r - 1] < a)) L = r - 1;
+        }
+        if (L < 0) L = gamma;
+        accept_len[b] = L;
+        for (int k = 0; k < B; ++k) ob[k] = (tb[k] <= L) ? xb[k] : -1;
+        int rs = -1;
+        if (L < gamma) {
+            rs = o[L + 1];
+            const float *lk = logits + ((size_t)b * B + rs) * V;
+            const float *pk = probs + ((size_t)b * B + rs) * V;
+            ob[rs] = (int32_t)svo_residual(lk, pk, V, (double)ub[gamma], NULL, NULL, NULL);
+        }
+        if (resample_slot) resample_slot[b] = rs;
+        if (o != order) free(o);
+    }
+    return err;
+}

@@ -1,0 +1,518 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each pin takes an ``oracle.Oracle`` handle and raises AssertionError when the
+oracle disagrees with an independent fact: a hand-worked fixture under
+``tests/golden/``, an invariant that follows from the pages' definitions, a
+closed form, a special case that reduces to a textbook computation, or brute
+force on a tiny input.  None of them retypes the oracle's own formula.  The
+same pins run against deliberately broken copies of the oracle
+(``test_oracle_mutants.py``) to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- fixtures
+def load_mask_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(t) for t in line.split()])
+    B, P = rows[0]
+    tau = np.array(rows[1], np.int32)
+    M = np.array(rows[2:], np.uint8)
+    return B, P, tau, M
+
+
+def load_accept_golden():
+    with open(os.path.join(GOLDEN, "accept_tiny.json")) as f:
+        return json.load(f)["cases"]
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def random_tau(B, seed):
+    return (rng(seed).permutation(B) + 1).astype(np.int32)
+
+
+# --------------------------------------------------------------------- mask
+def pin_mask_golden(o):
+    for name in ("mask_B3_tau213_P2.txt", "mver_B4.txt"):
+        B, P, tau, M = load_mask_golden(name)
+        got = o.mask(tau, P)
+        assert got.shape == M.shape, name
+        assert np.array_equal(got, M), f"{name}: oracle mask differs from the hand-worked fixture"
+
+
+def pin_mask_invariants(o, tau, P):
+    """Every response row sees the whole prompt, exactly one of D_k / D~_k for
+    each slot k, hence exactly P + B keys (follows from the four cases being
+    complementary per slot)."""
+    B = len(tau)
+    M = o.mask(tau, P).astype(np.int64)
+    assert M.shape == (2 * B, P + 2 * B)
+    assert (M[:, :P] == 1).all(), "prompt must be visible to every response row"
+    pair = M[:, P:P + B] + M[:, P + B:]
+    assert (pair == 1).all(), "exactly one of D_k, D~_k must be visible per row and slot"
+    assert (M.sum(axis=1) == P + B).all()
+
+
+def pin_mask_extremes(o, tau, P):
+    """The mask slot decoded first (tau = 1) has no earlier data: it sees no
+    D and every D~.  The data row decoded last (tau = B) sees all of D and no
+    D~.  Each D~ row never sees its own data slot (no leak of the token it
+    predicts) and each D row sees its own token."""
+    B = len(tau)
+    M = o.mask(tau, P)
+    k1 = int(np.where(tau == 1)[0][0])
+    kB = int(np.where(tau == B)[0][0])
+    assert (M[B + k1, P:P + B] == 0).all() and (M[B + k1, P + B:] == 1).all()
+    assert (M[kB, P:P + B] == 1).all() and (M[kB, P + B:] == 0).all()
+    for k in range(B):
+        assert M[B + k, P + k] == 0, "a mask slot must not see its own data token"
+        assert M[k, P + k] == 1, "a data slot sees its own token"
+        assert M[B + k, P + B + k] == 1, "a mask slot sees itself"
+
+
+def pin_mask_identity(o, B, P):
+    """tau = identity gives the block-triangular 2L verification view."""
+    tau = np.arange(1, B + 1, dtype=np.int32)
+    M = o.mask(tau, P)
+    one = np.ones((B, B), np.uint8)
+    ref = np.block([[np.tril(one), np.triu(one, 1)], [np.tril(one, -1), np.triu(one)]])
+    assert np.array_equal(M[:, P:], ref)
+    assert (M[:, :P] == 1).all()
+
+
+def slot_perm_index(sigma, P):
+    """Column/row index map for a slot permutation: new slot k holds old slot
+    sigma[k] (prompt positions fixed)."""
+    B = len(sigma)
+    rows = np.concatenate([sigma, B + sigma])
+    cols = np.concatenate([np.arange(P), P + sigma, P + B + sigma])
+    return rows, cols
+
+
+def pin_mask_equivariance(o, tau, sigma, P):
+    """Relabelling slots permutes rows and columns of the mask: the mask
+    depends on kinds and step labels only, not on slot indices."""
+    tau2 = tau[sigma]
+    M = o.mask(tau, P)
+    M2 = o.mask(tau2, P)
+    rows, cols = slot_perm_index(sigma, P)
+    assert np.array_equal(M2, M[np.ix_(rows, cols)])
+
+
+def pin_mask_rejects_bad_tau(o):
+    import oracle as om
+    for bad in ([1, 1, 2], [0, 1, 2], [1, 2, 4]):
+        try:
+            o.mask(np.array(bad, np.int32), 3)
+        except om.OracleError:
+            continue
+        raise AssertionError(f"tau {bad} accepted")
+
+
+def all_mask_pins(o):
+    pin_mask_golden(o)
+    for B in (1, 2, 3):
+        for perm in itertools.permutations(range(1, B + 1)):
+            tau = np.array(perm, np.int32)
+            for P in (0, 3):
+                pin_mask_invariants(o, tau, P)
+                pin_mask_extremes(o, tau, P)
+    for s in range(20):
+        B = (8, 16, 64)[s % 3]
+        tau = random_tau(B, 100 + s)
+        pin_mask_invariants(o, tau, 5)
+        pin_mask_extremes(o, tau, 5)
+        pin_mask_equivariance(o, tau, rng(200 + s).permutation(B), 5)
+        pin_mask_equivariance(o, tau, np.argsort(tau), 0)
+    for B in (1, 4, 8, 32):
+        pin_mask_identity(o, B, 7)
+    pin_mask_rejects_bad_tau(o)
+
+
+# --------------------------------------------------------------------- RoPE
+def pin_rope_zero_position(o):
+    x = rng(1).standard_normal((3, 2, 16))
+    y = o.rope(x, np.zeros(3), 1e4)
+    assert np.array_equal(x, y)
+
+
+def pin_rope_2d(o):
+    """d = 2: the only pair turns by exactly pos radians (theta^0 = 1), the
+    textbook plane rotation."""
+    x = rng(2).standard_normal((5, 2))
+    pos = np.array([0.0, 1.0, 2.5, -3.0, 100.0])
+    y = o.rope(x, pos, 1e4)
+    c, s = np.cos(pos), np.sin(pos)
+    ref = np.stack([x[:, 0] * c - x[:, 1] * s, x[:, 0] * s + x[:, 1] * c], axis=1)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def pin_rope_pairs_and_frequencies(o, d=16, theta=1e4):
+    """Unit vector e_i (i < d/2) at position p stays in the plane (i, i+d/2)
+    and turns by p * theta^(-2i/d) counter-clockwise."""
+    half = d // 2
+    for i in range(half):
+        e = np.zeros((1, d))
+        e[0, i] = 1.0
+        p = 0.7
+        y = o.rope(e, np.array([p]), theta)[0]
+        others = np.delete(y, [i, i + half])
+        assert np.abs(others).max() < 1e-15, "rotate-half pairs (i, i + d/2)"
+        ang = np.arctan2(y[i + half], y[i])
+        assert abs(ang - p * theta ** (-2.0 * i / d)) < 1e-12
+
+
+def pin_rope_norm_and_relative(o, d=64, theta=1e4):
+    """Rotation preserves norms, and <R_m q, R_n k> = <R_{m-n} q, k>."""
+    r = rng(3)
+    q = r.standard_normal((1, d))
+    k = r.standard_normal((1, d))
+    for m, n in ((5, 2), (100, 37), (2080, 3), (16400, 16400)):
+        qm = o.rope(q, np.array([float(m)]), theta)
+        kn = o.rope(k, np.array([float(n)]), theta)
+        qd = o.rope(q, np.array([float(m - n)]), theta)
+        assert abs(np.linalg.norm(qm) - np.linalg.norm(q)) < 1e-12
+        assert abs(np.dot(qm[0], kn[0]) - np.dot(qd[0], k[0])) < 1e-9
+
+
+def all_rope_pins(o):
+    pin_rope_zero_position(o)
+    pin_rope_2d(o)
+    pin_rope_pairs_and_frequencies(o)
+    pin_rope_pairs_and_frequencies(o, d=128, theta=1e6)
+    pin_rope_norm_and_relative(o)
+
+
+# ---------------------------------------------------------------- attention
+def tiny_attn_inputs(seed, B=8, P=32, Hq=4, Hkv=2, d=16):
+    r = rng(seed)
+    R = 2 * B
+    return dict(
+        q=r.standard_normal((R, Hq, d)).astype(np.float32),
+        k_new=r.standard_normal((R, Hkv, d)).astype(np.float32),
+        v_new=r.standard_normal((R, Hkv, d)).astype(np.float32),
+        k_cache=r.standard_normal((Hkv, P, d)).astype(np.float32),
+        v_cache=r.standard_normal((Hkv, P, d)).astype(np.float32),
+        tau=random_tau(B, seed + 1),
+    )
+
+
+def textbook_attention(q, K, V, scale):
+    """Ordinary unmasked softmax attention of one query over rows of K, V."""
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ V
+
+
+def pin_attn_bruteforce(o, inp, theta):
+    """One-layer invariant: each response row equals plain unmasked attention
+    over its explicitly rebuilt context.  D~_i: prompt, data tokens D_k with
+    tau(k) < tau(i), mask tokens D~_k for the other slots.  D_i: prompt, D_k
+    with tau(k) <= tau(i), D~_k otherwise.  Every token is rotated at its true
+    position (prompt already rotated; slot k at P + k)."""
+    q, kn, vn, kc, vc, tau = (inp[k] for k in ("q", "k_new", "v_new", "k_cache", "v_cache", "tau"))
+    R, Hq, d = q.shape
+    B = R // 2
+    Hkv, P = kc.shape[0], kc.shape[1]
+    g = Hq // Hkv
+    got = o.attention(q, kn, vn, kc, vc, tau, theta)
+    slot_pos = P + np.arange(B, dtype=np.float64)
+    kD = o.rope(kn[:B].astype(np.float64), slot_pos, theta) if theta > 0 else kn[:B].astype(np.float64)
+    kM = o.rope(kn[B:].astype(np.float64), slot_pos, theta) if theta > 0 else kn[B:].astype(np.float64)
+    qD = o.rope(q[:B].astype(np.float64), slot_pos, theta) if theta > 0 else q[:B].astype(np.float64)
+    qM = o.rope(q[B:].astype(np.float64), slot_pos, theta) if theta > 0 else q[B:].astype(np.float64)
+    vD, vM = vn[:B].astype(np.float64), vn[B:].astype(np.float64)
+    worst = 0.0
+    for i in range(B):
+        for is_mask in (False, True):
+            use_data = (tau < tau[i]) if is_mask else (tau <= tau[i])
+            for h in range(Hq):
+                kv = h // g
+                Kctx = np.concatenate([kc[kv].astype(np.float64),
+                                       np.where(use_data[:, None], kD[:, kv], kM[:, kv])])
+                Vctx = np.concatenate([vc[kv].astype(np.float64),
+                                       np.where(use_data[:, None], vD[:, kv], vM[:, kv])])
+                qi = (qM if is_mask else qD)[i, h]
+                ref = textbook_attention(qi, Kctx, Vctx, 1.0 / np.sqrt(d))
+                row = (B + i) if is_mask else i
+                worst = max(worst, np.abs(got[row, h] - ref).max())
+    assert worst < 1e-12, f"brute-force context mismatch {worst}"
+
+
+def pin_attn_single_key(o):
+    """P = 0, B = 1: D_1 sees only itself and D~_1 only itself, so each
+    output is that token's value vector exactly."""
+    inp = tiny_attn_inputs(5, B=1, P=0, Hq=2, Hkv=1, d=8)
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 1e4)
+    for h in range(2):
+        assert np.abs(out[0, h] - inp["v_new"][0, 0]).max() < 1e-14
+        assert np.abs(out[1, h] - inp["v_new"][1, 0]).max() < 1e-14
+
+
+def pin_attn_two_keys_scale(o):
+    """P = 1, B = 1, no rotation: D_1 sees the prompt key and itself, so the
+    output is a logistic mix with weight sigmoid((s0 - s1)/sqrt(d))."""
+    d = 8
+    inp = tiny_attn_inputs(6, B=1, P=1, Hq=1, Hkv=1, d=d)
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 0.0)
+    q = inp["q"][0, 0].astype(np.float64)
+    s0 = q @ inp["k_cache"][0, 0] / np.sqrt(d)
+    s1 = q @ inp["k_new"][0, 0] / np.sqrt(d)
+    w0 = 1.0 / (1.0 + np.exp(s1 - s0))
+    ref = w0 * inp["v_cache"][0, 0] + (1 - w0) * inp["v_new"][0, 0]
+    assert np.abs(out[0, 0] - ref).max() < 1e-13
+    out2 = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                       inp["tau"], 0.0, scale=1.0 / np.sqrt(d))
+    assert np.abs(out2 - out).max() == 0.0
+
+
+def pin_attn_gqa_mapping(o):
+    """Query heads 2k and 2k+1 read kv-head k when Hq = 4, Hkv = 2: zero
+    values on kv-head 1 zero exactly heads 2 and 3."""
+    inp = tiny_attn_inputs(7, B=4, P=6, Hq=4, Hkv=2, d=8)
+    inp["v_new"][:, 1] = 0
+    inp["v_cache"][1] = 0
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 1e4)
+    assert (out[:, 2:] == 0).all()
+    assert (np.abs(out[:, :2]).max(axis=2) > 0).all()
+
+
+def pin_attn_constant_values(o):
+    """Softmax weights sum to one: constant value rows give that constant."""
+    inp = tiny_attn_inputs(8, B=5, P=9, Hq=2, Hkv=1, d=8)
+    inp["v_new"][:] = 0.75
+    inp["v_cache"][:] = 0.75
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 1e4)
+    assert np.abs(out - 0.75).max() < 1e-14
+
+
+def pin_attn_equivariance(o, seed):
+    """Relabelling slots (rows and keys of D and D~ together, tau' = tau o
+    sigma) permutes the outputs in the same way (pre-rotated inputs)."""
+    inp = tiny_attn_inputs(seed, B=6, P=5, Hq=2, Hkv=1, d=8)
+    B = 6
+    sigma = rng(seed + 9).permutation(B)
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 0.0)
+    rows = np.concatenate([sigma, B + sigma])
+    out2 = o.attention(inp["q"][rows], inp["k_new"][rows], inp["v_new"][rows], inp["k_cache"],
+                       inp["v_cache"], inp["tau"][sigma], 0.0)
+    assert np.abs(out2 - out[rows]).max() < 1e-13
+
+
+def pin_attn_copy_alignment(o):
+    """Identical raw query rows for D_k and D~_k are rotated at the same
+    position: with every key made visible-equivalent (identical D and D~
+    keys/values), D_k and D~_k see the same multiset of tokens and give the
+    same output."""
+    inp = tiny_attn_inputs(9, B=4, P=3, Hq=1, Hkv=1, d=8)
+    B = 4
+    inp["q"][B:] = inp["q"][:B]
+    inp["k_new"][B:] = inp["k_new"][:B]
+    inp["v_new"][B:] = inp["v_new"][:B]
+    out = o.attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                      inp["tau"], 1e4)
+    assert np.abs(out[:B] - out[B:]).max() < 1e-13
+
+
+def all_attention_pins(o):
+    for seed, P in ((11, 32), (12, 0), (13, 7)):
+        inp = tiny_attn_inputs(seed, B=8, P=P)
+        pin_attn_bruteforce(o, inp, 1e4)
+    pin_attn_bruteforce(o, tiny_attn_inputs(14, B=3, P=5, Hq=2, Hkv=2, d=8), 0.0)
+    pin_attn_single_key(o)
+    pin_attn_two_keys_scale(o)
+    pin_attn_gqa_mapping(o)
+    pin_attn_constant_values(o)
+    pin_attn_equivariance(o, 21)
+    pin_attn_copy_alignment(o)
+
+
+# ------------------------------------------------------------------- accept
+def pin_accept_golden(o):
+    for c in load_accept_golden():
+        tp = np.array(c["target_probs"], np.float64)
+        logits = np.log(tp).astype(np.float32)[None]
+        probs = np.array(c["draft_probs"], np.float32)[None]
+        L, ot, al, _ = o.accept(logits, probs, np.array([c["draft_tokens"]], np.int32),
+                                np.array([c["tau"]], np.int32),
+                                np.array([c["uniforms"]], np.float32), c["gamma"])
+        assert int(L[0]) == c["accept_len"], c["note"]
+        assert ot[0].tolist() == c["out_tokens"], c["note"]
+        assert np.allclose(al[0], c["alpha"], rtol=1e-6, atol=0), c["note"]
+
+
+def pin_softmax(o):
+    """V = 2 gives the logistic function; shifting logits changes nothing;
+    probabilities sum to one."""
+    p, m, s = o.softmax(np.array([1.5, -0.5], np.float32))
+    assert abs(p[0] - 1.0 / (1.0 + np.exp(-2.0))) < 1e-15
+    # logits on a 2^-10 grid so that adding 64 is exact in float32
+    l = (np.round(rng(4).standard_normal(1000) * 3 * 1024) / 1024).astype(np.float32)
+    p1, _, _ = o.softmax(l)
+    p2, _, _ = o.softmax(l + np.float32(64.0))
+    assert abs(p1.sum() - 1) < 1e-13 and np.abs(p1 - p2).max() < 1e-12
+
+
+def _one_slot(o, lt, pd, x, u0, u1):
+    L, ot, al, _ = o.accept(lt[None, None], pd[None, None], np.array([[x]], np.int32),
+                            np.array([[1]], np.int32), np.array([[u0, u1]], np.float32), 1)
+    return int(L[0]), int(ot[0, 0]), float(al[0, 0])
+
+
+def pin_accept_tv_identity(o, V=6, seed=30):
+    """E_{x ~ p_phi}[alpha(x)] = sum_v min(p_theta, p_phi) = 1 - D_TV
+    (the acceptance rate of rejection sampling equals one minus the total
+    variation distance)."""
+    r = rng(seed)
+    lt = (r.standard_normal(V) * 1.5).astype(np.float32)
+    pt, _, _ = o.softmax(lt)
+    pd = r.dirichlet(np.ones(V)).astype(np.float32)
+    acc = sum(float(pd[x]) * _one_slot(o, lt, pd, x, 0.0, 0.5)[2] for x in range(V))
+    tv = 0.5 * np.abs(pt - pd.astype(np.float64)).sum()
+    ref = np.minimum(pt, pd.astype(np.float64)).sum()
+    assert abs(acc - ref) < 1e-12
+    assert abs(ref - (1 - tv)) < 1e-6  # p_phi sums to one only up to float32
+
+
+def pin_accept_exact_distribution(o, V=4, seed=31, N=4000):
+    """Exact law of the emitted token at a slot, by enumeration: draft token
+    x with probability p_phi(x); accept with probability alpha(x) (measure of
+    u < alpha); otherwise the resample, whose law is the measure of the
+    resample uniform mapping to each token (a fine midpoint grid).  The
+    result must be the target distribution p_theta."""
+    r = rng(seed)
+    lt = (r.standard_normal(V) * 1.2).astype(np.float32)
+    pt, _, _ = o.softmax(lt)
+    pd = r.dirichlet(np.ones(V)).astype(np.float64)
+    pd /= pd.sum()
+    pd32 = pd.astype(np.float32)
+    law = np.zeros(V)
+    grid = (np.arange(N) + 0.5) / N
+    for x in range(V):
+        a = _one_slot(o, lt, pd32, x, 0.0, 0.5)[2]
+        law[x] += float(pd32[x]) * a
+        counts = np.zeros(V)
+        for u1 in grid:
+            L, t, _ = _one_slot(o, lt, pd32, x, 0.999999, float(u1))
+            if L == 0:
+                counts[t] += 1
+        if counts.sum():
+            law += float(pd32[x]) * (1 - a) * counts / N
+    assert np.abs(law - pt).max() < 2.0 / N + 1e-6, (law, pt)
+
+
+def pin_accept_special_cases(o):
+    r = rng(32)
+    V = 50
+    lt = r.standard_normal(V).astype(np.float32)
+    pt, _, _ = o.softmax(lt)
+    pd = pt.astype(np.float32)
+    # p_theta == p_phi: every step accepted (alpha = 1 up to float32 rounding)
+    B = 5
+    lts = np.stack([lt] * B)[None]
+    pds = np.stack([pd] * B)[None]
+    tau = random_tau(B, 33)[None]
+    toks = r.integers(0, V, (1, B)).astype(np.int32)
+    u = np.full((1, B + 1), 0.99, np.float32)
+    L, ot, al, rs = o.accept(lts, pds, toks, tau, u, B)
+    assert L[0] == B and (ot == toks).all() and rs[0] == -1
+    assert np.abs(al - 1).max() < 1e-6
+    # p_theta(x) = 0: rejected even with u = 0
+    lt0 = lt.copy()
+    lt0[7] = np.float32(-3e38)
+    Lx, tx, ax = _one_slot(o, lt0, pd, 7, 0.0, 0.5)
+    assert Lx == 0 and ax == 0.0 and tx != 7
+    # p_phi >= p_theta everywhere: the residual is empty and the target is used
+    pd_big = (pt * 1.25).astype(np.float32)
+    tok, cdf, Z, used = o.residual(lt, pd_big, 0.5)
+    assert used and abs(Z - 1) < 1e-12 and cdf[tok] > 0.5 and (tok == 0 or cdf[tok - 1] <= 0.5)
+
+
+def pin_accept_assembly(o, seed=34):
+    """Output layout: tokens of steps 1..L are the draft tokens, the slot of
+    step L+1 holds the resample, slots of later steps and of steps > gamma
+    hold -1; alpha is reported for every step in draft order."""
+    r = rng(seed)
+    n, B, V = 200, 6, 16
+    lt = (r.standard_normal((n, B, V)) * 1.5).astype(np.float32)
+    pd = r.dirichlet(np.ones(V), (n, B)).astype(np.float32)
+    toks = r.integers(0, V, (n, B)).astype(np.int32)
+    tau = np.stack([random_tau(B, 1000 + i) for i in range(n)])
+    u = r.random((n, B + 1)).astype(np.float32)
+    for gamma in (B, 3):
+        uu = u[:, :gamma + 1].copy()
+        L, ot, al, rs = o.accept(lt, pd, toks, tau, uu, gamma)
+        for b in range(n):
+            l = int(L[b])
+            assert 0 <= l <= gamma
+            steps = tau[b]
+            # leading accepts: every step r <= L has u < alpha, step L+1 fails
+            assert all(uu[b, s] < al[b, s] for s in range(l))
+            if l < gamma:
+                assert not (uu[b, l] < al[b, l])
+            for k in range(B):
+                if steps[k] <= l:
+                    assert ot[b, k] == toks[b, k]
+                elif steps[k] == l + 1 and l < gamma:
+                    assert rs[b] == k and 0 <= ot[b, k] < V
+                else:
+                    assert ot[b, k] == -1
+            # alpha in draft order: step s verifies the slot with tau = s
+            for s in range(gamma):
+                k = int(np.where(steps == s + 1)[0][0])
+                x = toks[b, k]
+                pt, _, _ = o.softmax(lt[b, k])
+                assert abs(al[b, s] - min(1.0, pt[x] / float(pd[b, k, x]))) < 1e-12
+
+
+def pin_accept_energy(o, seed=35):
+    """S2D2's residual-energy form: alpha = min(1, exp(-E)), with
+    E = -log q + log p (q the verifier's, p the draft's probability)."""
+    r = rng(seed)
+    V = 12
+    for _ in range(10):
+        lt = (r.standard_normal(V) * 2).astype(np.float32)
+        pd = r.dirichlet(np.ones(V)).astype(np.float32)
+        x = int(r.integers(V))
+        pt, _, _ = o.softmax(lt)
+        a = _one_slot(o, lt, pd, x, 0.0, 0.5)[2]
+        E = -np.log(pt[x]) + np.log(float(pd[x]))
+        assert abs(a - min(1.0, np.exp(-E))) < 1e-12
+
+
+def all_accept_pins(o, exact=True):
+    pin_accept_golden(o)
+    pin_softmax(o)
+    pin_accept_tv_identity(o)
+    pin_accept_special_cases(o)
+    pin_accept_assembly(o)
+    pin_accept_energy(o)
+    if exact:
+        pin_accept_exact_distribution(o, N=1000)
+
+
+def all_pins(o):
+    all_mask_pins(o)
+    all_rope_pins(o)
+    all_attention_pins(o)
+    all_accept_pins(o)

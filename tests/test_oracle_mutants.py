@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the oracle's C source (on the CPU)
+and check that at least one pin fails for each: the pins would catch a
+dropped term, a wrong comparison, sign, index or operand order."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+# (name, original text, replacement) -- each original must occur exactly once
+MUTANTS = [
+    ("D-D case strict", "tj <= ti) vis = 1;          /* i,j in D ", "tj < ti) vis = 1;          /* i,j in D "),
+    ("D-D~ case non-strict", "tj > ti) vis = 1;     /* i in D, j in D~", "tj >= ti) vis = 1;     /* i in D, j in D~"),
+    ("D~-D case non-strict", "tj < ti) vis = 1;     /* i in D~, j in D", "tj <= ti) vis = 1;     /* i in D~, j in D"),
+    ("D~-D~ case strict", "tj >= ti) vis = 1;   /* i,j in D~", "tj > ti) vis = 1;   /* i,j in D~"),
+    ("D~ rows see future data", "tj < ti) vis = 1;     /* i in D~, j in D", "tj > ti) vis = 1;     /* i in D~, j in D"),
+    ("prompt as mask kind", "col_is_data = 1; tj = 0;", "col_is_data = 0; tj = 0;"),
+    ("slot index instead of label", "const int ti = tau[i % B];", "const int ti = 1 + i % B;"),
+    ("rope frequency exponent", "pow(theta, -2.0 * i / d)", "pow(theta, -1.0 * i / d)"),
+    ("rope sign", "v[i] = a * c - b * s;", "v[i] = a * c + b * s;"),
+    ("rope physical positions", "pos[r] = (double)P + (double)(r % B);", "pos[r] = (double)P + (double)r;"),
+    ("rope skips keys", "svo_rope(kd, R, Hkv, d, pos, theta);", ";"),
+    ("gqa mapping", "const int kvh = h / g;", "const int kvh = h % Hkv;"),
+    ("softmax scale", "scale = 1.0 / sqrt((double)d);", "scale = 1.0 / (double)d;"),
+    ("unnormalised weights", "const double w = sc[j] / den;", "const double w = sc[j];"),
+    ("ratio inverted", "double a = (pd > 0.0) ? pt / pd : 1.0;", "double a = (pd > 0.0) ? pd / pt : 1.0;"),
+    ("target prob unnormalised", "const double pt = exp((double)lk[x] - m) / s;", "const double pt = exp((double)lk[x] - m);"),
+    ("slot order instead of draft order", "const int k = o[r];", "const int k = r - 1;"),
+    ("prefix off by one", "L = r - 1;", "L = r;"),
+    ("assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;", "ob[k] = (tb[k] < L) ? xb[k] : -1;"),
+    ("residual operands swapped", "const double r = pt - (double)pphi[v];", "const double r = (double)pphi[v] - pt;"),
+    ("resample mass operands swapped", "double mass = use_t ? pt : pt - (double)pphi[v];", "double mass = use_t ? pt : (double)pphi[v] - pt;"),
+    ("resample at wrong slot", "rs = o[L + 1];", "rs = o[L > 0 ? L : 1];"),
+    ("resample uses step uniform", "(double)ub[gamma], NULL", "(double)ub[0], NULL"),
+]
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, src_text, name, old, new):
+    assert src_text.count(old) == 1, f"mutation site not unique/present: {old!r}"
+    mut = src_text.replace(old, new)
+    src = tmp_path / "svo_mut.c"
+    src.write_text(mut)
+    lib = str(tmp_path / "libsvo_mut.so")
+    subprocess.run(oracle.gcc_cmd(str(src), lib), check=True)
+    o = oracle.Oracle(lib)
+    try:
+        pins.all_pins(o)
+    except (AssertionError, oracle.OracleError, IndexError, ValueError):
+        return
+    pytest.fail(f"no pin caught mutant '{name}'")
+
+
+def test_unmutated_passes_all_pins():
+    pins.all_pins(oracle.Oracle())

@@ -1,0 +1,117 @@
+"""ctypes binding of libspecverify.so -- argument marshalling only.
+
+Functions carry the names and argument order of ``include/spec_verify.h``.
+Pointer arguments accept a torch tensor (its ``data_ptr()``), a plain
+integer address, or None (NULL).  ``stream`` defaults to torch's current
+stream on the current device.  Every step of the computation runs in the HIP
+library; a non-zero status raises ``SpecVerifyError``.  There is no fallback:
+if the library is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_E_NULL, SV_E_SHAPE, SV_E_UNSUPPORTED, SV_E_ALIGN, SV_E_WORKSPACE, SV_E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+SV_F32, SV_BF16 = 0, 1
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def load(path: str | None = None):
+    """Load the built library (raises OSError if it is missing)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"libspecverify.so not built at {p}: run __graft_entry__.build() "
+                      "or python -m diffusion_speculative_verification_amd.build")
+    lib = ctypes.CDLL(p)
+    V, I, D, F, SZ, I64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float,
+                           ctypes.c_size_t, ctypes.c_int64)
+    lib.spec_verify_abi_version.restype = I
+    lib.spec_verify_abi_version.argtypes = []
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_status_string.argtypes = [I]
+    lib.spec_verify_rope.restype = I
+    lib.spec_verify_rope.argtypes = [V, V, V, V, I, I, I, I, I, I, I, D, V]
+    lib.spec_verify_attn_workspace_size.restype = SZ
+    lib.spec_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.spec_verify_attn.restype = I
+    lib.spec_verify_attn.argtypes = [V, V, V, V, V, V, V, I, I, I, I, I, I, I, D, F, V, SZ, V]
+    lib.spec_verify_accept_workspace_size.restype = SZ
+    lib.spec_verify_accept_workspace_size.argtypes = [I, I, I, I64]
+    lib.spec_verify_accept.restype = I
+    lib.spec_verify_accept.argtypes = [V, V, V, V, V, I, I, I, I64, V, V, V, V, SZ, V]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc: int):
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, spec_verify_status_string(rc))
+
+
+def spec_verify_abi_version() -> int:
+    return load().spec_verify_abi_version()
+
+
+def spec_verify_status_string(status: int) -> str:
+    return load().spec_verify_status_string(status).decode()
+
+
+def spec_verify_rope(q_in, k_in, q_out, k_out, dtype, batch, block, n_qh, n_kvh, head_dim, prefix_len,
+                     theta, stream=None) -> None:
+    _check(load().spec_verify_rope(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), dtype, batch, block,
+                                   n_qh, n_kvh, head_dim, prefix_len, float(theta), _stream(stream)))
+
+
+def spec_verify_attn_workspace_size(dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim) -> int:
+    return int(load().spec_verify_attn_workspace_size(dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim))
+
+
+def spec_verify_attn(q, k_new, v_new, k_cache, v_cache, tau, out, dtype, batch, block, prefix_len, n_qh,
+                     n_kvh, head_dim, rope_theta, softmax_scale, workspace, workspace_bytes,
+                     stream=None) -> None:
+    _check(load().spec_verify_attn(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(tau), _ptr(out), dtype, batch, block, prefix_len, n_qh, n_kvh,
+                                   head_dim, float(rope_theta), float(softmax_scale), _ptr(workspace),
+                                   int(workspace_bytes), _stream(stream)))
+
+
+def spec_verify_accept_workspace_size(batch, block, gamma, vocab) -> int:
+    return int(load().spec_verify_accept_workspace_size(batch, block, gamma, vocab))
+
+
+def spec_verify_accept(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma, vocab,
+                       accept_len, out_tokens, alpha, workspace, workspace_bytes, stream=None) -> None:
+    _check(load().spec_verify_accept(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(tau),
+                                     _ptr(uniforms), batch, block, gamma, vocab, _ptr(accept_len),
+                                     _ptr(out_tokens), _ptr(alpha), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream)))

@@ -1,0 +1,116 @@
+// abi.hip -- extern "C" entry points of libspecverify.so: host-side argument
+// checks, workspace sizing and launches on the caller's stream.  No entry
+// point allocates, synchronises or keeps state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+#include "sv_internal.h"
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int dtype, int batch, int block, int n_qh, int n_kvh, int head_dim, int prefix) {
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_E_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return SV_E_UNSUPPORTED;
+    if (batch < 1 || block < 1 || block > 64 || n_qh < 1 || n_kvh < 1 || prefix < 0) return SV_E_SHAPE;
+    if (n_qh % n_kvh) return SV_E_SHAPE;
+    // index arithmetic of the kernels stays within 32-bit grid sizes
+    if ((long long)batch * 2 * block * n_qh > (1ll << 30)) return SV_E_SHAPE;
+    if ((long long)prefix + 2 * block > (1ll << 30)) return SV_E_SHAPE;
+    return SV_OK;
+}
+
+int map_launch(hipError_t e) { return e == hipSuccess ? SV_OK : SV_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_abi_version(void) { return SPEC_VERIFY_ABI_VERSION; }
+
+const char *spec_verify_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_E_NULL: return "a required pointer is NULL";
+        case SV_E_SHAPE: return "a size is out of range or inconsistent";
+        case SV_E_UNSUPPORTED: return "unsupported dtype or head_dim";
+        case SV_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case SV_E_WORKSPACE: return "workspace missing or too small";
+        case SV_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int spec_verify_rope(const void *q_in, const void *k_in, void *q_out, void *k_out, int dtype, int batch,
+                     int block, int n_qh, int n_kvh, int head_dim, int prefix_len, double theta,
+                     void *stream) {
+    int rc = check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, prefix_len);
+    if (rc) return rc;
+    if (!q_in || !k_in || !q_out || !k_out) return SV_E_NULL;
+    if (!(theta > 0) || !isfinite(theta)) return SV_E_SHAPE;
+    if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out)) return SV_E_ALIGN;
+    return map_launch(sv::launch_rope(q_in, k_in, q_out, k_out, dtype, batch, block, n_qh, n_kvh, head_dim,
+                                      prefix_len, theta, (hipStream_t)stream));
+}
+
+size_t spec_verify_attn_workspace_size(int dtype, int batch, int block, int prefix_len, int n_qh, int n_kvh,
+                                       int head_dim) {
+    if (check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, prefix_len)) return 0;
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim};
+    return sv::attn_plan(s).ws_total;
+}
+
+int spec_verify_attn(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                     const void *v_cache, const int32_t *tau, void *out, int dtype, int batch, int block,
+                     int prefix_len, int n_qh, int n_kvh, int head_dim, double rope_theta,
+                     float softmax_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, prefix_len);
+    if (rc) return rc;
+    if (!q || !k_new || !v_new || !tau || !out) return SV_E_NULL;
+    if (prefix_len > 0 && (!k_cache || !v_cache)) return SV_E_NULL;
+    if (!isfinite(rope_theta) || !isfinite(softmax_scale)) return SV_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(tau))
+        return SV_E_ALIGN;
+    if (prefix_len > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return SV_E_ALIGN;
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim};
+    const sv::AttnPlan p = sv::attn_plan(s);
+    const bool need_ws = (dtype == SV_BF16) ? p.n_split > 1 : rope_theta > 0;
+    if (need_ws && (!workspace || workspace_bytes < p.ws_total)) return SV_E_WORKSPACE;
+    if (need_ws && !aligned16(workspace)) return SV_E_ALIGN;
+    const float scale = softmax_scale > 0 ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+    return map_launch(sv::launch_attn(s, p, q, k_new, v_new, k_cache, v_cache, tau, out, rope_theta, scale,
+                                      workspace, (hipStream_t)stream));
+}
+
+size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab >= (1ll << 31))
+        return 0;
+    return sv::accept_plan(batch, block, gamma, vocab).ws_total;
+}
+
+int spec_verify_accept(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                       const int32_t *tau, const float *uniforms, int batch, int block, int gamma,
+                       int64_t vocab, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab >= (1ll << 31))
+        return SV_E_SHAPE;
+    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!target_logits || !draft_probs || !draft_tokens || !tau || !uniforms || !accept_len || !out_tokens)
+        return SV_E_NULL;
+    if (!aligned16(target_logits) || !aligned16(draft_probs) || !aligned16(draft_tokens) || !aligned16(tau) ||
+        !aligned16(uniforms) || !aligned16(accept_len) || !aligned16(out_tokens) || (alpha && !aligned16(alpha)))
+        return SV_E_ALIGN;
+    const sv::AcceptPlan p = sv::accept_plan(batch, block, gamma, vocab);
+    if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
+    if (!aligned16(workspace)) return SV_E_ALIGN;
+    return map_launch(sv::launch_accept(p, target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block,
+                                        gamma, vocab, accept_len, out_tokens, alpha, workspace,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

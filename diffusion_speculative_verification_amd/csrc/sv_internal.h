@@ -1,0 +1,59 @@
+// sv_internal.h -- host-side plans and launchers shared by the translation
+// units of libspecverify.so (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kTileKeys = 64;        // keys per attention tile
+constexpr int kRowsPerWave = 64;     // query rows per wave (two 32-row MFMA blocks)
+constexpr int kRowsPerBlock = 256;   // 4 waves
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct AttnShape {
+    int dtype, batch, block, prefix, n_qh, n_kvh, head_dim;
+};
+
+struct AttnPlan {
+    int rows;            // rows per kv head = (n_qh / n_kvh) * 2 * block
+    int n_rb;            // row blocks of 256 rows per kv head
+    int n_tiles;         // key tiles over prefix + 2 * block keys
+    int n_split;         // prefix splits (1 = no combine pass)
+    int tiles_per_split;
+    size_t ws_partial_o;   // bytes of split partial outputs (float32)
+    size_t ws_partial_ml;  // bytes of split (max, sum) pairs
+    size_t ws_rope;        // bytes of rotated q/k copies (float32 path)
+    size_t ws_total;
+};
+
+AttnPlan attn_plan(const AttnShape &s);
+
+hipError_t launch_rope(const void *q_in, const void *k_in, void *q_out, void *k_out, int dtype,
+                       int batch, int block, int n_qh, int n_kvh, int head_dim, int prefix,
+                       double theta, hipStream_t st);
+
+hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, const void *k_new,
+                       const void *v_new, const void *k_cache, const void *v_cache,
+                       const int32_t *tau, void *out, double theta, float scale, void *ws,
+                       hipStream_t st);
+
+struct AcceptPlan {
+    int rows;        // batch * block logits rows
+    int n_vsplit;    // vocab splits of the normaliser pass
+    int64_t chunk;   // vocab elements per residual chunk
+    int n_chunk;
+    size_t off_part, off_res, off_chunk, off_ticket, ws_total;
+};
+
+AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab);
+
+hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *probs,
+                         const int32_t *tokens, const int32_t *tau, const float *u, int batch,
+                         int block, int gamma, int64_t vocab, int32_t *accept_len,
+                         int32_t *out_tokens, float *alpha, void *ws, hipStream_t st);
+
+}  // namespace sv

@@ -1,0 +1,77 @@
+"""Device buffers for one verification step (torch is used for device memory
+and streams only) and the step itself as three library calls."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as sv
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class StepBuffers:
+    """Inputs of a Case resident in HBM, plus outputs and workspaces.
+
+    ``inputs`` is the dict made by ``synth.make_inputs``; float32 arrays of
+    bf16 cases hold bf16-representable values, so the device conversion is
+    exact.
+    """
+
+    def __init__(self, case, inputs: dict, device="cuda", parts=("attn", "accept")):
+        torch = _torch()
+        self.case = case
+        self.device = device
+        c = case
+        dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        self.dtype_code = sv.SV_BF16 if c.dtype == "bf16" else sv.SV_F32
+
+        def up(a, to=None):
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+            return t.to(to) if to is not None else t
+
+        self.tau = up(inputs["tau"])
+        if "attn" in parts:
+            self.q = up(inputs["q"], dt)
+            self.k_new = up(inputs["k_new"], dt)
+            self.v_new = up(inputs["v_new"], dt)
+            self.k_cache = up(inputs["k_cache"], dt)
+            self.v_cache = up(inputs["v_cache"], dt)
+            self.out = torch.empty_like(self.q)
+            n = sv.spec_verify_attn_workspace_size(self.dtype_code, c.batch, c.block, c.prefix_len, c.n_qh,
+                                                   c.n_kvh, c.head_dim)
+            self.attn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.attn_ws_bytes = n
+        if "accept" in parts:
+            self.target_logits = up(inputs["target_logits"])
+            self.draft_probs = up(inputs["draft_probs"])
+            self.draft_tokens = up(inputs["draft_tokens"])
+            self.uniforms = up(inputs["uniforms"])
+            self.accept_len = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.out_tokens = torch.empty((c.batch, c.block), dtype=torch.int32, device=device)
+            self.alpha = torch.empty((c.batch, c.gamma), dtype=torch.float32, device=device)
+            n = sv.spec_verify_accept_workspace_size(c.batch, c.block, c.gamma, c.vocab)
+            self.acc_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.acc_ws_bytes = n
+
+    def attn(self, rope_theta=None, stream=None, q=None, k_new=None):
+        c = self.case
+        theta = c.theta if rope_theta is None else rope_theta
+        sv.spec_verify_attn(self.q if q is None else q, self.k_new if k_new is None else k_new, self.v_new,
+                            self.k_cache, self.v_cache, self.tau, self.out, self.dtype_code, c.batch, c.block,
+                            c.prefix_len, c.n_qh, c.n_kvh, c.head_dim, theta, 0.0, self.attn_ws,
+                            self.attn_ws_bytes, stream)
+
+    def accept(self, stream=None):
+        c = self.case
+        sv.spec_verify_accept(self.target_logits, self.draft_probs, self.draft_tokens, self.tau, self.uniforms,
+                              c.batch, c.block, c.gamma, c.vocab, self.accept_len, self.out_tokens, self.alpha,
+                              self.acc_ws, self.acc_ws_bytes, stream)
+
+    def step(self, stream=None):
+        """One verification step: attention with fused copy-aligned RoPE,
+        then the acceptance epilogue."""
+        self.attn(stream=stream)
+        self.accept(stream=stream)

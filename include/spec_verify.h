@@ -1,0 +1,146 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify.so: the single-forward speculative
+ * verification step of a block-diffusion language model on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The step (one transformer attention layer's worth of it plus the
+ * verification epilogue) as described on the page "SimSD: Simple Speculative
+ * Decoding in Diffusion Language Models":
+ *   - 关键设计 1: after the cached prompt come B data slots D_1..D_B (draft
+ *     tokens) and B mask slots D~_1..D~_B; D~_k is the slot whose output
+ *     verifies slot k.  Response rows are numbered r = 0..2B-1: r < B is
+ *     D_{r+1}, r >= B is D~_{r-B+1}.
+ *   - 关键设计 2: step labels tau(k) in 1..B (a permutation; the prompt has
+ *     label 0) and the temporal-causal mask A_ij.
+ *   - 关键设计 3: RoPE in which D~_k reuses the position of D_k; the prompt
+ *     uses positions 0..P-1 and slot k uses P + k (0-based k).
+ *   - 关键设计 4: acceptance alpha_r = min(1, p_theta/p_phi) in draft order,
+ *     the longest accepted prefix, and a resample at the first rejection from
+ *     the residual (P_target - P_draft)^+ (page "S2D2: Fast Decoding for
+ *     Diffusion LLMs via Training-Free Self-Speculation", 方法步骤 (5)).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller,
+ *     contiguous, row-major and 16-byte aligned.  The library allocates no
+ *     memory, keeps no state between calls, never synchronises the device
+ *     and is reentrant; scratch memory comes in through `workspace`.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream).  A call returns once the work is enqueued.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     non-zero status nothing is enqueued and no output is touched.
+ *     SV_E_LAUNCH reports a launch the runtime refused.
+ *   - tau being a permutation of 1..block is a precondition (not checked on
+ *     the device).
+ *   - dtype SV_BF16: bfloat16 tensors, bf16 MFMA with fp32 accumulation.
+ *     dtype SV_F32: float32 tensors and float32 arithmetic throughout.
+ *   - Shape limits: 1 <= block <= 64, n_qh % n_kvh == 0, head_dim in
+ *     {64, 128}, prefix_len >= 0, batch >= 1; accept: 1 <= gamma <= block,
+ *     1 <= vocab < 2^31.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_VERIFY_ABI_VERSION 1
+
+enum {
+    SV_OK = 0,
+    SV_E_NULL = -1,        /* a required pointer is NULL                  */
+    SV_E_SHAPE = -2,       /* a size is out of range or inconsistent      */
+    SV_E_UNSUPPORTED = -3, /* dtype / head_dim not provided by the library */
+    SV_E_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned     */
+    SV_E_WORKSPACE = -5,   /* workspace missing or smaller than required  */
+    SV_E_LAUNCH = -6       /* the HIP runtime refused a kernel launch     */
+};
+
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+/* Returns SPEC_VERIFY_ABI_VERSION of the built library. */
+int spec_verify_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *spec_verify_status_string(int status);
+
+/*
+ * Copy-aligned RoPE (SimSD 关键设计 3) of the 2B response rows.
+ *   q_in  [batch][2*block][n_qh][head_dim], k_in [batch][2*block][n_kvh][head_dim]
+ *   q_out, k_out: same shapes; may equal q_in / k_in (in place).
+ * Row r is rotated at position prefix_len + (r mod block), rotate-half pairs
+ * (i, i + head_dim/2) turning by pos * theta^(-2i/head_dim); angles are
+ * formed in float64.  theta > 0.
+ */
+int spec_verify_rope(const void *q_in, const void *k_in, void *q_out, void *k_out, int dtype,
+                     int batch, int block, int n_qh, int n_kvh, int head_dim, int prefix_len,
+                     double theta, void *stream);
+
+/* Bytes of workspace spec_verify_attn needs for these sizes and dtype. */
+size_t spec_verify_attn_workspace_size(int dtype, int batch, int block, int prefix_len, int n_qh,
+                                       int n_kvh, int head_dim);
+
+/*
+ * Masked GQA attention of the 2B response rows over [prompt KV | D | D~]
+ * (SimSD 关键设计 1-3).
+ *   q      [batch][2*block][n_qh][head_dim]
+ *   k_new, v_new [batch][2*block][n_kvh][head_dim]   (response keys/values)
+ *   k_cache, v_cache [batch][n_kvh][prefix_len][head_dim] (prompt KV, keys
+ *          already rotated at positions 0..prefix_len-1; may be NULL when
+ *          prefix_len == 0)
+ *   tau    [batch][block] int32, step labels 1..block
+ *   out    [batch][2*block][n_qh][head_dim] in dtype
+ * rope_theta > 0: q and k_new are raw and are rotated on the fly with the
+ * copy-aligned positions (as spec_verify_rope would); rope_theta <= 0: q and
+ * k_new are taken as already rotated.  softmax_scale <= 0 means
+ * 1/sqrt(head_dim).  Query head h reads kv head h / (n_qh / n_kvh).
+ * Response row i sees key j iff j is a prompt key, or j is a response key
+ * and the four-case mask admits it.
+ */
+int spec_verify_attn(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                     const void *v_cache, const int32_t *tau, void *out, int dtype, int batch,
+                     int block, int prefix_len, int n_qh, int n_kvh, int head_dim,
+                     double rope_theta, float softmax_scale, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace spec_verify_accept needs for these sizes. */
+size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab);
+
+/*
+ * Verification epilogue (SimSD 关键设计 4; S2D2 方法步骤 (5)).
+ *   target_logits [batch][block][vocab] float32: target logits of each
+ *                 slot's D~ row (slot order)
+ *   draft_probs   [batch][block][vocab] float32: the draft distribution
+ *                 p_phi of each slot
+ *   draft_tokens  [batch][block] int32 in [0, vocab)
+ *   tau           [batch][block] int32 step labels 1..block
+ *   uniforms      [batch][gamma+1] float32 in [0,1): uniforms[r-1] tests
+ *                 draft step r, uniforms[gamma] drives the resample
+ * Draft step r = 1..gamma verifies the slot o_r with tau(o_r) = r:
+ * p_theta = softmax(target_logits[o_r]) (normaliser accumulated in float64),
+ * alpha_r = min(1, p_theta(x)/p_phi(x)) for x = draft_tokens[o_r] (alpha = 1
+ * when p_phi(x) = 0); step r is accepted iff uniforms[r-1] < alpha_r.
+ * Outputs:
+ *   accept_len [batch]: L = number of leading accepted steps (0..gamma)
+ *   out_tokens [batch][block]: the draft token for slots with tau <= L; for
+ *     the slot with tau = L+1 (only when L < gamma) the resampled token: the
+ *     smallest v whose running sum of r(v) = max(0, p_theta(v) - p_phi(v))
+ *     in ascending token order exceeds uniforms[gamma] * sum_v r(v) (p_theta
+ *     itself when that sum is zero); -1 for every other slot
+ *   alpha [batch][gamma] float32 (may be NULL): alpha_r of every step, in
+ *     draft order
+ */
+int spec_verify_accept(const float *target_logits, const float *draft_probs,
+                       const int32_t *draft_tokens, const int32_t *tau, const float *uniforms,
+                       int batch, int block, int gamma, int64_t vocab, int32_t *accept_len,
+                       int32_t *out_tokens, float *alpha, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

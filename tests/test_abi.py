@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+its host-side argument checks return the documented status codes without
+touching a GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_speculative_verification_amd import binding as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert sv.spec_verify_abi_version() == 1
+    for code in range(0, -7, -1):
+        assert sv.spec_verify_status_string(code)
+    assert sv.spec_verify_status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    # bf16 headline shape needs no split; the long-prefix shape splits
+    assert sv.spec_verify_attn_workspace_size(1, 32, 32, 2048, 32, 8, 128) == 0
+    assert sv.spec_verify_attn_workspace_size(1, 4, 32, 16384, 32, 8, 128) > 0
+    assert sv.spec_verify_attn_workspace_size(0, 1, 8, 32, 4, 4, 64) > 0   # fp32 rope copies
+    assert sv.spec_verify_attn_workspace_size(1, 1, 8, 32, 4, 4, 96) == 0  # unsupported -> 0
+    assert sv.spec_verify_accept_workspace_size(32, 32, 32, 151936) > 0
+    assert sv.spec_verify_accept_workspace_size(32, 32, 33, 151936) == 0  # gamma > block
+
+
+A = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced
+
+
+def attn(lib, **kw):
+    args = dict(q=A, k_new=A, v_new=A, k_cache=A, v_cache=A, tau=A, out=A, dtype=1, batch=1, block=8,
+                prefix=32, n_qh=4, n_kvh=4, head_dim=64, theta=1e4, scale=0.0, ws=A, ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.spec_verify_attn(args["q"], args["k_new"], args["v_new"], args["k_cache"], args["v_cache"],
+                                args["tau"], args["out"], args["dtype"], args["batch"], args["block"],
+                                args["prefix"], args["n_qh"], args["n_kvh"], args["head_dim"], args["theta"],
+                                args["scale"], args["ws"], args["ws_bytes"], None)
+
+
+def test_attn_argument_checks(lib):
+    assert attn(lib, q=None) == sv.SV_E_NULL
+    assert attn(lib, k_cache=None) == sv.SV_E_NULL
+    assert attn(lib, head_dim=96) == sv.SV_E_UNSUPPORTED
+    assert attn(lib, dtype=7) == sv.SV_E_UNSUPPORTED
+    assert attn(lib, n_qh=6, n_kvh=4) == sv.SV_E_SHAPE
+    assert attn(lib, block=65) == sv.SV_E_SHAPE
+    assert attn(lib, block=0) == sv.SV_E_SHAPE
+    assert attn(lib, prefix=-1) == sv.SV_E_SHAPE
+    assert attn(lib, q=A + 8) == sv.SV_E_ALIGN
+    assert attn(lib, dtype=0, ws=None) == sv.SV_E_WORKSPACE  # fp32 + rope needs workspace
+    assert attn(lib, dtype=0, ws_bytes=16) == sv.SV_E_WORKSPACE
+    assert attn(lib, batch=4, prefix=16384, block=32, n_qh=32, n_kvh=8, head_dim=128, ws=None) == sv.SV_E_WORKSPACE
+
+
+def accept(lib, **kw):
+    args = dict(tl=A, dp=A, dt=A, tau=A, u=A, batch=2, block=8, gamma=8, vocab=512, L=A, ot=A, al=A, ws=A,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.spec_verify_accept(args["tl"], args["dp"], args["dt"], args["tau"], args["u"], args["batch"],
+                                  args["block"], args["gamma"], args["vocab"], args["L"], args["ot"], args["al"],
+                                  args["ws"], args["ws_bytes"], None)
+
+
+def test_accept_argument_checks(lib):
+    assert accept(lib, tl=None) == sv.SV_E_NULL
+    assert accept(lib, L=None) == sv.SV_E_NULL
+    assert accept(lib, gamma=9) == sv.SV_E_SHAPE
+    assert accept(lib, gamma=0) == sv.SV_E_SHAPE
+    assert accept(lib, vocab=0) == sv.SV_E_SHAPE
+    assert accept(lib, block=65, gamma=8) == sv.SV_E_SHAPE
+    assert accept(lib, u=A + 4) == sv.SV_E_ALIGN
+    assert accept(lib, ws=None) == sv.SV_E_WORKSPACE
+    assert accept(lib, ws_bytes=8) == sv.SV_E_WORKSPACE
+
+
+def test_rope_argument_checks(lib):
+    f = lib.spec_verify_rope
+    assert f(None, A, A, A, 1, 1, 8, 4, 4, 64, 32, 1e4, None) == sv.SV_E_NULL
+    assert f(A, A, A, A, 1, 1, 8, 4, 4, 64, 32, 0.0, None) == sv.SV_E_SHAPE
+    assert f(A, A, A, A, 1, 1, 8, 4, 4, 80, 32, 1e4, None) == sv.SV_E_UNSUPPORTED
+    assert f(A, A, A + 2, A, 1, 1, 8, 4, 4, 64, 32, 1e4, None) == sv.SV_E_ALIGN
+
+
+def test_binding_raises(lib):
+    with pytest.raises(sv.SpecVerifyError) as ei:
+        sv.spec_verify_rope(None, A, A, A, 1, 1, 8, 4, 4, 64, 32, 1e4, stream=0)
+    assert ei.value.status == sv.SV_E_NULL

@@ -1,0 +1,181 @@
+"""HIP path vs the CPU oracle, through the C-ABI, on the same seeded inputs.
+
+Small cases are compared element by element in full; the five workloads run
+at full size in the launch configuration the benchmark times, compared on
+sampled sequences (every head, row and slot of each sampled sequence)."""
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from diffusion_speculative_verification_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.Oracle()
+
+
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run(case, inp, parts=("attn", "accept"), rope_theta=None):
+    from diffusion_speculative_verification_amd.device import StepBuffers
+    buf = StepBuffers(case, inp, parts=parts)
+    if "attn" in parts:
+        buf.attn(rope_theta=rope_theta)
+    if "accept" in parts:
+        buf.accept()
+    torch.cuda.synchronize()
+    res = {}
+    if "attn" in parts:
+        res["out"] = buf.out.float().cpu().numpy()
+    if "accept" in parts:
+        res["L"] = buf.accept_len.cpu().numpy()
+        res["tok"] = buf.out_tokens.cpu().numpy()
+        res["alpha"] = buf.alpha.cpu().numpy()
+    return res
+
+
+def oracle_attn(o, case, inp, b, theta=None):
+    th = case.theta if theta is None else theta
+    return o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
+                       inp["tau"][b], th)
+
+
+def check_case(o, case, attn_seqs=None, acc_seqs=None, rope_theta=None):
+    print(f"[case] {case}", flush=True)
+    _cuda()
+    inp = synth.make_inputs(case)
+    res = run(case, inp, rope_theta=rope_theta)
+    seqs = range(case.batch) if attn_seqs is None else attn_seqs
+    worst = (0.0, 0.0)
+    for b in seqs:
+        ref = oracle_attn(o, case, inp, b, theta=rope_theta)
+        mx, rel = parity.check_attn(res["out"][b], ref, case.dtype, f"{case.name} seq {b}")
+        worst = (max(worst[0], mx), max(worst[1], rel))
+    ties = parity.check_accept(o, inp, case.gamma, res["L"], res["tok"], res["alpha"], acc_seqs)
+    print(f"[result] {case.name}: attn max {worst[0]:.3e} relrms {worst[1]:.3e}; accept ties {ties}; "
+          f"mean accept_len {res['L'].mean():.2f}", flush=True)
+    return res
+
+
+# ---------------------------------------------------------------- workloads
+def test_tiny_fp32(o):
+    check_case(o, synth.config_by_name("tiny"))
+
+
+def test_small_bf16(o):
+    check_case(o, synth.config_by_name("small"), attn_seqs=[0, 5])
+
+
+def test_headline_bf16(o):
+    check_case(o, synth.config_by_name("headline"), attn_seqs=[0, 17, 31])
+
+
+def test_longprefix_bf16(o):
+    check_case(o, synth.config_by_name("longprefix"), attn_seqs=[2])
+
+
+def test_wide_bf16(o):
+    # sequence 7 uses tau = identity (the 2L view), 0 a random order
+    check_case(o, synth.config_by_name("wide"), attn_seqs=[0, 7], acc_seqs=range(0, 64, 4))
+
+
+# --------------------------------------------------------------- edge cases
+SMALL = synth.Case("edge", 3, 100, 8, 8, 8, 2, 128, 1000, "bf16", 1e6, "perturb", 3.0, 1.0, 0, seed=50)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(prefix_len=0),                        # no prompt: only response keys
+    dict(prefix_len=100),                      # ragged tail tile (100 + 16 keys)
+    dict(prefix_len=64, block=1, gamma=1),     # B = 1
+    dict(gamma=5),                             # gamma < B: slots tau > gamma stay -1
+    dict(head_dim=64),                         # head_dim 64 bf16
+    dict(n_qh=8, n_kvh=8),                     # no GQA grouping
+    dict(n_qh=16, n_kvh=2, block=64, gamma=64, prefix_len=200),  # two row blocks per kv head
+    dict(vocab=1001),                          # vocab not a multiple of 4
+    dict(vocab=1),                             # one token: always accepted
+    dict(batch=1, prefix_len=5000, block=16, gamma=16),  # split prefix + combine
+    dict(dtype="f32", head_dim=64, n_qh=4, n_kvh=2, prefix_len=70),
+    dict(dtype="f32", head_dim=128, prefix_len=0, block=4, gamma=4),
+    dict(identity_every=1),                    # every sequence tau = identity
+    dict(logit_model="iid", target_var=2.0, draft_var=2.0),
+], ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_edge(o, kw):
+    check_case(o, SMALL.with_(**kw))
+
+
+def test_pre_rotated_inputs(o):
+    """rope_theta <= 0: inputs taken as already rotated (no rotation on
+    either side)."""
+    check_case(o, SMALL.with_(prefix_len=37), rope_theta=0.0)
+    check_case(o, SMALL.with_(dtype="f32", head_dim=64, prefix_len=37), rope_theta=0.0)
+
+
+def test_all_accepted_and_all_rejected(o):
+    _cuda()
+    case = SMALL.with_(vocab=4096)
+    inp = synth.make_inputs(case)
+    # identical target and draft distributions: every step accepted
+    p = np.exp(inp["target_logits"].astype(np.float64))
+    inp["draft_probs"] = (p / p.sum(axis=2, keepdims=True)).astype(np.float32)
+    inp["uniforms"][:] = np.float32(0.5)
+    res = run(case, inp, parts=("accept",))
+    parity.check_accept(o, inp, case.gamma, res["L"], res["tok"], res["alpha"])
+    assert (res["L"] == case.gamma).all()
+    # draft tokens with zero target mass: rejected at step 1
+    inp["target_logits"][:, :, :] = np.float32(0.0)
+    for b in range(case.batch):
+        for k in range(case.block):
+            inp["target_logits"][b, k, inp["draft_tokens"][b, k]] = np.float32(-3e38)
+    res = run(case, inp, parts=("accept",))
+    parity.check_accept(o, inp, case.gamma, res["L"], res["tok"], res["alpha"])
+    assert (res["L"] == 0).all()
+
+
+def test_standalone_rope(o):
+    """spec_verify_rope, out of place and in place, against the oracle."""
+    _cuda()
+    from diffusion_speculative_verification_amd import binding as sv
+    for dt in ("f32", "bf16"):
+        case = SMALL.with_(dtype=dt, prefix_len=16000)
+        inp = synth.make_inputs(case, parts=("attn",))
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        q = torch.from_numpy(inp["q"]).cuda().to(tdt)
+        k = torch.from_numpy(inp["k_new"]).cuda().to(tdt)
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+        code = sv.SV_BF16 if dt == "bf16" else sv.SV_F32
+        args = (code, case.batch, case.block, case.n_qh, case.n_kvh, case.head_dim, case.prefix_len, case.theta)
+        sv.spec_verify_rope(q, k, qo, ko, *args)
+        sv.spec_verify_rope(q, k, q, k, *args)  # in place
+        torch.cuda.synchronize()
+        R = 2 * case.block
+        pos = case.prefix_len + (np.arange(R) % case.block).astype(np.float64)
+        for name, g, g2, raw in (("q", qo, q, inp["q"]), ("k", ko, k, inp["k_new"])):
+            gout = g.float().cpu().numpy()
+            assert np.array_equal(gout, g2.float().cpu().numpy()), "in place differs from out of place"
+            for b in range(case.batch):
+                ref = o.rope(raw[b], pos, case.theta)
+                err = np.abs(gout[b] - ref)
+                tol = 1e-5 if dt == "f32" else 2.0 ** -8 * np.abs(ref) + 1e-6
+                assert (err <= tol).all(), (dt, name, b, float(err.max()))
+
+
+def test_repeat_runs_bit_identical(o):
+    """Two runs of the same step give identical bytes (no LDS or reduction
+    races)."""
+    _cuda()
+    case = synth.config_by_name("small")
+    inp = synth.make_inputs(case)
+    a = run(case, inp)
+    b = run(case, inp)
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["L"], b["L"]) and np.array_equal(a["tok"], b["tok"])
+    assert np.array_equal(a["alpha"], b["alpha"])

@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-forward speculative verification step on one GPU.
+
+One step = the whole hot path on one batch of synthetic input already
+resident in HBM: masked GQA attention of the 2B response rows with the
+copy-aligned RoPE fused into its loads (spec_verify_attn), then the
+verification epilogue (spec_verify_accept: per-slot softmax normaliser,
+acceptance in draft order, residual resample).  Metric: verified draft slots
+per second = batch * gamma / step time.
+
+Default workload: batch 32, cached prefix 2048, block B = gamma = 32, 32
+query / 8 KV heads, head_dim 128, vocab 151936, bf16 attention inputs,
+float32 logits.  Two copies of the inputs live in HBM and steps alternate
+between them, so a step never finds the previous step's data in the 256 MB
+last-level cache.
+
+Prints ONE JSON line (rank 0, N = 1).  Also reports the roofline of the
+dominant call (timed live with HIP events on the launch stream) and the CPU
+oracle timed on this host over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft slots/sec (attn+accept), B=32 prefix 2048; % of roofline"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def attn_bytes(c) -> float:
+    """Algorithmic HBM bytes of one attention call: prompt K/V cache, Q,
+    response K/V and the output, each read or written once."""
+    e = 2 if c.dtype == "bf16" else 4
+    R = 2 * c.block
+    return e * (2 * c.batch * c.n_kvh * c.prefix_len * c.head_dim
+                + c.batch * R * c.n_qh * c.head_dim * 2
+                + 2 * c.batch * R * c.n_kvh * c.head_dim)
+
+
+def attn_flops(c) -> float:
+    """Algorithmic FLOPs: every response row attends to exactly P + B keys
+    (QK^T and PV, 2 flops per multiply-add)."""
+    return 4.0 * c.batch * 2 * c.block * c.n_qh * c.head_dim * (c.prefix_len + c.block)
+
+
+def accept_bytes(c, n_rejecting: int) -> float:
+    """Algorithmic HBM bytes of one epilogue call: the float32 target logits
+    of every verified slot once, plus for each sequence that rejects the
+    target and draft rows of the rejected slot, plus the per-step gathers
+    (logit and draft probability of each draft token), tau, tokens,
+    uniforms and outputs."""
+    V = c.vocab
+    small = c.batch * (c.block * 4 * 3 + (c.gamma + 1) * 4 + c.gamma * 4 * 3 + 4)
+    return 4.0 * c.batch * c.gamma * V + n_rejecting * 2 * 4.0 * V + small
+
+
+def cpu_baseline(case, inp) -> dict:
+    """The CPU oracle on this host over the same workload (one step)."""
+    import oracle
+    o = oracle.Oracle()
+    threads = o.max_threads()
+    t = time.perf_counter()
+    for b in range(case.batch):
+        o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
+                    inp["tau"][b], case.theta)
+    t_attn = time.perf_counter() - t
+    t = time.perf_counter()
+    o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"], inp["uniforms"],
+             case.gamma)
+    t_acc = time.perf_counter() - t
+    total = t_attn + t_acc
+    return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step of the same workload ({case.batch} sequences): attention "
+                      f"{t_attn:.2f} s + accept {t_acc:.2f} s on {threads} OpenMP threads "
+                      f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the verification step is sharded across GPUs only by design, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibrate:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "reps": 5}))
+        return
+
+    from diffusion_speculative_verification_amd import synth
+    from diffusion_speculative_verification_amd.device import StepBuffers
+
+    case = synth.config_by_name(args.config)
+    inp = synth.make_inputs(case)
+    sets = [StepBuffers(case, inp), StepBuffers(case, inp)]
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        sets[i & 1].step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        s = sets[i & 1]
+        ev[i][0].record(stream)
+        s.attn()
+        ev[i][1].record(stream)
+        s.accept()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    ms_step = total_ms / K
+    attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
+    acc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
+    L = sets[0].accept_len.cpu()
+    n_rej = int((L < case.gamma).sum())
+    slots = case.batch * case.gamma
+    value = slots / (ms_step * 1e-3)
+
+    a_bytes, a_flops = attn_bytes(case), attn_flops(case)
+    c_bytes = accept_bytes(case, n_rej)
+    rl_attn = {"bound": "hbm", "achieved": a_bytes / (attn_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "tflops": a_flops / (attn_ms * 1e-3) / 1e12, "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+               "ms": attn_ms, "bytes": a_bytes}
+    rl_acc = {"bound": "hbm", "achieved": c_bytes / (acc_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "ms": acc_ms, "bytes": c_bytes}
+    for r in (rl_attn, rl_acc):
+        r["frac"] = r["achieved"] / r["peak"]
+    dom = ("spec_verify_accept", rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
+    roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
+        c_bytes / (HBM_PEAK_GBS * 1e9)
+    roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
+                "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": None,
+                "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, inp)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "slots/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{case.name} verify step: batch {case.batch}, prefix {case.prefix_len}, "
+                               f"B=gamma={case.block}, {case.n_qh}/{case.n_kvh} heads, head_dim {case.head_dim}, "
+                               f"vocab {case.vocab}, {case.dtype} attention, fp32 logits",
+                   "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
+                   "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "attn": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_attn.items()},
+            "accept": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_acc.items()},
+            "step_roofline_us": round(roof_step_s * 1e6, 2),
+            "frac_of_step_roofline": round(roof_step_s / (ms_step * 1e-3), 4),
+            "wall_s": round(wall, 4),
+            "mean_accept_len": float(L.float().mean()),
+            "rejecting_sequences": n_rej,
+        },
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

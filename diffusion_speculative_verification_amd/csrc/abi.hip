@@ -87,7 +87,7 @@ int spec_verify_attn(const void *q, const void *k_new, const void *v_new, const 
 
 size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
-        vocab >= (1ll << 31))
+        vocab > (1ll << 21))
         return 0;
     return sv::accept_plan(batch, block, gamma, vocab).ws_total;
 }
@@ -97,7 +97,7 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs, con
                        int64_t vocab, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
                        size_t workspace_bytes, void *stream) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
-        vocab >= (1ll << 31))
+        vocab > (1ll << 21))
         return SV_E_SHAPE;
     if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
     if (!target_logits || !draft_probs || !draft_tokens || !tau || !uniforms || !accept_len || !out_tokens)

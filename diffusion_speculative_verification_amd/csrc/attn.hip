@@ -5,13 +5,15 @@
 // 关键设计 1 (paired layout [prompt | D | D~]), 关键设计 2 (mask A_ij from step
 // labels tau), 关键设计 3 (D~_k reuses D_k's RoPE position).
 //
-// bf16 kernel (attn_bf16_kernel), one workgroup = 4 waves = 256 query rows of
-// one kv head (all n_qh/n_kvh query heads of the GQA group share the K/V tile
-// read, so every K/V byte of a (sequence, kv head) leaves HBM once per row
-// block), looping over 64-key tiles of [prompt | D | D~]:
+// bf16 kernel (attn_bf16_kernel), one workgroup = 4 waves x 32 query rows of
+// one kv head (the n_qh/n_kvh query heads of a GQA group are rows of the same
+// workgroup, so they share each K/V tile read; the row blocks of one kv head
+// run on the same XCD and meet its K/V in that XCD's L2), two workgroups per
+// CU, looping over 64-key tiles of [prompt | D | D~]:
 //   - K tile staged row-major in LDS, V tile staged transposed ([dim][key])
-//     so both MFMA operands are contiguous LDS reads; double-buffered, the
-//     next tile's global loads are in flight during the current tile's math;
+//     so both MFMA operands are contiguous LDS reads; the next tile's global
+//     loads are in flight during the current tile's math, and the other
+//     workgroup on the CU computes while this one refills LDS;
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on MFMA rows, queries
 //     on columns): each lane then owns one query's scores, so the row
 //     max/sum need one cross-lane exchange (lane ^ 32) per tile;
@@ -80,14 +82,21 @@ __global__ void __launch_bounds__(256) rope_kernel(const T *__restrict__ q_in, c
 }
 
 // ------------------------------------------------------- bf16 MFMA kernel
+// LDS tile layout: 64 rows (keys) x D bf16, rows of D*2 bytes, 16-byte
+// chunks XOR-swizzled per row so that both the S^T operand reads (16 B of one
+// row per lane, 8 consecutive rows per LDS cycle) and the transposed V reads
+// (8 B from 4 consecutive rows per 16-lane group) are bank-conflict free.
 template <int D>
-struct BfCfg {
-    static constexpr int NS = D / 16;         // 16-dim k-steps of S^T
-    static constexpr int NDB = D / 32;        // 32-dim blocks of O^T
-    static constexpr int KROW = D + 8;        // K tile row stride (bf16), 16 B pad
-    static constexpr int VROW = 34;           // V^T tile row stride (dwords): 64 keys + 2 pad dwords
-    static constexpr int NKI = D / 64;        // K load items per thread (2 chunks each)
-    static constexpr int NVI = D / 64;        // V load items per thread (2 keys each)
+struct Tile {
+    static constexpr int NCH = D / 8;             // 16-byte chunks per row
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int BYTES = kTileKeys * ROW_BYTES;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide 16 B/lane load fills
+    static constexpr int LOADS = kTileKeys / ROWS_PER_LOAD;  // wave loads per tile and tensor
+    __device__ static __forceinline__ int swz(int row) { return D == 128 ? ((row & 7) << 1) : (row & 7); }
+    __device__ static __forceinline__ int off(int row, int chunk) {  // byte offset of a logical chunk
+        return row * ROW_BYTES + ((chunk ^ swz(row)) << 4);
+    }
 };
 
 struct BfArgs {
@@ -106,28 +115,297 @@ template <int D>
 __device__ __forceinline__ const uint16_t *key_row(const BfArgs &a, const uint16_t *cache,
                                                    const uint16_t *fresh, int b, int kvh, int j) {
     const int R = 2 * a.block;
+    if (j >= a.prefix + R) j = a.prefix + R - 1;  // padding rows of the last tile: any valid row
     if (j < a.prefix) return cache + (((size_t)b * a.n_kvh + kvh) * a.prefix + j) * D;
-    if (j < a.prefix + R) return fresh + (((size_t)b * R + (j - a.prefix)) * a.n_kvh + kvh) * D;
-    return nullptr;
+    return fresh + (((size_t)b * R + (j - a.prefix)) * a.n_kvh + kvh) * D;
 }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define SV_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ uint16_t u4_elem(const uint4 &v, int e) {
     const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
     return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
+
+// Wave-wide direct global -> LDS copy of one tile of one tensor: load i of
+// wave w fills rows [r0, r0 + ROWS_PER_LOAD) with r0 = (w + NW * i) *
+// ROWS_PER_LOAD; lane l writes physical chunk l % NCH of its row and
+// therefore fetches the logical chunk that the swizzle places there.
+// One wave-wide direct global->LDS load: lane l's 16 bytes at `src` land at
+// LDS address lds_dst + 16 * l.  Issued as inline assembly so that the
+// compiler's wait insertion does not treat later LDS reads of other ring
+// stages as dependent on it: every wait on these loads is explicit
+// (wait_vmcnt), and no compiler-visible global load is issued while tile
+// loads are in flight inside the tile loop.
+__device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SV_LDS char *)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(src)
+                 : "memory", "m0");
+}
+
+// Keys at or past `jend` (the end of this workgroup's key range) read the
+// row jend - 1 instead: such tiles are never consumed, and re-reading one row
+// keeps them in cache.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache, const uint16_t *fresh,
+                                          int b, int kvh, int base, int jend, char *lds_tile, int w, int lane) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int i = 0; i < T::LOADS / NW; ++i) {
+        const int r0 = (w + NW * i) * T::ROWS_PER_LOAD;
+        const int row = r0 + lane / T::NCH, pc = lane % T::NCH;
+        const int q = pc ^ T::swz(row);
+        const uint16_t *src = key_row<D>(a, cache, fresh, b, kvh, min(base + row, jend - 1)) + q * 8;
+        direct_load16(src, lds_tile + r0 * T::ROW_BYTES);
+    }
+}
+
+// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
+// insertion knows about it (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the tile ring: this wave's LDS writes are complete
+// (lgkmcnt) before it arrives.  Unlike __syncthreads() it carries no
+// release fence, so the direct global->LDS loads of later tiles stay in
+// flight across it; each wave waits for its own loads of the current tile
+// (wait_vmcnt) before arriving, which makes that tile visible to all.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0), vmcnt/expcnt: no wait
+    __builtin_amdgcn_s_barrier();
+}
+
 template <int D>
-__global__ void __launch_bounds__(256, 1) attn_bf16_kernel(BfArgs a) {
-    using C = BfCfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys][C::KROW];
-    __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2][D][C::VROW];
+struct RowState {  // per-lane attention state of one query row
+    f32x16 oacc[D / 32];
+    float m_run, l_run;
+};
+
+// Rotate the 8-dim chunk pair (lo: dims 8c.., hi: dims 8c + D/2 ..) of one
+// row with cos/sin entries cs[0..7] (copy-aligned RoPE, rotate-half pairs).
+__device__ __forceinline__ void rotate_pair(uint4 &lo, uint4 &hi, const float2 *__restrict__ cs) {
+    uint32_t lw[4], hw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = 2 * e2 + u;
+            const float2 c = cs[e];
+            const float x1 = bf16_to_f32(u4_elem(lo, e)), x2 = bf16_to_f32(u4_elem(hi, e));
+            y1[u] = x1 * c.x - x2 * c.y;
+            y2[u] = x1 * c.y + x2 * c.x;
+        }
+        lw[e2] = pack_bf16x2(y1[0], y1[1]);
+        hw[e2] = pack_bf16x2(y2[0], y2[1]);
+    }
+    lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+}
+
+struct RowInfo {
+    int t_row;     // step label of the row's slot
+    bool is_data;  // D row (true) or D~ row
+};
+
+// One ring step.  Tile `it` sits in (kt, vt); the stage consumed in the
+// previous step, (kn, vn), is refilled with tile it + 2.  All LDS regions are
+// __restrict__ parameters of this inlined function, which lets the compiler
+// prove that the refill in flight never aliases this step's reads.
+template <int D, int NW>
+__device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t0, int nt, int it, bool wave_active,
+                                          const RowInfo &ri, const bf16x8 *qop, RowState<D> &st,
+                                          char *__restrict__ kt, char *__restrict__ vt, char *__restrict__ kn,
+                                          char *__restrict__ vn, const float2 *__restrict__ cs,
+                                          const int *__restrict__ taus) {
+    using T = Tile<D>;
+    constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
+    constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int B = a.block, P = a.prefix, Nk = P + 2 * B;
+    const int base = (t0 + it) * kTileKeys;
+    const int jend = min(Nk, (t0 + nt) * kTileKeys);
+    // the LPT most recent loads are the refill issued one step ago (tile
+    // it + 1); everything older, tile it included, has landed
+    wait_vmcnt<LPT>();
+    ring_barrier();
+    // ---- RoPE of response keys, in place in the K tile
+    if (a.use_rope && base + kTileKeys > P) {
+        for (int idx = tid; idx < kTileKeys * (T::NCH / 2); idx += NTH) {
+            const int row = idx / (T::NCH / 2), cp = idx % (T::NCH / 2);
+            const int j = base + row;
+            if (j < P || j >= Nk) continue;
+            uint4 *plo = reinterpret_cast<uint4 *>(kt + T::off(row, cp));
+            uint4 *phi = reinterpret_cast<uint4 *>(kt + T::off(row, cp + T::NCH / 2));
+            uint4 lo = *plo, hi = *phi;
+            rotate_pair(lo, hi, cs + ((j - P) % B) * (D / 2) + 8 * cp);
+            *plo = lo;
+            *phi = hi;
+        }
+        ring_barrier();
+    }
+    // ---- refill the stage consumed in the previous step (issued on every
+    // step, so the number of loads in flight is the same on every path)
+    {
+        const int nb = (t0 + it + 2) * kTileKeys;
+        load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
+        load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
+    }
+    if (!wave_active) return;
+
+    // ---- S^T = K Q^T (keys x queries): 2 key blocks of 32
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + T::off(kb * 32 + l32, 2 * s + h));
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], sacc[kb], 0, 0, 0);
+        }
+    }
+    // ---- temporal-causal mask, only where response / padding keys occur
+    if (base + kTileKeys > P) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int j = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3);
+                if (j >= P) {
+                    bool vis = false;
+                    if (j < Nk) {
+                        const int c = j - P;
+                        vis = visible(ri.t_row, ri.is_data, taus[c % B], c < B);
+                    }
+                    if (!vis) sacc[kb][x] = -INFINITY;
+                }
+            }
+        }
+    }
+    // ---- online softmax (log2 domain); each lane owns one query
+    bf16x8 pop[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[kb][x]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx * a.scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            bf16x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * sub + e], a.scale_log2, -m_use));
+                const __bf16 pb = (__bf16)p;
+                ls += (float)pb;
+                pv[e] = pb;
+            }
+            pop[2 * kb + sub] = pv;
+        }
+    }
+    st.l_run = st.l_run * alpha + ls;
+    st.m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) st.oacc[db][x] *= alpha;
+    }
+    // ---- O^T += V^T P^T: k-step s covers tile keys 16s..16s+15; lane half h
+    // supplies keys 16s+4h+{0..3} and 16s+8+4h+{0..3}.  V^T comes from the
+    // row-major V tile through the transposing LDS read: in 16-lane group gq,
+    // lane j = 4k + c reads row key(k) at dims dim0 + 4c, and lane i receives
+    // the four keys of dim dim0 + i.
+    const int gq = lane >> 4, jl = lane & 15;
+    const int v_dim_lo = 16 * (gq & 1) + 4 * (jl & 3);
+    const int v_key_lo = 4 * h + (jl >> 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int dim = 32 * db + v_dim_lo;
+            const int k0 = 16 * s + v_key_lo;
+            const int o0 = T::off(k0, dim >> 3) + ((dim & 7) << 1);
+            const int o1 = T::off(k0 + 8, dim >> 3) + ((dim & 7) << 1);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o1));
+            const v4i16 cat[2] = {lo, hi};
+            const bf16x8 va = __builtin_bit_cast(bf16x8, cat);
+            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[s], st.oacc[db], 0, 0, 0);
+        }
+    }
+}
+
+// Prologue: start the first two tiles' direct loads, build the RoPE table
+// and rotate this lane's query row.  LDS regions are __restrict__
+// parameters (see tile_step).
+template <int D, int NW>
+__device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v, uint4 *raw,
+                                         bool rvalid, int pos_idx, bf16x8 *qop, char *__restrict__ k0, char *__restrict__ v0,
+                                         char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
+                                         double *__restrict__ invf, int *__restrict__ taus) {
+    constexpr int NS = D / 16, NTH = 64 * NW;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
+    const int B = a.block, P = a.prefix;
+    // the first two tiles (every split has at least one; a second tile past
+    // the end reads clamped rows and is never consumed)
+    load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
+    load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
+    load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
+    load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
+    if (tid < B) taus[tid] = tau_v;
+    // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
+    if (a.use_rope) {
+        if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
+        ring_barrier();
+        for (int idx = tid; idx < B * (D / 2); idx += NTH) {
+            const int pr = idx / (D / 2), i = idx % (D / 2);
+            cs[idx] = rope_cs((double)P + (double)pr, invf[i]);
+        }
+    }
+    ring_barrier();
+    if (a.use_rope) {
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) rotate_pair(raw[s], raw[s + NS / 2], cs + pos_idx * (D / 2) + 16 * s + 8 * h);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, rvalid ? raw[s] : make_uint4(0, 0, 0, 0));
+}
+
+// NW waves x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles fed
+// by direct global->LDS loads.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
+    using T = Tile<D>;
+    constexpr int NS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int ROWS_B = 32 * NW;
+    // one LDS array per ring stage and tensor
+    __shared__ __attribute__((aligned(1024))) char k_st0[T::BYTES], k_st1[T::BYTES], k_st2[T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
     __shared__ __attribute__((aligned(16))) float2 cs_lds[64 * (D / 2)];
     __shared__ double invf_lds[D / 2];
     __shared__ int tau_lds[64];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int B = a.block, R2 = 2 * B, g = a.n_qh / a.n_kvh, R = g * R2;
-    const int P = a.prefix, Nk = P + R2;
 
     // workgroup -> (b, kvh, rb, split); consecutive logical ids land on one
     // XCD when the grid divides by 8, so row blocks / splits of one kv head
@@ -143,291 +421,82 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(BfArgs a) {
     const int b = rest / a.n_kvh;
     const int t0 = split * a.tiles_per_split;
     const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
+    const int nt = t1 - t0;
 
-    if (tid < B) tau_lds[tid] = a.tau[(size_t)b * B + tid];
-
-    // ---- global -> register staging of one K/V tile
-    uint4 kreg[C::NKI][2], vreg[C::NVI][2];
-    auto issue_loads = [&](int t) {
-        const int base = t * kTileKeys;
+    // ---- tau and this lane's query row (one 32-row MFMA block per wave):
+    // their loads go out before the tiles' so that waiting for them does not
+    // drain the tile loads
+    const int tau_v = a.tau[(size_t)b * B + min(tid, B - 1)];
+    const int rho = rb * ROWS_B + w * 32 + l32;
+    const bool rvalid = rho < R;
+    const int rr = rvalid ? rho : 0;
+    const int rrow = rr % R2;
+    const int qhead = kvh * g + rr / R2;
+    uint4 raw[NS];
+    {
+        const uint16_t *qp = a.q + (((size_t)b * R2 + rrow) * a.n_qh + qhead) * D + 8 * h;
 #pragma unroll
-        for (int s = 0; s < C::NKI; ++s) {
-            const int it = tid + 256 * s, key = it / (D / 16), cp = it % (D / 16);
-            const uint16_t *src = key_row<D>(a, a.k_cache, a.k_new, b, kvh, base + key);
-            if (src) {
-                kreg[s][0] = *reinterpret_cast<const uint4 *>(src + 8 * cp);
-                kreg[s][1] = *reinterpret_cast<const uint4 *>(src + 8 * cp + D / 2);
-            } else {
-                kreg[s][0] = make_uint4(0, 0, 0, 0);
-                kreg[s][1] = make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < C::NVI; ++s) {
-            const int c = (lane & 7) + 8 * s, kp = w * 8 + (lane >> 3);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint16_t *src = key_row<D>(a, a.v_cache, a.v_new, b, kvh, base + 2 * kp + u);
-                vreg[s][u] = src ? *reinterpret_cast<const uint4 *>(src + 8 * c) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto write_lds = [&](int buf, int t) {
-        const int base = t * kTileKeys;
-#pragma unroll
-        for (int s = 0; s < C::NKI; ++s) {
-            const int it = tid + 256 * s, key = it / (D / 16), cp = it % (D / 16);
-            const int j = base + key;
-            uint4 lo = kreg[s][0], hi = kreg[s][1];
-            if (a.use_rope && j >= P && j < Nk) {
-                const int pr = (j - P) % B;
-                uint32_t lw[4], hw[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float y1[2], y2[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = 2 * e2 + u;
-                        const float2 cs = cs_lds[pr * (D / 2) + 8 * cp + e];
-                        const float x1 = bf16_to_f32(u4_elem(lo, e)), x2 = bf16_to_f32(u4_elem(hi, e));
-                        y1[u] = x1 * cs.x - x2 * cs.y;
-                        y2[u] = x1 * cs.y + x2 * cs.x;
-                    }
-                    lw[e2] = pack_bf16x2(y1[0], y1[1]);
-                    hw[e2] = pack_bf16x2(y2[0], y2[1]);
-                }
-                lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-                hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            }
-            *reinterpret_cast<uint4 *>(&k_lds[buf][key][8 * cp]) = lo;
-            *reinterpret_cast<uint4 *>(&k_lds[buf][key][8 * cp + D / 2]) = hi;
-        }
-#pragma unroll
-        for (int s = 0; s < C::NVI; ++s) {
-            const int c = (lane & 7) + 8 * s, kp = w * 8 + (lane >> 3);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vt_lds[buf][8 * c + e][kp] =
-                    (uint32_t)u4_elem(vreg[s][0], e) | ((uint32_t)u4_elem(vreg[s][1], e) << 16);
-        }
-    };
-
-    if (t0 < t1) issue_loads(t0);
-
-    // ---- RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
-    if (a.use_rope) {
-        if (tid < D / 2) invf_lds[tid] = rope_inv_freq(tid, D, a.log2_theta);
-        __syncthreads();
-        for (int idx = tid; idx < B * (D / 2); idx += 256) {
-            const int pr = idx / (D / 2), i = idx % (D / 2);
-            cs_lds[idx] = rope_cs((double)P + (double)pr, invf_lds[i]);
-        }
+        for (int s = 0; s < NS; ++s) raw[s] = *reinterpret_cast<const uint4 *>(qp + 16 * s);  // rr is a valid row
     }
-    __syncthreads();
+    const int jend = min(a.prefix + R2, t1 * kTileKeys);
+    bf16x8 qop[NS];
+    prologue<D, NW>(a, b, kvh, t0, jend, tau_v, raw, rvalid, rrow % B, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
+                    invf_lds, tau_lds);
+    RowInfo ri;
+    ri.t_row = tau_lds[rrow % B];
+    ri.is_data = rrow < B;
+    const bool wave_active = (rb * ROWS_B + w * 32) < R;
 
-    // ---- per-lane query rows (two 32-row blocks per wave)
-    int qhead[2], rrow[2], t_row[2];
-    bool rvalid[2], r_is_d[2];
-    bf16x8 qop[2][C::NS];
+    RowState<D> st;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int rho = rb * kRowsPerBlock + w * kRowsPerWave + qb * 32 + l32;
-        rvalid[qb] = rho < R;
-        const int rr = rvalid[qb] ? rho : 0;
-        const int r = rr % R2;
-        qhead[qb] = kvh * g + rr / R2;
-        rrow[qb] = r;
-        r_is_d[qb] = r < B;
-        t_row[qb] = tau_lds[r % B];
-        const uint16_t *qp = a.q + (((size_t)b * R2 + r) * a.n_qh + qhead[qb]) * D + 8 * h;
-        uint4 raw[C::NS];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-            raw[s] = rvalid[qb] ? *reinterpret_cast<const uint4 *>(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-        if (a.use_rope) {
-            const int pr = r % B;
-#pragma unroll
-            for (int s = 0; s < C::NS / 2; ++s) {
-                uint32_t lw[4], hw[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float y1[2], y2[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = 2 * e2 + u;
-                        const float2 cs = cs_lds[pr * (D / 2) + 16 * s + 8 * h + e];
-                        const float x1 = bf16_to_f32(u4_elem(raw[s], e));
-                        const float x2 = bf16_to_f32(u4_elem(raw[s + C::NS / 2], e));
-                        y1[u] = x1 * cs.x - x2 * cs.y;
-                        y2[u] = x1 * cs.y + x2 * cs.x;
-                    }
-                    lw[e2] = pack_bf16x2(y1[0], y1[1]);
-                    hw[e2] = pack_bf16x2(y2[0], y2[1]);
-                }
-                raw[s] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-                raw[s + C::NS / 2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) qop[qb][s] = __builtin_bit_cast(bf16x8, raw[s]);
+        for (int x = 0; x < 16; ++x) st.oacc[db][x] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    for (int it = 0; it < nt; it += 3) {
+        tile_step<D, NW>(a, b, kvh, t0, nt, it, wave_active, ri, qop, st, k_st0, v_st0, k_st2, v_st2, cs_lds,
+                         tau_lds);
+        if (it + 1 < nt)
+            tile_step<D, NW>(a, b, kvh, t0, nt, it + 1, wave_active, ri, qop, st, k_st1, v_st1, k_st0, v_st0,
+                             cs_lds, tau_lds);
+        if (it + 2 < nt)
+            tile_step<D, NW>(a, b, kvh, t0, nt, it + 2, wave_active, ri, qop, st, k_st2, v_st2, k_st1, v_st1,
+                             cs_lds, tau_lds);
     }
-    const bool wave_active = (rb * kRowsPerBlock + w * kRowsPerWave) < R;
-
-    f32x16 oacc[2][C::NDB];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) oacc[qb][db][x] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-    if (t0 < t1) write_lds(0, t0);
-    __syncthreads();
-
-    for (int t = t0; t < t1; ++t) {
-        const int buf = (t - t0) & 1;
-        if (t + 1 < t1) issue_loads(t + 1);
-        if (wave_active) {
-            const int base = t * kTileKeys;
-            // ---- S^T = K Q^T (keys x queries), 2 key blocks x 2 query blocks
-            f32x16 sacc[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) sacc[qb][kb][x] = 0.f;
-#pragma unroll
-            for (int s = 0; s < C::NS; ++s) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&k_lds[buf][kb * 32 + l32][16 * s + 8 * h]);
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][s], sacc[qb][kb], 0, 0, 0);
-                }
-            }
-            // ---- temporal-causal mask, only where response / padding keys occur
-            if (base + kTileKeys > P) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) {
-                        const int j = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3);
-                        if (j >= P) {
-                            bool key_ok = false, key_d = false;
-                            int tk = 0;
-                            if (j < Nk) {
-                                const int c = j - P;
-                                key_d = c < B;
-                                tk = tau_lds[c % B];
-                                key_ok = true;
-                            }
-#pragma unroll
-                            for (int qb = 0; qb < 2; ++qb)
-                                if (!key_ok || !visible(t_row[qb], r_is_d[qb], tk, key_d))
-                                    sacc[qb][kb][x] = -INFINITY;
-                        }
-                    }
-                }
-            }
-            // ---- online softmax (log2 domain); each lane owns one query
-            bf16x8 pop[2][4];
-            bool rescale = false;
-            float alpha[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[qb][kb][x]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-                rescale |= (alpha[qb] != 1.f);
-                float ls = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub) {
-                        bf16x8 pv;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][8 * sub + e], a.scale_log2, -m_use));
-                            const __bf16 pb = (__bf16)p;
-                            ls += (float)pb;
-                            pv[e] = pb;
-                        }
-                        pop[qb][2 * kb + sub] = pv;
-                    }
-                }
-                l_run[qb] = l_run[qb] * alpha[qb] + ls;
-                m_run[qb] = m_new;
-            }
-            if (__any(rescale)) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                        for (int x = 0; x < 16; ++x) oacc[qb][db][x] *= alpha[qb];
-            }
-            // ---- O^T += V^T P^T: k-step s covers tile keys 16s..16s+15; lane
-            // half h supplies keys 16s+4h+{0..3} and 16s+8+4h+{0..3}
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const uint32_t *vrow = &vt_lds[buf][db * 32 + l32][0];
-                    const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow + 8 * s + 2 * h);
-                    const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 8 * s + 4 + 2 * h);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][s], oacc[qb][db], 0, 0, 0);
-                }
-            }
-        }
-        if (t + 1 < t1) write_lds(buf ^ 1, t + 1);
-        __syncthreads();
-    }
+    wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 
     if (!wave_active) return;
-    // ---- epilogue: lane owns query (qb, l32); O^T rows dim = db*32 + 8*jj + 4*h + i
+    // ---- epilogue: lane owns query l32; O^T rows dim = db*32 + 8*jj + 4*h + i
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    if (!rvalid) return;
+    const size_t row = ((size_t)b * R2 + rrow) * a.n_qh + qhead;
+    if (a.n_split == 1) {
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        uint16_t *op = a.out + row * D + 4 * h;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-        if (!rvalid[qb]) continue;
-        const size_t row = ((size_t)b * R2 + rrow[qb]) * a.n_qh + qhead[qb];
-        if (a.n_split == 1) {
-            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-            uint16_t *op = a.out + row * D + 4 * h;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x16 &o = st.oacc[db];
+                uint2 pk;
+                pk.x = pack_bf16x2(o[4 * jj + 0] * inv, o[4 * jj + 1] * inv);
+                pk.y = pack_bf16x2(o[4 * jj + 2] * inv, o[4 * jj + 3] * inv);
+                *reinterpret_cast<uint2 *>(op + db * 32 + 8 * jj) = pk;
+            }
+    } else {
+        const size_t prow = (size_t)split * a.batch * R2 * a.n_qh + row;
+        float *op = a.ws_o + prow * D + 4 * h;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x16 &o = oacc[qb][db];
-                    uint2 pk;
-                    pk.x = pack_bf16x2(o[4 * jj + 0] * inv, o[4 * jj + 1] * inv);
-                    pk.y = pack_bf16x2(o[4 * jj + 2] * inv, o[4 * jj + 3] * inv);
-                    *reinterpret_cast<uint2 *>(op + db * 32 + 8 * jj) = pk;
-                }
-        } else {
-            const size_t prow = (size_t)split * a.batch * R2 * a.n_qh + row;
-            float *op = a.ws_o + prow * D + 4 * h;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x16 &o = oacc[qb][db];
-                    *reinterpret_cast<float4 *>(op + db * 32 + 8 * jj) =
-                        make_float4(o[4 * jj + 0], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]);
-                }
-            if (h == 0) a.ws_ml[prow] = make_float2(m_run[qb], l_tot);
-        }
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x16 &o = st.oacc[db];
+                *reinterpret_cast<float4 *>(op + db * 32 + 8 * jj) =
+                    make_float4(o[4 * jj + 0], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]);
+            }
+        if (h == 0) a.ws_ml[prow] = make_float2(st.m_run, l_tot);
     }
 }
 
@@ -534,7 +603,8 @@ AttnPlan attn_plan(const AttnShape &s) {
     AttnPlan p{};
     const int g = s.n_qh / s.n_kvh;
     p.rows = g * 2 * s.block;
-    p.n_rb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    p.nw = p.rows > 128 ? 8 : 4;
+    p.n_rb = (p.rows + 32 * p.nw - 1) / (32 * p.nw);
     const int nk = s.prefix + 2 * s.block;
     p.n_tiles = (nk + kTileKeys - 1) / kTileKeys;
     p.n_split = 1;
@@ -612,10 +682,11 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.log2_theta = theta > 0 ? log2(theta) : 0.0;
         a.scale_log2 = scale * kLog2e;
         const unsigned grid = (unsigned)((size_t)s.batch * s.n_kvh * p.n_rb * p.n_split);
-        if (s.head_dim == 128)
-            hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
-        else
-            hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+        const dim3 blk(64 * p.nw);
+        if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), dim3(grid), blk, 0, st, a);
+        else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), dim3(grid), blk, 0, st, a);
+        else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), dim3(grid), blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), dim3(grid), blk, 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.n_split == 1) return e;
         const size_t rows_total = (size_t)s.batch * R2 * s.n_qh;

@@ -8,8 +8,6 @@
 namespace sv {
 
 constexpr int kTileKeys = 64;        // keys per attention tile
-constexpr int kRowsPerWave = 64;     // query rows per wave (two 32-row MFMA blocks)
-constexpr int kRowsPerBlock = 256;   // 4 waves
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -20,7 +18,8 @@ struct AttnShape {
 
 struct AttnPlan {
     int rows;            // rows per kv head = (n_qh / n_kvh) * 2 * block
-    int n_rb;            // row blocks of 256 rows per kv head
+    int nw;              // waves per workgroup (32 query rows each)
+    int n_rb;            // row blocks of 32 * nw rows per kv head
     int n_tiles;         // key tiles over prefix + 2 * block keys
     int n_split;         // prefix splits (1 = no combine pass)
     int tiles_per_split;
@@ -46,7 +45,7 @@ struct AcceptPlan {
     int n_vsplit;    // vocab splits of the normaliser pass
     int64_t chunk;   // vocab elements per residual chunk
     int n_chunk;
-    size_t off_part, off_res, off_chunk, off_ticket, ws_total;
+    size_t off_part, off_res, off_chunk, ws_total;
 };
 
 AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab);

@@ -35,7 +35,7 @@
  *     dtype SV_F32: float32 tensors and float32 arithmetic throughout.
  *   - Shape limits: 1 <= block <= 64, n_qh % n_kvh == 0, head_dim in
  *     {64, 128}, prefix_len >= 0, batch >= 1; accept: 1 <= gamma <= block,
- *     1 <= vocab < 2^31.
+ *     1 <= vocab <= 2^21.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

@@ -107,6 +107,8 @@ SMALL = synth.Case("edge", 3, 100, 8, 8, 8, 2, 128, 1000, "bf16", 1e6, "perturb"
     dict(dtype="f32", head_dim=128, prefix_len=0, block=4, gamma=4),
     dict(identity_every=1),                    # every sequence tau = identity
     dict(logit_model="iid", target_var=2.0, draft_var=2.0),
+    dict(draft_var=1e-4, vocab=20000),         # draft close to target: small residual mass Z
+    dict(draft_var=1e-6, vocab=20000, batch=8),
 ], ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
 def test_edge(o, kw):
     check_case(o, SMALL.with_(**kw))

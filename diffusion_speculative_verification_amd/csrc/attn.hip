@@ -86,14 +86,22 @@ __global__ void __launch_bounds__(256) rope_kernel(const T *__restrict__ q_in, c
 // chunks XOR-swizzled per row so that both the S^T operand reads (16 B of one
 // row per lane, 8 consecutive rows per LDS cycle) and the transposed V reads
 // (8 B from 4 consecutive rows per 16-lane group) are bank-conflict free.
-template <int D>
+// K tiles (IS_V = false): chunk ^ (row & 7), so the 8 rows that one LDS
+// cycle serves for the 16-byte S^T operand reads land in 8 distinct bank
+// groups.  V tiles (IS_V = true): chunk ^ ((row & 7) << 1) for D = 128 and
+// chunk ^ ((row & 3) << 1) for D = 64, so the two adjacent chunks that each
+// row contributes to a transposing read stay adjacent and the 4 rows of a
+// 16-lane group hit disjoint banks.
+template <int D, bool IS_V>
 struct Tile {
     static constexpr int NCH = D / 8;             // 16-byte chunks per row
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int BYTES = kTileKeys * ROW_BYTES;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide 16 B/lane load fills
     static constexpr int LOADS = kTileKeys / ROWS_PER_LOAD;  // wave loads per tile and tensor
-    __device__ static __forceinline__ int swz(int row) { return D == 128 ? ((row & 7) << 1) : (row & 7); }
+    __device__ static __forceinline__ int swz(int row) {
+        return IS_V ? (D == 128 ? ((row & 7) << 1) : ((row & 3) << 1)) : (row & 7);
+    }
     __device__ static __forceinline__ int off(int row, int chunk) {  // byte offset of a logical chunk
         return row * ROW_BYTES + ((chunk ^ swz(row)) << 4);
     }
@@ -150,10 +158,10 @@ __device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
 // Keys at or past `jend` (the end of this workgroup's key range) read the
 // row jend - 1 instead: such tiles are never consumed, and re-reading one row
 // keeps them in cache.
-template <int D, int NW>
+template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache, const uint16_t *fresh,
                                           int b, int kvh, int base, int jend, char *lds_tile, int w, int lane) {
-    using T = Tile<D>;
+    using T = Tile<D, IS_V>;
 #pragma unroll
     for (int i = 0; i < T::LOADS / NW; ++i) {
         const int r0 = (w + NW * i) * T::ROWS_PER_LOAD;
@@ -216,17 +224,47 @@ struct RowInfo {
     bool is_data;  // D row (true) or D~ row
 };
 
+// Loop-invariant LDS byte offsets of this lane's MFMA operand reads.  The
+// swizzle of a row depends on row & 7 only, and every read family below
+// moves in steps of 8 rows, so the swizzled chunk is fixed per lane:
+//   S^T operand (K, row kb*32 + l32, chunk 2s + h):  k[s] + kb * 32 * ROW_BYTES
+//   V^T operand (V, rows 16s + 4h + j/4 (+ 8), dims 32db + v_dim_lo):
+//                                          v[db] + 16 * s * ROW_BYTES (+ 8 * ROW_BYTES)
+template <int D>
+struct LdsOffs {
+    int k[D / 16];
+    int v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ LdsOffs<D> lds_offsets(int lane) {
+    using TK = Tile<D, false>;
+    using T = Tile<D, true>;
+    const int h = lane >> 5, l32 = lane & 31, gq = lane >> 4, jl = lane & 15;
+    LdsOffs<D> o;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) o.k[s] = TK::off(l32, 2 * s + h);
+    const int v_dim_lo = 16 * (gq & 1) + 4 * (jl & 3);
+    const int k0 = 4 * h + (jl >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int dim = 32 * db + v_dim_lo;
+        o.v[db] = T::off(k0, dim >> 3) + ((dim & 7) << 1);
+    }
+    return o;
+}
+
 // One ring step.  Tile `it` sits in (kt, vt); the stage consumed in the
 // previous step, (kn, vn), is refilled with tile it + 2.  All LDS regions are
 // __restrict__ parameters of this inlined function, which lets the compiler
 // prove that the refill in flight never aliases this step's reads.
 template <int D, int NW>
 __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t0, int nt, int it, bool wave_active,
-                                          const RowInfo &ri, const bf16x8 *qop, RowState<D> &st,
-                                          char *__restrict__ kt, char *__restrict__ vt, char *__restrict__ kn,
-                                          char *__restrict__ vn, const float2 *__restrict__ cs,
-                                          const int *__restrict__ taus) {
-    using T = Tile<D>;
+                                          const RowInfo &ri, const LdsOffs<D> &lo_, const bf16x8 *qop,
+                                          RowState<D> &st, char *__restrict__ kt, char *__restrict__ vt,
+                                          char *__restrict__ kn, char *__restrict__ vn,
+                                          const float2 *__restrict__ cs, const int *__restrict__ klab) {
+    using T = Tile<D, false>;
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -256,8 +294,8 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // step, so the number of loads in flight is the same on every path)
     {
         const int nb = (t0 + it + 2) * kTileKeys;
-        load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
-        load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
+        load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
+        load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
     }
     if (!wave_active) return;
 
@@ -271,55 +309,61 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + T::off(kb * 32 + l32, 2 * s + h));
+            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + lo_.k[s] + kb * 32 * T::ROW_BYTES);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], sacc[kb], 0, 0, 0);
         }
     }
-    // ---- temporal-causal mask, only where response / padding keys occur
+    // ---- temporal-causal mask, only where response / padding keys occur;
+    // klab[c] = (step label << 1) | is_data of response key c, and -1 past
+    // the last response key
     if (base + kTileKeys > P) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                const int j = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3);
-                if (j >= P) {
-                    bool vis = false;
-                    if (j < Nk) {
-                        const int c = j - P;
-                        vis = visible(ri.t_row, ri.is_data, taus[c % B], c < B);
-                    }
-                    if (!vis) sacc[kb][x] = -INFINITY;
+                const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;
+                if (c >= 0) {
+                    const int lab = klab[min(c, 2 * kMaxBlock)];
+                    const bool vis = lab >= 0 && visible(ri.t_row, ri.is_data, lab >> 1, lab & 1);
+                    sacc[kb][x] = vis ? sacc[kb][x] : -INFINITY;
                 }
             }
         }
     }
     // ---- online softmax (log2 domain); each lane owns one query
-    bf16x8 pop[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[kb][x]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m_run, mx * a.scale_log2);
+    // lazy rescale: the running max moves only when the tile max exceeds it
+    // by more than 8 (log2 units); otherwise P = 2^(s - m_run) <= 2^8 and the
+    // accumulators keep their scale (exact after the final normalisation)
+    const float m_tile = mx * a.scale_log2;
+    const float m_new = (m_tile > st.m_run + 8.f) ? m_tile : st.m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
     float ls = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            sacc[kb][x] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][x], a.scale_log2, -m_use));
+            ls += sacc[kb][x];
+        }
+    bf16x8 pop[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            bf16x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * sub + e], a.scale_log2, -m_use));
-                const __bf16 pb = (__bf16)p;
-                ls += (float)pb;
-                pv[e] = pb;
-            }
-            pop[2 * kb + sub] = pv;
+            const f32x16 &pp = sacc[kb];
+            const uint4 w4 = make_uint4(pack_bf16x2(pp[8 * sub + 0], pp[8 * sub + 1]),
+                                        pack_bf16x2(pp[8 * sub + 2], pp[8 * sub + 3]),
+                                        pack_bf16x2(pp[8 * sub + 4], pp[8 * sub + 5]),
+                                        pack_bf16x2(pp[8 * sub + 6], pp[8 * sub + 7]));
+            pop[2 * kb + sub] = __builtin_bit_cast(bf16x8, w4);
         }
-    }
     st.l_run = st.l_run * alpha + ls;
     st.m_run = m_new;
     if (__any(alpha != 1.f)) {
@@ -333,19 +377,13 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // row-major V tile through the transposing LDS read: in 16-lane group gq,
     // lane j = 4k + c reads row key(k) at dims dim0 + 4c, and lane i receives
     // the four keys of dim dim0 + i.
-    const int gq = lane >> 4, jl = lane & 15;
-    const int v_dim_lo = 16 * (gq & 1) + 4 * (jl & 3);
-    const int v_key_lo = 4 * h + (jl >> 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const int dim = 32 * db + v_dim_lo;
-            const int k0 = 16 * s + v_key_lo;
-            const int o0 = T::off(k0, dim >> 3) + ((dim & 7) << 1);
-            const int o1 = T::off(k0 + 8, dim >> 3) + ((dim & 7) << 1);
+            const int o0 = lo_.v[db] + 16 * s * T::ROW_BYTES;
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o1));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0 + 8 * T::ROW_BYTES));
             const v4i16 cat[2] = {lo, hi};
             const bf16x8 va = __builtin_bit_cast(bf16x8, cat);
             st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[s], st.oacc[db], 0, 0, 0);
@@ -366,11 +404,13 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     const int B = a.block, P = a.prefix;
     // the first two tiles (every split has at least one; a second tile past
     // the end reads clamped rows and is never consumed)
-    load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
-    load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
-    load_tile<D, NW>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
-    load_tile<D, NW>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
-    if (tid < B) taus[tid] = tau_v;
+    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
+    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
+    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
+    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
+    // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
+    const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
+    if (tid <= 2 * kMaxBlock) taus[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
     if (a.use_rope) {
         if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
@@ -393,7 +433,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
 // by direct global->LDS loads.
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
-    using T = Tile<D>;
+    using T = Tile<D, false>;
     constexpr int NS = D / 16;
     constexpr int NDB = D / 32;
     constexpr int ROWS_B = 32 * NW;
@@ -402,7 +442,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
     __shared__ __attribute__((aligned(16))) float2 cs_lds[64 * (D / 2)];
     __shared__ double invf_lds[D / 2];
-    __shared__ int tau_lds[64];
+    __shared__ int klab_lds[2 * kMaxBlock + 1];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int B = a.block, R2 = 2 * B, g = a.n_qh / a.n_kvh, R = g * R2;
@@ -423,10 +463,10 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
     const int nt = t1 - t0;
 
-    // ---- tau and this lane's query row (one 32-row MFMA block per wave):
+    // ---- tau (lane k of every wave holds tau[k]) and this lane's query row (one 32-row MFMA block per wave):
     // their loads go out before the tiles' so that waiting for them does not
     // drain the tile loads
-    const int tau_v = a.tau[(size_t)b * B + min(tid, B - 1)];
+    const int tau_v = a.tau[(size_t)b * B + min(lane, B - 1)];
     const int rho = rb * ROWS_B + w * 32 + l32;
     const bool rvalid = rho < R;
     const int rr = rvalid ? rho : 0;
@@ -441,10 +481,11 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     const int jend = min(a.prefix + R2, t1 * kTileKeys);
     bf16x8 qop[NS];
     prologue<D, NW>(a, b, kvh, t0, jend, tau_v, raw, rvalid, rrow % B, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
-                    invf_lds, tau_lds);
+                    invf_lds, klab_lds);
     RowInfo ri;
-    ri.t_row = tau_lds[rrow % B];
+    ri.t_row = __shfl(tau_v, rrow % B);
     ri.is_data = rrow < B;
+    const LdsOffs<D> offs = lds_offsets<D>(lane);
     const bool wave_active = (rb * ROWS_B + w * 32) < R;
 
     RowState<D> st;
@@ -456,14 +497,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     st.l_run = 0.f;
 
     for (int it = 0; it < nt; it += 3) {
-        tile_step<D, NW>(a, b, kvh, t0, nt, it, wave_active, ri, qop, st, k_st0, v_st0, k_st2, v_st2, cs_lds,
-                         tau_lds);
+        tile_step<D, NW>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2, cs_lds,
+                         klab_lds);
         if (it + 1 < nt)
-            tile_step<D, NW>(a, b, kvh, t0, nt, it + 1, wave_active, ri, qop, st, k_st1, v_st1, k_st0, v_st0,
-                             cs_lds, tau_lds);
+            tile_step<D, NW>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0, v_st0,
+                             cs_lds, klab_lds);
         if (it + 2 < nt)
-            tile_step<D, NW>(a, b, kvh, t0, nt, it + 2, wave_active, ri, qop, st, k_st2, v_st2, k_st1, v_st1,
-                             cs_lds, tau_lds);
+            tile_step<D, NW>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1, v_st1,
+                             cs_lds, klab_lds);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 

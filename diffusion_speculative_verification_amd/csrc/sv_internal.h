@@ -8,6 +8,7 @@
 namespace sv {
 
 constexpr int kTileKeys = 64;        // keys per attention tile
+constexpr int kMaxBlock = 64;        // largest block size B
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }

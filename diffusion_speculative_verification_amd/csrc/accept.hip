@@ -6,25 +6,28 @@
 // Decoding for Diffusion LLMs via Training-Free Self-Speculation", 前置知识
 // "推测解码" and 方法步骤 (5) (residual (P_target - P_draft)^+).
 //
-// Four launches on the caller's stream:
-//   lse_partial_kernel  vocab-parallel softmax normaliser of every verified
-//                       slot: a streaming pass over the float32 target logits
-//                       (16-byte coalesced loads, 4 in flight per lane), per
-//                       lane running (max, sum) with the sum kept in float64,
-//                       merged per workgroup into one (m, s) partial per
-//                       (slot, vocab split).  This pass moves almost all the
-//                       bytes of the epilogue.
-//   accept_scan_kernel  one wave per sequence: lane r merges the partials of
-//                       the slot of draft step r+1, forms alpha in float64,
-//                       the first rejection is found with one ballot; writes
-//                       accept_len, alpha and the draft part of out_tokens.
-//   residual_sums_kernel  (sequence, vocab chunk) workgroups form the residual
-//                       and target mass of their chunk at the rejected slot;
-//   residual_pick_kernel  one workgroup per sequence picks the chunk holding
-//                       u * Z and rescans it for the token.  (Two launches:
-//                       the kernel boundary orders the chunk sums; a
-//                       last-workgroup handoff would need a device-scope
-//                       release per workgroup, which writes back the L2.)
+// Three launches on the caller's stream:
+//   lse_partial_kernel   vocab-parallel softmax normaliser of every verified
+//                        slot: a streaming pass over the float32 target
+//                        logits (16-byte coalesced loads, 4 in flight per
+//                        lane), per-lane running (max, sum) with the sum kept
+//                        in float64, merged per workgroup into one (m, s)
+//                        partial per (slot, vocab split).  This pass moves
+//                        almost all the bytes of the epilogue.
+//   accept_resid_kernel  one workgroup per (sequence, vocab chunk): wave 0
+//                        runs the acceptance scan of the sequence (lane r
+//                        merges the partials of the slot of draft step r+1,
+//                        alpha in float64, first rejection by one ballot);
+//                        chunk 0 writes accept_len, alpha and the draft part
+//                        of out_tokens; every workgroup then forms the
+//                        residual and target mass of its chunk at the
+//                        rejected slot.
+//   residual_pick_kernel one workgroup per sequence: block scans over the
+//                        chunk sums find the chunk holding u * Z, a second
+//                        scan inside it finds the token.
+// The kernel boundaries order the hand-offs: a last-workgroup hand-off
+// inside one kernel would need a device-scope release per workgroup, which on
+// this GPU writes back the L2.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -45,6 +48,10 @@ struct ResInfo {  // rejected slot of one sequence
     float m;      // merged max logit of that slot
     double s;     // merged sum exp(l - m)
 };
+
+constexpr int kResChunk = 2048;           // vocab entries per residual workgroup
+constexpr int kResRun = kResChunk / 256;  // contiguous entries per thread in the pick scan
+constexpr int kMaxChunks = 1024;          // vocab <= kResChunk * kMaxChunks = 2^21
 
 template <bool VEC>
 __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restrict__ logits,
@@ -118,68 +125,6 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
     }
 }
 
-__global__ void __launch_bounds__(64) accept_scan_kernel(
-    const float *__restrict__ logits, const float *__restrict__ probs, const int32_t *__restrict__ tokens,
-    const int32_t *__restrict__ tau, const float *__restrict__ u, const Part *__restrict__ parts,
-    int block, int gamma, int64_t vocab, int n_vsplit, int32_t *accept_len, int32_t *out_tokens,
-    float *alpha_out, ResInfo *res) {
-    __shared__ int inv_s[64];
-    __shared__ int tau_s[64];
-    const int b = blockIdx.x, lane = threadIdx.x;
-    inv_s[lane] = 0;  // tau is a permutation by contract; keep slot indices in range regardless
-    __syncthreads();
-    if (lane < block) {
-        const int t = tau[(size_t)b * block + lane];
-        tau_s[lane] = t;
-        if (t >= 1 && t <= block) inv_s[t - 1] = lane;
-    }
-    __syncthreads();
-    bool rejected = false;
-    float M = 0.f;
-    double S = 1.0;
-    if (lane < gamma) {
-        const int k = inv_s[lane];
-        const size_t row = (size_t)b * block + k;
-        M = -INFINITY;
-        for (int i = 0; i < n_vsplit; ++i) M = fmaxf(M, parts[row * n_vsplit + i].m);
-        S = 0.0;
-        for (int i = 0; i < n_vsplit; ++i) {
-            const Part p = parts[row * n_vsplit + i];
-            if (p.m != -INFINITY) S += p.s * exp((double)p.m - (double)M);
-        }
-        const int x = tokens[row];
-        double a = 0.0;  // out-of-range draft token: rejected
-        if (x >= 0 && x < vocab) {
-            const double pt = exp((double)logits[row * vocab + x] - (double)M) / S;
-            const double pd = (double)probs[row * vocab + x];
-            a = (pd > 0.0) ? fmin(1.0, pt / pd) : 1.0;
-        }
-        rejected = !((double)u[(size_t)b * (gamma + 1) + lane] < a);
-        if (alpha_out) alpha_out[(size_t)b * gamma + lane] = (float)a;
-    }
-    const unsigned long long rej = __ballot(rejected);
-    const int L = rej ? (__ffsll((long long)rej) - 1) : gamma;
-    if (lane < block)
-        out_tokens[(size_t)b * block + lane] = (tau_s[lane] <= L) ? tokens[(size_t)b * block + lane] : -1;
-    if (lane == 0) {
-        accept_len[b] = L;
-        if (L == gamma) {
-            ResInfo r;
-            r.slot = -1;
-            r.m = 0.f;
-            r.s = 0.0;
-            res[b] = r;
-        }
-    }
-    if (L < gamma && lane == L) {
-        ResInfo r;
-        r.slot = inv_s[L];
-        r.m = M;
-        r.s = S;
-        res[b] = r;
-    }
-}
-
 // Mass of one vocab entry at the rejected slot: p_theta(v) (float32 exp of
 // the logit against the merged max, scaled by the float64 reciprocal of the
 // merged normaliser) and the residual max(0, p_theta(v) - p_phi(v)) formed in
@@ -191,6 +136,7 @@ __device__ __forceinline__ void masses(float l, float pd, float m, double inv_s,
 }
 
 // Exclusive prefix sum over the 256 threads of a workgroup (thread order).
+// Contains a workgroup barrier; wave_tot is 4 doubles of LDS.
 __device__ __forceinline__ double block_exclusive_scan(double v, double *wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     double inc = v;
@@ -203,29 +149,109 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double *wave_to
     __syncthreads();
     double base = 0.0;
     for (int k = 0; k < w; ++k) base += wave_tot[k];
+    __syncthreads();  // wave_tot may be reused by the caller
     return base + inc - v;
 }
 
-constexpr int kResChunk = 2048;       // vocab entries per residual workgroup
-constexpr int kResRun = kResChunk / 256;  // contiguous entries per thread in the pick scan
-constexpr int kMaxChunks = 1024;          // vocab <= kResChunk * kMaxChunks = 2^21
+// Acceptance scan of one sequence, run by one wave (SimSD 关键设计 4): lane r
+// merges the normaliser partials of the slot verified at draft step r+1,
+// forms alpha in float64 and tests u[r] < alpha; one ballot gives the first
+// rejection.  Returns L (number of leading accepts); *slot/*m_out/*s_out
+// describe the rejected slot (slot -1 when L == gamma).
+__device__ __forceinline__ int acceptance_scan(const float *__restrict__ logits, const float *__restrict__ probs,
+                                               const int32_t *__restrict__ tokens, const float *__restrict__ u,
+                                               const Part *__restrict__ parts, const int *inv_s, int b, int block,
+                                               int gamma, int64_t vocab, int n_vsplit, double *alpha_lane,
+                                               int *slot, float *m_out, double *s_out) {
+    const int lane = threadIdx.x & 63;
+    bool rejected = false;
+    float M = 0.f;
+    double S = 1.0, a = 0.0;
+    if (lane < gamma) {
+        const int k = inv_s[lane];
+        const size_t row = (size_t)b * block + k;
+        M = -INFINITY;
+        for (int i = 0; i < n_vsplit; ++i) M = fmaxf(M, parts[row * n_vsplit + i].m);
+        S = 0.0;
+        for (int i = 0; i < n_vsplit; ++i) {
+            const Part p = parts[row * n_vsplit + i];
+            if (p.m != -INFINITY) S += p.s * exp((double)p.m - (double)M);
+        }
+        const int x = tokens[row];
+        if (x >= 0 && x < vocab) {  // an out-of-range draft token is rejected (alpha = 0)
+            const double pt = exp((double)logits[row * vocab + x] - (double)M) / S;
+            const double pd = (double)probs[row * vocab + x];
+            a = (pd > 0.0) ? fmin(1.0, pt / pd) : 1.0;
+        }
+        rejected = !((double)u[(size_t)b * (gamma + 1) + lane] < a);
+    }
+    *alpha_lane = a;
+    const unsigned long long rej = __ballot(rejected);
+    const int L = rej ? (__ffsll((long long)rej) - 1) : gamma;
+    const int src = L < gamma ? L : 0;
+    *slot = L < gamma ? inv_s[L] : -1;
+    *m_out = __shfl(M, src);
+    *s_out = __shfl(S, src);
+    return L;
+}
 
-// Residual pass 1: one workgroup per (sequence, vocab chunk) writes the
-// residual and target mass of its chunk at the rejected slot.
+// Acceptance + residual mass, one workgroup per (sequence, vocab chunk).
+// Every workgroup of a sequence repeats the (small) acceptance scan; chunk 0
+// writes accept_len, alpha, the draft part of out_tokens and the rejected
+// slot's normaliser for the pick kernel.  If a step was rejected, each
+// workgroup then forms the residual and target mass of its vocab chunk at
+// the rejected slot.
 template <bool VEC>
-__global__ void __launch_bounds__(256) residual_sums_kernel(const float *__restrict__ logits,
-                                                            const float *__restrict__ probs,
-                                                            const ResInfo *__restrict__ res, double2 *chunk_sums,
-                                                            int block, int64_t vocab, int n_chunk) {
+__global__ void __launch_bounds__(256) accept_resid_kernel(
+    const float *__restrict__ logits, const float *__restrict__ probs, const int32_t *__restrict__ tokens,
+    const int32_t *__restrict__ tau, const float *__restrict__ u, const Part *__restrict__ parts, int block,
+    int gamma, int64_t vocab, int n_vsplit, int n_chunk, int32_t *accept_len, int32_t *out_tokens,
+    float *alpha_out, ResInfo *res, double2 *chunk_sums) {
+    __shared__ int inv_s[64];
+    __shared__ int tau_s[64];
+    __shared__ int slot_s;
+    __shared__ float m_s;
+    __shared__ double s_s;
     __shared__ double red_a[4], red_b[4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x / n_chunk, c = blockIdx.x % n_chunk;
-    const ResInfo ri = res[b];
-    if (ri.slot < 0) return;
-    const size_t row = (size_t)b * block + ri.slot;
+    if (tid < 64) inv_s[tid] = 0;  // tau is a permutation by contract; keep slot indices in range regardless
+    __syncthreads();
+    if (tid < block) {
+        const int t = tau[(size_t)b * block + tid];
+        tau_s[tid] = t;
+        if (t >= 1 && t <= block) inv_s[t - 1] = tid;
+    }
+    __syncthreads();
+    if (w == 0) {
+        double a, S;
+        int slot;
+        float M;
+        const int L = acceptance_scan(logits, probs, tokens, u, parts, inv_s, b, block, gamma, vocab, n_vsplit, &a,
+                                      &slot, &M, &S);
+        if (c == 0) {
+            if (lane < gamma && alpha_out) alpha_out[(size_t)b * gamma + lane] = (float)a;
+            if (lane < block)
+                out_tokens[(size_t)b * block + lane] = (tau_s[lane] <= L) ? tokens[(size_t)b * block + lane] : -1;
+            if (lane == 0) {
+                accept_len[b] = L;
+                ResInfo r;
+                r.slot = slot;
+                r.m = M;
+                r.s = S;
+                res[b] = r;
+            }
+        }
+        if (lane == 0) { slot_s = slot; m_s = M; s_s = S; }
+    }
+    __syncthreads();
+    const int slot = slot_s;
+    if (slot < 0) return;
+    const float M = m_s;
+    const double inv_sum = 1.0 / s_s;
+    const size_t row = (size_t)b * block + slot;
     const float *lr = logits + row * vocab;
     const float *pr = probs + row * vocab;
-    const double inv_s = 1.0 / ri.s;
     const int64_t v0 = (int64_t)c * kResChunk;
     const int n = (int)min((int64_t)kResChunk, vocab - v0);
     double ra = 0.0, pa = 0.0;
@@ -233,17 +259,17 @@ __global__ void __launch_bounds__(256) residual_sums_kernel(const float *__restr
         const float4 *l4 = reinterpret_cast<const float4 *>(lr + v0);
         const float4 *p4 = reinterpret_cast<const float4 *>(pr + v0);
         for (int i = tid; i < (n >> 2); i += 256) {
-            const float4 a = l4[i], q = p4[i];
+            const float4 x = l4[i], q = p4[i];
             double r, pt;
-            masses(a.x, q.x, ri.m, inv_s, r, pt); ra += r; pa += pt;
-            masses(a.y, q.y, ri.m, inv_s, r, pt); ra += r; pa += pt;
-            masses(a.z, q.z, ri.m, inv_s, r, pt); ra += r; pa += pt;
-            masses(a.w, q.w, ri.m, inv_s, r, pt); ra += r; pa += pt;
+            masses(x.x, q.x, M, inv_sum, r, pt); ra += r; pa += pt;
+            masses(x.y, q.y, M, inv_sum, r, pt); ra += r; pa += pt;
+            masses(x.z, q.z, M, inv_sum, r, pt); ra += r; pa += pt;
+            masses(x.w, q.w, M, inv_sum, r, pt); ra += r; pa += pt;
         }
     } else {
         for (int i = tid; i < n; i += 256) {
             double r, pt;
-            masses(lr[v0 + i], pr[v0 + i], ri.m, inv_s, r, pt);
+            masses(lr[v0 + i], pr[v0 + i], M, inv_sum, r, pt);
             ra += r;
             pa += pt;
         }
@@ -257,8 +283,10 @@ __global__ void __launch_bounds__(256) residual_sums_kernel(const float *__restr
             make_double2(red_a[0] + red_a[1] + red_a[2] + red_a[3], red_b[0] + red_b[1] + red_b[2] + red_b[3]);
 }
 
-// Residual pass 2: one workgroup per sequence picks the chunk whose running
-// sum (ascending token order) crosses u * Z, then the token inside it.
+// Residual pick: one workgroup per sequence finds the chunk whose running sum
+// (ascending token order) crosses u * Z, then the token inside it.  Z is the
+// residual mass; when it is zero the target distribution is sampled instead.
+// If rounding leaves no crossing, the last entry with positive mass is taken.
 __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restrict__ logits,
                                                             const float *__restrict__ probs,
                                                             const float *__restrict__ u,
@@ -266,78 +294,85 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
                                                             const double2 *__restrict__ chunk_sums,
                                                             int32_t *out_tokens, int block, int gamma, int64_t vocab,
                                                             int n_chunk) {
-    __shared__ double mass_s[256 * (kResRun + 1)];  // skewed: thread t's run starts at t * (kResRun + 1)
-    __shared__ double csum_r[kMaxChunks], csum_t[kMaxChunks];
+    constexpr int CPT = kMaxChunks / 256;  // chunks per thread
     __shared__ double wave_tot[4];
-    __shared__ int sel_chunk, sel_use_t;
-    __shared__ double sel_base, sel_thr;
-    __shared__ int pick_first, pick_last;
+    __shared__ double tot_s[2];
+    __shared__ int sel_chunk;
+    __shared__ double sel_base;
+    __shared__ int pick_first, pick_last, last_chunk;
     const int tid = threadIdx.x, b = blockIdx.x;
     const ResInfo ri = res[b];
     if (ri.slot < 0) return;
-    const size_t row = (size_t)b * block + ri.slot;
-    const float *lr = logits + row * vocab;
-    const float *pr = probs + row * vocab;
-    const double inv_s = 1.0 / ri.s;
-    for (int k = tid; k < n_chunk; k += 256) {
-        const double2 cs = chunk_sums[(size_t)b * n_chunk + k];
-        csum_r[k] = cs.x;
-        csum_t[k] = cs.y;
+    // thread t owns chunks [t * CPT, t * CPT + CPT)
+    double cr[CPT], ct[CPT], my_r = 0.0, my_t = 0.0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int ch = tid * CPT + k;
+        const double2 v = ch < n_chunk ? chunk_sums[(size_t)b * n_chunk + ch] : make_double2(0.0, 0.0);
+        cr[k] = v.x;
+        ct[k] = v.y;
+        my_r += v.x;
+        my_t += v.y;
     }
+    if (tid == 0) { pick_first = 0x7fffffff; pick_last = -1; last_chunk = -1; sel_chunk = 0x7fffffff; sel_base = 0.0; }
+    const double ex_r = block_exclusive_scan(my_r, wave_tot);
+    const double ex_t = block_exclusive_scan(my_t, wave_tot);
+    if (tid == 255) { tot_s[0] = ex_r + my_r; tot_s[1] = ex_t + my_t; }
     __syncthreads();
-    if (tid == 0) {
-        double Z = 0.0, T = 0.0;
-        for (int k = 0; k < n_chunk; ++k) { Z += csum_r[k]; T += csum_t[k]; }
-        const int use_t = !(Z > 0.0);
-        const double *add_s = use_t ? csum_t : csum_r;
-        const double tot = use_t ? T : Z;
-        const double thr = (double)u[(size_t)b * (gamma + 1) + gamma] * tot;
-        double run = 0.0, last_base = 0.0, base = 0.0;
-        int pick = -1, last_pos = 0;
-        for (int k = 0; k < n_chunk; ++k) {
-            const double add = add_s[k];
-            if (add > 0.0) { last_pos = k; last_base = run; }
-            if (pick < 0 && run + add > thr) { pick = k; base = run; }
+    const bool use_t = !(tot_s[0] > 0.0);
+    const double tot = use_t ? tot_s[1] : tot_s[0];
+    const double thr = (double)u[(size_t)b * (gamma + 1) + gamma] * tot;
+    // each thread proposes the first of its chunks where the running sum
+    // crosses u * Z; the smallest proposal wins and its owner publishes the
+    // running sum before it
+    int last = -1, cand = 0x7fffffff;
+    double last_base = 0.0, cand_base = 0.0;
+    {
+        double run = use_t ? ex_t : ex_r;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const double add = use_t ? ct[k] : cr[k];
+            if (add > 0.0) { last = tid * CPT + k; last_base = run; }
+            if (cand == 0x7fffffff && run <= thr && run + add > thr) { cand = tid * CPT + k; cand_base = run; }
             run += add;
         }
-        if (pick < 0) { pick = last_pos; base = last_base; }
-        sel_chunk = pick;
-        sel_base = base;
-        sel_thr = thr;
-        sel_use_t = use_t;
-        pick_first = 0x7fffffff;
-        pick_last = -1;
+        if (cand != 0x7fffffff) atomicMin(&sel_chunk, cand);
+        if (last >= 0) atomicMax(&last_chunk, last);
     }
     __syncthreads();
-    // masses of the chosen chunk into LDS (coalesced), per-thread contiguous
-    // runs, exclusive prefix over threads, walk the run that crosses u * Z
-    const int cc = sel_chunk;
-    const bool use_t = sel_use_t;
+    if (sel_chunk == 0x7fffffff) {  // rounding left no crossing: the last chunk with mass
+        if (last >= 0 && last == last_chunk) { sel_chunk = last; sel_base = last_base; }
+    } else if (cand == sel_chunk) {
+        sel_base = cand_base;
+    }
+    __syncthreads();
+    // the chosen chunk: thread t takes kResRun contiguous entries
+    const int cc = (sel_chunk == 0x7fffffff) ? 0 : sel_chunk;
+    const double base = sel_base;
     const int64_t v0 = (int64_t)cc * kResChunk;
     const int n = (int)min((int64_t)kResChunk, vocab - v0);
-    for (int i = tid; i < kResChunk; i += 256) {
-        double mass = 0.0;
-        if (i < n) {
-            double r, pt;
-            masses(lr[v0 + i], pr[v0 + i], ri.m, inv_s, r, pt);
-            mass = use_t ? pt : r;
-        }
-        mass_s[(i / kResRun) * (kResRun + 1) + (i % kResRun)] = mass;
-    }
-    __syncthreads();
-    const double *run_s = mass_s + tid * (kResRun + 1);
-    double mine = 0.0;
+    const size_t row = (size_t)b * block + ri.slot;
+    const float *lr = logits + row * vocab + v0;
+    const float *pr = probs + row * vocab + v0;
+    const double inv_sum = 1.0 / ri.s;
+    double mass[kResRun], mine = 0.0;
     int lastpos = -1;
+#pragma unroll
     for (int k = 0; k < kResRun; ++k) {
-        mine += run_s[k];
-        if (run_s[k] > 0.0) lastpos = tid * kResRun + k;
+        const int i = tid * kResRun + k;
+        double r = 0.0, pt = 0.0;
+        if (i < n) masses(lr[i], pr[i], ri.m, inv_sum, r, pt);
+        mass[k] = use_t ? pt : r;
+        mine += mass[k];
+        if (mass[k] > 0.0) lastpos = i;
     }
     if (lastpos >= 0) atomicMax(&pick_last, lastpos);
-    double run = sel_base + block_exclusive_scan(mine, wave_tot);
-    if (run + mine > sel_thr) {
+    double run = base + block_exclusive_scan(mine, wave_tot);
+    if (run <= thr && run + mine > thr) {
+#pragma unroll
         for (int k = 0; k < kResRun; ++k) {
-            run += run_s[k];
-            if (run > sel_thr) { atomicMin(&pick_first, tid * kResRun + k); break; }
+            run += mass[k];
+            if (run > thr) { atomicMin(&pick_first, tid * kResRun + k); break; }
         }
     }
     __syncthreads();
@@ -383,17 +418,13 @@ hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *
                            gamma, vocab, p.n_vsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(accept_scan_kernel, dim3(batch), dim3(64), 0, st, logits, probs, tokens, tau, u, parts,
-                       block, gamma, vocab, p.n_vsplit, accept_len, out_tokens, alpha, res);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 g3((unsigned)((size_t)batch * p.n_chunk));
+    const dim3 g2((unsigned)((size_t)batch * p.n_chunk));
     if ((vocab & 3) == 0)
-        hipLaunchKernelGGL(residual_sums_kernel<true>, g3, dim3(256), 0, st, logits, probs, res, chunks, block, vocab,
-                           p.n_chunk);
+        hipLaunchKernelGGL(accept_resid_kernel<true>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts, block,
+                           gamma, vocab, p.n_vsplit, p.n_chunk, accept_len, out_tokens, alpha, res, chunks);
     else
-        hipLaunchKernelGGL(residual_sums_kernel<false>, g3, dim3(256), 0, st, logits, probs, res, chunks, block,
-                           vocab, p.n_chunk);
+        hipLaunchKernelGGL(accept_resid_kernel<false>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts,
+                           block, gamma, vocab, p.n_vsplit, p.n_chunk, accept_len, out_tokens, alpha, res, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(residual_pick_kernel, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks, out_tokens,

@@ -191,10 +191,10 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
-template <int D>
-struct RowState {  // per-lane attention state of one query row
-    f32x16 oacc[D / 32];
-    float m_run, l_run;
+template <int D, int QB>
+struct RowState {  // per-lane attention state of its QB query rows
+    f32x16 oacc[QB][D / 32];
+    float m_run[QB], l_run[QB];
 };
 
 // Rotate the 8-dim chunk pair (lo: dims 8c.., hi: dims 8c + D/2 ..) of one
@@ -219,9 +219,10 @@ __device__ __forceinline__ void rotate_pair(uint4 &lo, uint4 &hi, const float2 *
     hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
 }
 
+template <int QB>
 struct RowInfo {
-    int t_row;     // step label of the row's slot
-    bool is_data;  // D row (true) or D~ row
+    int t_row[QB];     // step label of each row's slot
+    bool is_data[QB];  // D row (true) or D~ row
 };
 
 // Loop-invariant LDS byte offsets of this lane's MFMA operand reads.  The
@@ -257,17 +258,19 @@ __device__ __forceinline__ LdsOffs<D> lds_offsets(int lane) {
 // One ring step.  Tile `it` sits in (kt, vt); the stage consumed in the
 // previous step, (kn, vn), is refilled with tile it + 2.  All LDS regions are
 // __restrict__ parameters of this inlined function, which lets the compiler
-// prove that the refill in flight never aliases this step's reads.
-template <int D, int NW>
+// prove that the refill in flight never aliases this step's reads.  Each
+// lane owns QB query rows (one per 32-row MFMA block); every K and V operand
+// read from LDS feeds QB MFMAs.
+template <int D, int NW, int QB>
 __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t0, int nt, int it, bool wave_active,
-                                          const RowInfo &ri, const LdsOffs<D> &lo_, const bf16x8 *qop,
-                                          RowState<D> &st, char *__restrict__ kt, char *__restrict__ vt,
+                                          const RowInfo<QB> &ri, const LdsOffs<D> &lo_, const bf16x8 (*qop)[D / 16],
+                                          RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
                                           char *__restrict__ kn, char *__restrict__ vn,
                                           const float2 *__restrict__ cs, const int *__restrict__ klab) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix, Nk = P + 2 * B;
     const int base = (t0 + it) * kTileKeys;
     const int jend = min(Nk, (t0 + nt) * kTileKeys);
@@ -299,18 +302,22 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     }
     if (!wave_active) return;
 
-    // ---- S^T = K Q^T (keys x queries): 2 key blocks of 32
-    f32x16 sacc[2];
+    // ---- S^T = K Q^T (keys x queries): 2 key blocks of 32 per query block
+    f32x16 sacc[QB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sacc[qb][kb][x] = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + lo_.k[s] + kb * 32 * T::ROW_BYTES);
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], sacc[kb], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][s], sacc[qb][kb], 0, 0, 0);
         }
     }
     // ---- temporal-causal mask, only where response / padding keys occur;
@@ -324,53 +331,64 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                 const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;
                 if (c >= 0) {
                     const int lab = klab[min(c, 2 * kMaxBlock)];
-                    const bool vis = lab >= 0 && visible(ri.t_row, ri.is_data, lab >> 1, lab & 1);
-                    sacc[kb][x] = vis ? sacc[kb][x] : -INFINITY;
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const bool vis = lab >= 0 && visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1);
+                        sacc[qb][kb][x] = vis ? sacc[qb][kb][x] : -INFINITY;
+                    }
                 }
             }
         }
     }
-    // ---- online softmax (log2 domain); each lane owns one query
-    float mx = -INFINITY;
+    // ---- online softmax (log2 domain); each lane owns its queries' scores
+    bf16x8 pop[QB][4];
+    bool rescale = false;
+    float alpha[QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[kb][x]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // lazy rescale: the running max moves only when the tile max exceeds it
-    // by more than 8 (log2 units); otherwise P = 2^(s - m_run) <= 2^8 and the
-    // accumulators keep their scale (exact after the final normalisation)
-    const float m_tile = mx * a.scale_log2;
-    const float m_new = (m_tile > st.m_run + 8.f) ? m_tile : st.m_run;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
-    float ls = 0.f;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[qb][kb][x]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // lazy rescale: the running max moves only when the tile max exceeds
+        // it by more than 8 (log2 units); otherwise P = 2^(s - m_run) <= 2^8
+        // and the accumulators keep their scale (exact after normalisation)
+        const float m_tile = mx * a.scale_log2;
+        const float m_new = (m_tile > st.m_run[qb] + 8.f) ? m_tile : st.m_run[qb];
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_use);
+        rescale |= alpha[qb] != 1.f;
+        float ls = 0.f;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-            sacc[kb][x] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][x], a.scale_log2, -m_use));
-            ls += sacc[kb][x];
-        }
-    bf16x8 pop[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+            for (int x = 0; x < 16; ++x) {
+                sacc[qb][kb][x] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][x], a.scale_log2, -m_use));
+                ls += sacc[qb][kb][x];
+            }
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const f32x16 &pp = sacc[kb];
-            const uint4 w4 = make_uint4(pack_bf16x2(pp[8 * sub + 0], pp[8 * sub + 1]),
-                                        pack_bf16x2(pp[8 * sub + 2], pp[8 * sub + 3]),
-                                        pack_bf16x2(pp[8 * sub + 4], pp[8 * sub + 5]),
-                                        pack_bf16x2(pp[8 * sub + 6], pp[8 * sub + 7]));
-            pop[2 * kb + sub] = __builtin_bit_cast(bf16x8, w4);
-        }
-    st.l_run = st.l_run * alpha + ls;
-    st.m_run = m_new;
-    if (__any(alpha != 1.f)) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int sub = 0; sub < 2; ++sub) {
+                const f32x16 &pp = sacc[qb][kb];
+                const uint4 w4 = make_uint4(pack_bf16x2(pp[8 * sub + 0], pp[8 * sub + 1]),
+                                            pack_bf16x2(pp[8 * sub + 2], pp[8 * sub + 3]),
+                                            pack_bf16x2(pp[8 * sub + 4], pp[8 * sub + 5]),
+                                            pack_bf16x2(pp[8 * sub + 6], pp[8 * sub + 7]));
+                pop[qb][2 * kb + sub] = __builtin_bit_cast(bf16x8, w4);
+            }
+        st.l_run[qb] = st.l_run[qb] * alpha[qb] + ls;
+        st.m_run[qb] = m_new;
+    }
+    if (__any(rescale)) {
 #pragma unroll
-            for (int x = 0; x < 16; ++x) st.oacc[db][x] *= alpha;
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) st.oacc[qb][db][x] *= alpha[qb];
     }
     // ---- O^T += V^T P^T: k-step s covers tile keys 16s..16s+15; lane half h
     // supplies keys 16s+4h+{0..3} and 16s+8+4h+{0..3}.  V^T comes from the
@@ -386,19 +404,22 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0 + 8 * T::ROW_BYTES));
             const v4i16 cat[2] = {lo, hi};
             const bf16x8 va = __builtin_bit_cast(bf16x8, cat);
-            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[s], st.oacc[db], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][s], st.oacc[qb][db], 0, 0, 0);
         }
     }
 }
 
 // Prologue: start the first two tiles' direct loads, build the RoPE table
-// and rotate this lane's query row.  LDS regions are __restrict__
-// parameters (see tile_step).
-template <int D, int NW>
-__device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v, uint4 *raw,
-                                         bool rvalid, int pos_idx, bf16x8 *qop, char *__restrict__ k0, char *__restrict__ v0,
+// and the key-label table, rotate this lane's query rows.  LDS regions are
+// __restrict__ parameters (see tile_step).
+template <int D, int NW, int QB>
+__device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v,
+                                         uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
+                                         bf16x8 (*qop)[D / 16], char *__restrict__ k0, char *__restrict__ v0,
                                          char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
-                                         double *__restrict__ invf, int *__restrict__ taus) {
+                                         double *__restrict__ invf, int *__restrict__ klab) {
     constexpr int NS = D / 16, NTH = 64 * NW;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
@@ -410,7 +431,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
     // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
     const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
-    if (tid <= 2 * kMaxBlock) taus[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
+    if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
     if (a.use_rope) {
         if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
@@ -421,26 +442,32 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
         }
     }
     ring_barrier();
-    if (a.use_rope) {
 #pragma unroll
-        for (int s = 0; s < NS / 2; ++s) rotate_pair(raw[s], raw[s + NS / 2], cs + pos_idx * (D / 2) + 16 * s + 8 * h);
+    for (int qb = 0; qb < QB; ++qb) {
+        if (a.use_rope) {
+#pragma unroll
+            for (int s = 0; s < NS / 2; ++s)
+                rotate_pair(raw[qb][s], raw[qb][s + NS / 2], cs + pos_idx[qb] * (D / 2) + 16 * s + 8 * h);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            qop[qb][s] = __builtin_bit_cast(bf16x8, rvalid[qb] ? raw[qb][s] : make_uint4(0, 0, 0, 0));
     }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, rvalid ? raw[s] : make_uint4(0, 0, 0, 0));
 }
 
-// NW waves x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles fed
-// by direct global->LDS loads.
-template <int D, int NW>
+// NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles
+// fed by direct global->LDS loads.
+template <int D, int NW, int QB>
 __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int ROWS_B = 32 * NW;
+    constexpr int ROWS_W = 32 * QB;
+    constexpr int ROWS_B = ROWS_W * NW;
     // one LDS array per ring stage and tensor
     __shared__ __attribute__((aligned(1024))) char k_st0[T::BYTES], k_st1[T::BYTES], k_st2[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
-    __shared__ __attribute__((aligned(16))) float2 cs_lds[64 * (D / 2)];
+    __shared__ __attribute__((aligned(16))) float2 cs_lds[kMaxBlock * (D / 2)];
     __shared__ double invf_lds[D / 2];
     __shared__ int klab_lds[2 * kMaxBlock + 1];
 
@@ -463,81 +490,94 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
     const int nt = t1 - t0;
 
-    // ---- tau (lane k of every wave holds tau[k]) and this lane's query row (one 32-row MFMA block per wave):
+    // ---- tau (lane k of every wave holds tau[k]) and this lane's query rows:
     // their loads go out before the tiles' so that waiting for them does not
     // drain the tile loads
     const int tau_v = a.tau[(size_t)b * B + min(lane, B - 1)];
-    const int rho = rb * ROWS_B + w * 32 + l32;
-    const bool rvalid = rho < R;
-    const int rr = rvalid ? rho : 0;
-    const int rrow = rr % R2;
-    const int qhead = kvh * g + rr / R2;
-    uint4 raw[NS];
-    {
-        const uint16_t *qp = a.q + (((size_t)b * R2 + rrow) * a.n_qh + qhead) * D + 8 * h;
+    bool rvalid[QB];
+    int rrow[QB], qhead[QB], pos_idx[QB];
+    uint4 raw[QB][NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) raw[s] = *reinterpret_cast<const uint4 *>(qp + 16 * s);  // rr is a valid row
+    for (int qb = 0; qb < QB; ++qb) {
+        const int rho = rb * ROWS_B + w * ROWS_W + qb * 32 + l32;
+        rvalid[qb] = rho < R;
+        const int rr = rvalid[qb] ? rho : 0;
+        rrow[qb] = rr % R2;
+        qhead[qb] = kvh * g + rr / R2;
+        pos_idx[qb] = rrow[qb] % B;
+        const uint16_t *qp = a.q + (((size_t)b * R2 + rrow[qb]) * a.n_qh + qhead[qb]) * D + 8 * h;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) raw[qb][s] = *reinterpret_cast<const uint4 *>(qp + 16 * s);  // valid row
     }
     const int jend = min(a.prefix + R2, t1 * kTileKeys);
-    bf16x8 qop[NS];
-    prologue<D, NW>(a, b, kvh, t0, jend, tau_v, raw, rvalid, rrow % B, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
-                    invf_lds, klab_lds);
-    RowInfo ri;
-    ri.t_row = __shfl(tau_v, rrow % B);
-    ri.is_data = rrow < B;
+    bf16x8 qop[QB][NS];
+    prologue<D, NW, QB>(a, b, kvh, t0, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
+                        invf_lds, klab_lds);
+    RowInfo<QB> ri;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        ri.t_row[qb] = __shfl(tau_v, pos_idx[qb]);
+        ri.is_data[qb] = rrow[qb] < B;
+    }
     const LdsOffs<D> offs = lds_offsets<D>(lane);
-    const bool wave_active = (rb * ROWS_B + w * 32) < R;
+    const bool wave_active = (rb * ROWS_B + w * ROWS_W) < R;
 
-    RowState<D> st;
+    RowState<D, QB> st;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) st.oacc[db][x] = 0.f;
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) st.oacc[qb][db][x] = 0.f;
+        st.m_run[qb] = -INFINITY;
+        st.l_run[qb] = 0.f;
+    }
 
     for (int it = 0; it < nt; it += 3) {
-        tile_step<D, NW>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2, cs_lds,
-                         klab_lds);
+        tile_step<D, NW, QB>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
+                             cs_lds, klab_lds);
         if (it + 1 < nt)
-            tile_step<D, NW>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0, v_st0,
-                             cs_lds, klab_lds);
+            tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
+                                 v_st0, cs_lds, klab_lds);
         if (it + 2 < nt)
-            tile_step<D, NW>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1, v_st1,
-                             cs_lds, klab_lds);
+            tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
+                                 v_st1, cs_lds, klab_lds);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 
     if (!wave_active) return;
-    // ---- epilogue: lane owns query l32; O^T rows dim = db*32 + 8*jj + 4*h + i
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    if (!rvalid) return;
-    const size_t row = ((size_t)b * R2 + rrow) * a.n_qh + qhead;
-    if (a.n_split == 1) {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        uint16_t *op = a.out + row * D + 4 * h;
+    // ---- epilogue: lane owns query l32 of each block; O^T rows dim = db*32 + 8*jj + 4*h + i
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
+        if (!rvalid[qb]) continue;
+        const size_t row = ((size_t)b * R2 + rrow[qb]) * a.n_qh + qhead[qb];
+        if (a.n_split == 1) {
+            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+            uint16_t *op = a.out + row * D + 4 * h;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const f32x16 &o = st.oacc[db];
-                uint2 pk;
-                pk.x = pack_bf16x2(o[4 * jj + 0] * inv, o[4 * jj + 1] * inv);
-                pk.y = pack_bf16x2(o[4 * jj + 2] * inv, o[4 * jj + 3] * inv);
-                *reinterpret_cast<uint2 *>(op + db * 32 + 8 * jj) = pk;
-            }
-    } else {
-        const size_t prow = (size_t)split * a.batch * R2 * a.n_qh + row;
-        float *op = a.ws_o + prow * D + 4 * h;
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x16 &o = st.oacc[qb][db];
+                    uint2 pk;
+                    pk.x = pack_bf16x2(o[4 * jj + 0] * inv, o[4 * jj + 1] * inv);
+                    pk.y = pack_bf16x2(o[4 * jj + 2] * inv, o[4 * jj + 3] * inv);
+                    *reinterpret_cast<uint2 *>(op + db * 32 + 8 * jj) = pk;
+                }
+        } else {
+            const size_t prow = (size_t)split * a.batch * R2 * a.n_qh + row;
+            float *op = a.ws_o + prow * D + 4 * h;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const f32x16 &o = st.oacc[db];
-                *reinterpret_cast<float4 *>(op + db * 32 + 8 * jj) =
-                    make_float4(o[4 * jj + 0], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]);
-            }
-        if (h == 0) a.ws_ml[prow] = make_float2(st.m_run, l_tot);
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x16 &o = st.oacc[qb][db];
+                    *reinterpret_cast<float4 *>(op + db * 32 + 8 * jj) =
+                        make_float4(o[4 * jj + 0], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]);
+                }
+            if (h == 0) a.ws_ml[prow] = make_float2(st.m_run[qb], l_tot);
+        }
     }
 }
 
@@ -644,8 +684,10 @@ AttnPlan attn_plan(const AttnShape &s) {
     AttnPlan p{};
     const int g = s.n_qh / s.n_kvh;
     p.rows = g * 2 * s.block;
+    // 32 query rows per wave; 8 waves when a kv head has more than 128 rows
+    p.qb = 1;
     p.nw = p.rows > 128 ? 8 : 4;
-    p.n_rb = (p.rows + 32 * p.nw - 1) / (32 * p.nw);
+    p.n_rb = (p.rows + 32 * p.qb * p.nw - 1) / (32 * p.qb * p.nw);
     const int nk = s.prefix + 2 * s.block;
     p.n_tiles = (nk + kTileKeys - 1) / kTileKeys;
     p.n_split = 1;
@@ -724,10 +766,10 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.scale_log2 = scale * kLog2e;
         const unsigned grid = (unsigned)((size_t)s.batch * s.n_kvh * p.n_rb * p.n_split);
         const dim3 blk(64 * p.nw);
-        if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), dim3(grid), blk, 0, st, a);
-        else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), dim3(grid), blk, 0, st, a);
-        else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), dim3(grid), blk, 0, st, a);
-        else hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), dim3(grid), blk, 0, st, a);
+        if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1>), dim3(grid), blk, 0, st, a);
+        else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1>), dim3(grid), blk, 0, st, a);
+        else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1>), dim3(grid), blk, 0, st, a);
+        else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1>), dim3(grid), blk, 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.n_split == 1) return e;
         const size_t rows_total = (size_t)s.batch * R2 * s.n_qh;

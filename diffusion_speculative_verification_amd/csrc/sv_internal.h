@@ -19,8 +19,9 @@ struct AttnShape {
 
 struct AttnPlan {
     int rows;            // rows per kv head = (n_qh / n_kvh) * 2 * block
-    int nw;              // waves per workgroup (32 query rows each)
-    int n_rb;            // row blocks of 32 * nw rows per kv head
+    int nw;              // waves per workgroup
+    int qb;              // 32-row query blocks per wave
+    int n_rb;            // row blocks of 32 * qb * nw rows per kv head
     int n_tiles;         // key tiles over prefix + 2 * block keys
     int n_split;         // prefix splits (1 = no combine pass)
     int tiles_per_split;

@@ -5,26 +5,28 @@
 // 关键设计 1 (paired layout [prompt | D | D~]), 关键设计 2 (mask A_ij from step
 // labels tau), 关键设计 3 (D~_k reuses D_k's RoPE position).
 //
-// bf16 kernel (attn_bf16_kernel), one workgroup = 4 waves x 32 query rows of
-// one kv head (the n_qh/n_kvh query heads of a GQA group are rows of the same
-// workgroup, so they share each K/V tile read; the row blocks of one kv head
-// run on the same XCD and meet its K/V in that XCD's L2), two workgroups per
-// CU, looping over 64-key tiles of [prompt | D | D~]:
-//   - K tile staged row-major in LDS, V tile staged transposed ([dim][key])
-//     so both MFMA operands are contiguous LDS reads; the next tile's global
-//     loads are in flight during the current tile's math, and the other
-//     workgroup on the CU computes while this one refills LDS;
+// bf16 kernel (attn_bf16_kernel): one workgroup = NW waves x 32 query rows
+// of one kv head (NW = 8 when the kv head has more than 128 rows, else 4;
+// the n_qh/n_kvh query heads of a GQA group are rows of the same workgroup,
+// so they share every K/V tile; row blocks and prefix splits of one kv head
+// are placed on one XCD so that they meet its K/V in that XCD's L2).  One
+// workgroup per CU (about 129 KB of LDS), looping over 64-key tiles of
+// [prompt | D | D~]:
+//   - a 3-stage LDS ring of (K, V) tiles, filled by direct global->LDS loads
+//     (global_load_lds_dwordx4) two tiles ahead of the math; both tiles are
+//     row-major with XOR-swizzled 16-byte chunks;
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on MFMA rows, queries
 //     on columns): each lane then owns one query's scores, so the row
 //     max/sum need one cross-lane exchange (lane ^ 32) per tile;
-//   - the mask is evaluated in registers from tau only on tiles that reach
-//     the response keys; prompt tiles take the unmasked path;
+//   - the mask is evaluated in registers from the step labels, only on
+//     tiles that reach the response keys; prompt tiles take the unmasked path;
 //   - online softmax in the log2 domain, P rounded to bf16 and fed straight
-//     from the S^T accumulators as the B operand of O^T = V^T P^T (same
-//     lane ownership, no shuffle); O is rescaled only when some lane's
-//     running max moved;
-//   - RoPE of Q and of the response keys is applied on load from a cos/sin
-//     table built in LDS (angles formed in float64).
+//     from the S^T accumulators as the B operand of O^T = V^T P^T (same lane
+//     ownership, no shuffle); V^T comes from the row-major V tile through
+//     the transposing LDS read ds_read_b64_tr_b16; O is rescaled only when
+//     the running max moves by more than 8 (log2 units);
+//   - RoPE of Q is applied on load and that of the response keys in place in
+//     the K tile, from a cos/sin table built in LDS (angles formed in float64).
 // Long prefixes with few (sequence, kv head) units are split over
 // workgroups (flash-decoding style) and merged by attn_combine_kernel.
 //
@@ -181,14 +183,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup barrier for the tile ring: this wave's LDS writes are complete
-// (lgkmcnt) before it arrives.  Unlike __syncthreads() it carries no
-// release fence, so the direct global->LDS loads of later tiles stay in
+// Workgroup barrier for the tile ring, with release/acquire ordering of
+// LDS only (the fences name the local address space): this wave's LDS
+// accesses complete (lgkmcnt) before it arrives, and the compiler may not
+// move LDS accesses across it.  Unlike __syncthreads() it does not order
+// global memory, so the direct global->LDS loads of later tiles stay in
 // flight across it; each wave waits for its own loads of the current tile
 // (wait_vmcnt) before arriving, which makes that tile visible to all.
 __device__ __forceinline__ void ring_barrier() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0), vmcnt/expcnt: no wait
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int D, int QB>
@@ -328,14 +333,13 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;
-                if (c >= 0) {
-                    const int lab = klab[min(c, 2 * kMaxBlock)];
+                const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;  // < 0: prompt key
+                const int lab = klab[max(0, min(c, 2 * kMaxBlock))];
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        const bool vis = lab >= 0 && visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1);
-                        sacc[qb][kb][x] = vis ? sacc[qb][kb][x] : -INFINITY;
-                    }
+                for (int qb = 0; qb < QB; ++qb) {
+                    // bitwise, so that the select stays a select (no branches)
+                    const bool vis = (c < 0) | ((lab >= 0) & visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1));
+                    sacc[qb][kb][x] = vis ? sacc[qb][kb][x] : -INFINITY;
                 }
             }
         }

@@ -21,6 +21,7 @@ oracle timed on this host over the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -59,6 +60,25 @@ def accept_bytes(c, n_rejecting: int) -> float:
     V = c.vocab
     small = c.batch * (c.block * 4 * 3 + (c.gamma + 1) * 4 + c.gamma * 4 * 3 + 4)
     return 4.0 * c.batch * c.gamma * V + n_rejecting * 2 * 4.0 * V + small
+
+
+def measured_traffic(call: str):
+    """HBM bytes per launch of `call` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration),
+    or None when that summary is missing or the kernel source has changed
+    since the counters were taken (its sha256 no longer matches)."""
+    path = os.path.join(ROOT, "profiles", "headline_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == call:
+            src = os.path.join(ROOT, "diffusion_speculative_verification_amd", "csrc", f[3])
+            if not os.path.exists(src):
+                return None
+            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            return int(f[2]) if digest == f[4] else None
+    return None
 
 
 def cpu_baseline(case, inp) -> dict:
@@ -155,9 +175,13 @@ def main():
     dom = ("spec_verify_accept", rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
     roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
         c_bytes / (HBM_PEAK_GBS * 1e9)
+    # traffic only applies to the headline workload the counters were taken on
+    headline = case.name == "headline"
+    rl_attn["traffic"] = measured_traffic("spec_verify_attn") if headline else None
+    rl_acc["traffic"] = measured_traffic("spec_verify_accept") if headline else None
     roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
-                "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": None,
-                "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
+                "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
+                "traffic_unit": "bytes/launch", "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:

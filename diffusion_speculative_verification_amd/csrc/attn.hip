@@ -157,19 +157,25 @@ __device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
                  : "memory", "m0");
 }
 
-// Keys at or past `jend` (the end of this workgroup's key range) read the
-// row jend - 1 instead: such tiles are never consumed, and re-reading one row
+// Tiles that lie wholly inside the prompt take the fast path: the cache rows
+// of one (sequence, kv head) are contiguous, so the source is a uniform tile
+// base plus this lane's row/chunk offset.  Other tiles go through key_row;
+// there, keys at or past `jend` (the end of this workgroup's key range) read
+// the row jend - 1 instead: such rows are never used, and re-reading one row
 // keeps them in cache.
 template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache, const uint16_t *fresh,
                                           int b, int kvh, int base, int jend, char *lds_tile, int w, int lane) {
     using T = Tile<D, IS_V>;
+    const bool fast = base + kTileKeys <= a.prefix;  // uniform
+    const uint16_t *tile = fast ? cache + (((size_t)b * a.n_kvh + kvh) * a.prefix + base) * D : nullptr;
 #pragma unroll
     for (int i = 0; i < T::LOADS / NW; ++i) {
         const int r0 = (w + NW * i) * T::ROWS_PER_LOAD;
         const int row = r0 + lane / T::NCH, pc = lane % T::NCH;
         const int q = pc ^ T::swz(row);
-        const uint16_t *src = key_row<D>(a, cache, fresh, b, kvh, min(base + row, jend - 1)) + q * 8;
+        const uint16_t *src = fast ? tile + row * D + q * 8
+                                   : key_row<D>(a, cache, fresh, b, kvh, min(base + row, jend - 1)) + q * 8;
         direct_load16(src, lds_tile + r0 * T::ROW_BYTES);
     }
 }

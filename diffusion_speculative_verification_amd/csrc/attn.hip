@@ -592,25 +592,39 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 }
 
 // Merge prefix splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per (row, head, 4 dims): the split partials of one row are
+// independent loads (unrolled, so many are in flight), and the 32 threads of
+// a row read the same (m, l) entries as one broadcast.
 template <typename T>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ ws_o,
                                                            const float2 *__restrict__ ws_ml, T *out,
-                                                           int n_split, size_t rows_total, int n_qh, int d) {
-    const size_t row0 = (size_t)blockIdx.x * n_qh;  // one (b, r): all heads
-    for (int idx = threadIdx.x; idx < n_qh * d; idx += blockDim.x) {
-        const int hh = idx / d, e = idx % d;
-        const size_t row = row0 + hh;
-        float M = -INFINITY;
-        for (int s = 0; s < n_split; ++s) M = fmaxf(M, ws_ml[s * rows_total + row].x);
-        float num = 0.f, den = 0.f;
-        for (int s = 0; s < n_split; ++s) {
-            const float2 ml = ws_ml[s * rows_total + row];
-            const float f = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-            den += f * ml.y;
-            num += f * ws_o[(s * rows_total + row) * d + e];
-        }
-        st_elem(out, row * d + e, den > 0.f ? num / den : 0.f);
+                                                           int n_split, size_t rows_total, int d) {
+    const int d4 = d >> 2;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= rows_total * d4) return;
+    const size_t row = gid / d4;
+    const int e = (int)(gid % d4) * 4;
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ws_ml[s * rows_total + row].x);
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < n_split; ++s) {
+        const float2 ml = ws_ml[s * rows_total + row];
+        const float4 o = *reinterpret_cast<const float4 *>(ws_o + (s * rows_total + row) * d + e);
+        const float f = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        den += f * ml.y;
+        num.x += f * o.x;
+        num.y += f * o.y;
+        num.z += f * o.z;
+        num.w += f * o.w;
     }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    st_elem(out, row * d + e + 0, num.x * inv);
+    st_elem(out, row * d + e + 1, num.y * inv);
+    st_elem(out, row * d + e + 2, num.z * inv);
+    st_elem(out, row * d + e + 3, num.w * inv);
 }
 
 // ------------------------------------------------------------ float32 path
@@ -783,9 +797,10 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.n_split == 1) return e;
         const size_t rows_total = (size_t)s.batch * R2 * s.n_qh;
-        hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, dim3((unsigned)((size_t)s.batch * R2)), dim3(256), 0,
+        const size_t threads = rows_total * (size_t)(s.head_dim / 4);
+        hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                            st, (const float *)a.ws_o, (const float2 *)a.ws_ml, (uint16_t *)out, p.n_split,
-                           rows_total, s.n_qh, s.head_dim);
+                           rows_total, s.head_dim);
         return hipGetLastError();
     }
     // float32: rotate into the workspace (if asked), then attend

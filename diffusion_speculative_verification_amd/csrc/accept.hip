@@ -9,8 +9,9 @@
 // Three launches on the caller's stream:
 //   lse_partial_kernel   vocab-parallel softmax normaliser of every verified
 //                        slot: a streaming pass over the float32 target
-//                        logits (16-byte coalesced loads, 4 in flight per
-//                        lane), per-lane running (max, sum) with the sum kept
+//                        logits (16-byte coalesced non-temporal loads -- the
+//                        logits are read once -- 4 in flight per lane),
+//                        per-lane running (max, sum) with the sum kept
 //                        in float64, merged per workgroup into one (m, s)
 //                        partial per (slot, vocab split).  This pass moves
 //                        almost all the bytes of the epilogue.
@@ -49,6 +50,9 @@ struct ResInfo {  // rejected slot of one sequence
     double s;     // merged sum exp(l - m)
 };
 
+// float4 as a clang vector type, for the non-temporal load builtin
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+
 constexpr int kResChunk = 2048;           // vocab entries per residual workgroup
 constexpr int kResRun = kResChunk / 256;  // contiguous entries per thread in the pick scan
 constexpr int kMaxChunks = 1024;          // vocab <= kResChunk * kMaxChunks = 2^21
@@ -74,7 +78,12 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 ok[u] = i + 256 * u < c1;
-                x[u] = ok[u] ? src[i + 256 * u] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                if (ok[u]) {
+                    const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(src + i + 256 * u));
+                    x[u] = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    x[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                }
             }
             float gm = m;
 #pragma unroll

@@ -144,14 +144,15 @@ __device__ __forceinline__ uint16_t u4_elem(const uint4 &v, int e) {
 // ROWS_PER_LOAD; lane l writes physical chunk l % NCH of its row and
 // therefore fetches the logical chunk that the swizzle places there.
 // One wave-wide direct global->LDS load: lane l's 16 bytes at `src` land at
-// LDS address lds_dst + 16 * l.  Issued as inline assembly so that the
+// LDS address lds_dst + 16 * l, with the non-temporal hint (K/V tiles are
+// streamed: each is read once per workgroup).  Issued as inline assembly so that the
 // compiler's wait insertion does not treat later LDS reads of other ring
 // stages as dependent on it: every wait on these loads is explicit
 // (wait_vmcnt), and no compiler-visible global load is issued while tile
 // loads are in flight inside the tile loop.
 __device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SV_LDS char *)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                  :
                  : "s"(m0), "v"(src)
                  : "memory", "m0");

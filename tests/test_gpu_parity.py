@@ -103,6 +103,7 @@ SMALL = synth.Case("edge", 3, 100, 8, 8, 8, 2, 128, 1000, "bf16", 1e6, "perturb"
     dict(vocab=1001),                          # vocab not a multiple of 4
     dict(vocab=1),                             # one token: always accepted
     dict(batch=1, prefix_len=5000, block=16, gamma=16),  # split prefix + combine
+    dict(batch=1, prefix_len=20000, n_qh=8, n_kvh=1),    # one kv head: 105 prefix splits + combine
     dict(dtype="f32", head_dim=64, n_qh=4, n_kvh=2, prefix_len=70),
     dict(dtype="f32", head_dim=128, prefix_len=0, block=4, gamma=4),
     dict(identity_every=1),                    # every sequence tau = identity

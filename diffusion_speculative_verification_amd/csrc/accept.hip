@@ -13,15 +13,20 @@
 //                        logits are read once -- 4 in flight per lane),
 //                        per-lane running (max, sum) with the sum kept
 //                        in float64, merged per workgroup into one (m, s)
-//                        partial per (slot, vocab split).  This pass moves
+//                        partial per (slot, vocab split).  The first split of
+//                        each slot also gathers the target logit and draft
+//                        probability of the slot's draft token, issued
+//                        beside its first stream loads.  This pass moves
 //                        almost all the bytes of the epilogue.
 //   accept_resid_kernel  one workgroup per (sequence, vocab chunk): wave 0
-//                        runs the acceptance scan of the sequence (lane r
-//                        merges the partials of the slot of draft step r+1,
-//                        alpha in float64, first rejection by one ballot);
-//                        chunk 0 writes accept_len, alpha and the draft part
-//                        of out_tokens; every workgroup then forms the
-//                        residual and target mass of its chunk at the
+//                        runs the acceptance scan of the sequence with lane k
+//                        on slot k (every operand it needs is loaded in one
+//                        round trip: labels, tokens, uniforms, partials,
+//                        gathers); alpha in float64, the first rejection in
+//                        draft order is a wave minimum over the rejected
+//                        steps.  Chunk 0 writes accept_len, alpha and the
+//                        draft part of out_tokens; every workgroup then forms
+//                        the residual and target mass of its chunk at the
 //                        rejected slot.
 //   residual_pick_kernel one workgroup per sequence: block scans over the
 //                        chunk sums find the chunk holding u * Z, a second
@@ -44,6 +49,13 @@ struct Part {   // normaliser partial of one (slot, vocab split)
     double s;   // sum exp(l - m)
 };
 
+struct Gath {  // draft token of one slot, gathered during the normaliser pass
+    float l;    // target logit of the draft token
+    float p;    // draft probability of the draft token
+    int ok;     // 0: the draft token lies outside [0, vocab)
+    int pad;
+};
+
 struct ResInfo {  // rejected slot of one sequence
     int slot;     // -1: every step accepted, nothing to resample
     float m;      // merged max logit of that slot
@@ -53,18 +65,31 @@ struct ResInfo {  // rejected slot of one sequence
 // float4 as a clang vector type, for the non-temporal load builtin
 typedef float nt_f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kResChunk = 2048;           // vocab entries per residual workgroup
-constexpr int kResRun = kResChunk / 256;  // contiguous entries per thread in the pick scan
-constexpr int kMaxChunks = 1024;          // vocab <= kResChunk * kMaxChunks = 2^21
+constexpr int kResChunk = 4096;             // vocab entries per residual workgroup
+constexpr int kPickChunk = kResChunk / 2;   // vocab entries per published chunk sum
+constexpr int kPickRun = kPickChunk / 256;  // contiguous entries per thread in the pick scan
+constexpr int kMaxChunks = 1024;            // vocab <= kPickChunk * kMaxChunks = 2^21
 
 template <bool VEC>
 __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restrict__ logits,
-                                                          const int32_t *__restrict__ tau, Part *parts,
+                                                          const float *__restrict__ probs,
+                                                          const int32_t *__restrict__ tokens,
+                                                          const int32_t *__restrict__ tau, Part *parts, Gath *gath,
                                                           int block, int gamma, int64_t vocab, int n_vsplit) {
     __shared__ float red_m[4];
     __shared__ double red_s[4];
     const int row = blockIdx.x / n_vsplit, sp = blockIdx.x % n_vsplit;
-    if (tau[row] > gamma) return;  // slot not verified in this call
+    const bool gatherer = sp == 0 && threadIdx.x == 0;
+    const int t = tau[row];
+    const int x = gatherer ? tokens[row] : -1;
+    if (t > gamma) return;  // slot not verified in this call
+    // the draft-token gather; its loads travel with the first stream loads
+    Gath g{0.f, 0.f, 0, 0};
+    if (gatherer && x >= 0 && x < vocab) {
+        g.l = logits[(size_t)row * vocab + x];
+        g.p = probs[(size_t)row * vocab + x];
+        g.ok = 1;
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float m = -INFINITY;
     double s = 0.0;
@@ -131,6 +156,7 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
         p.pad = 0.f;
         p.s = SS;
         parts[(size_t)row * n_vsplit + sp] = p;
+        if (sp == 0) gath[row] = g;
     }
 }
 
@@ -162,49 +188,67 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double *wave_to
     return base + inc - v;
 }
 
-// Acceptance scan of one sequence, run by one wave (SimSD 关键设计 4): lane r
-// merges the normaliser partials of the slot verified at draft step r+1,
-// forms alpha in float64 and tests u[r] < alpha; one ballot gives the first
-// rejection.  Returns L (number of leading accepts); *slot/*m_out/*s_out
-// describe the rejected slot (slot -1 when L == gamma).
-__device__ __forceinline__ int acceptance_scan(const float *__restrict__ logits, const float *__restrict__ probs,
-                                               const int32_t *__restrict__ tokens, const float *__restrict__ u,
-                                               const Part *__restrict__ parts, const int *inv_s, int b, int block,
-                                               int gamma, int64_t vocab, int n_vsplit, double *alpha_lane,
-                                               int *slot, float *m_out, double *s_out) {
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Acceptance scan of one sequence, run by one wave (SimSD 关键设计 4).  Lane
+// k takes slot k: it merges the slot's normaliser partials (max first, then
+// the rescaled sums, float64), forms alpha = min(1, p_theta(x)/p_phi(x)) of
+// its draft token in float64 and tests the uniform of its draft step
+// tau(k).  The first rejection in draft order is the smallest rejected step.
+// Returns L (number of leading accepts); *slot/*m_out/*s_out describe the
+// rejected slot (slot -1 when L == gamma).  *alpha_lane, *step and *token
+// are lane k's alpha, label and draft token.
+__device__ __forceinline__ int acceptance_scan(const int32_t *__restrict__ tokens, const int32_t *__restrict__ tau,
+                                               const float *__restrict__ u, const Part *__restrict__ parts,
+                                               const Gath *__restrict__ gath, int b, int block, int gamma,
+                                               int n_vsplit, double *alpha_lane, int *step, int *token, int *slot,
+                                               float *m_out, double *s_out) {
     const int lane = threadIdx.x & 63;
-    bool rejected = false;
-    float M = 0.f;
-    double S = 1.0, a = 0.0;
-    if (lane < gamma) {
-        const int k = inv_s[lane];
-        const size_t row = (size_t)b * block + k;
-        M = -INFINITY;
+    const bool in = lane < block;
+    const size_t row = (size_t)b * block + (in ? lane : 0);
+    // one round trip: every load below is independent of the others
+    const int t = in ? tau[row] : 0;
+    const int x = in ? tokens[row] : -1;
+    const float ul = lane < gamma ? u[(size_t)b * (gamma + 1) + lane] : 1.f;
+    const Gath g = in ? gath[row] : Gath{0.f, 0.f, 0, 0};
+    float M = -INFINITY;
+    double S = 0.0;
+    if (in) {
+#pragma unroll 4
         for (int i = 0; i < n_vsplit; ++i) M = fmaxf(M, parts[row * n_vsplit + i].m);
-        S = 0.0;
+#pragma unroll 4
         for (int i = 0; i < n_vsplit; ++i) {
             const Part p = parts[row * n_vsplit + i];
             if (p.m != -INFINITY) S += p.s * exp((double)p.m - (double)M);
         }
-        const int x = tokens[row];
-        if (x >= 0 && x < vocab) {  // an out-of-range draft token is rejected (alpha = 0)
-            const double pt = exp((double)logits[row * vocab + x] - (double)M) / S;
-            const double pd = (double)probs[row * vocab + x];
-            a = (pd > 0.0) ? fmin(1.0, pt / pd) : 1.0;
-        }
-        rejected = !((double)u[(size_t)b * (gamma + 1) + lane] < a);
     }
-    *alpha_lane = a;
-    const unsigned long long rej = __ballot(rejected);
-    const int L = rej ? (__ffsll((long long)rej) - 1) : gamma;
-    const int src = L < gamma ? L : 0;
-    *slot = L < gamma ? inv_s[L] : -1;
+    const bool ver = in && t >= 1 && t <= gamma;  // slot verified at draft step t
+    double a = 0.0;
+    if (ver && g.ok) {  // an out-of-range draft token is rejected (alpha = 0)
+        const double pt = exp((double)g.l - (double)M) / S;
+        const double pd = (double)g.p;
+        a = (pd > 0.0) ? fmin(1.0, pt / pd) : 1.0;
+    }
+    const float ur = __shfl(ul, ver ? t - 1 : 0);  // uniform of draft step t
+    const bool rejected = ver && !((double)ur < a);
+    const int L = wave_min_int(rejected ? t - 1 : gamma);
+    const unsigned long long at = __ballot(rejected && t - 1 == L);
+    const int src = at ? (__ffsll((long long)at) - 1) : 0;
+    *slot = L < gamma ? src : -1;
     *m_out = __shfl(M, src);
     *s_out = __shfl(S, src);
+    *alpha_lane = a;
+    *step = t;
+    *token = x;
     return L;
 }
 
-// Acceptance + residual mass, one workgroup per (sequence, vocab chunk).
+// Acceptance + residual mass, one workgroup per (sequence, vocab chunk of
+// kResChunk entries); the masses are published per half chunk.
 // Every workgroup of a sequence repeats the (small) acceptance scan; chunk 0
 // writes accept_len, alpha, the draft part of out_tokens and the rejected
 // slot's normaliser for the pick kernel.  If a step was rejected, each
@@ -213,35 +257,26 @@ __device__ __forceinline__ int acceptance_scan(const float *__restrict__ logits,
 template <bool VEC>
 __global__ void __launch_bounds__(256) accept_resid_kernel(
     const float *__restrict__ logits, const float *__restrict__ probs, const int32_t *__restrict__ tokens,
-    const int32_t *__restrict__ tau, const float *__restrict__ u, const Part *__restrict__ parts, int block,
-    int gamma, int64_t vocab, int n_vsplit, int n_chunk, int32_t *accept_len, int32_t *out_tokens,
-    float *alpha_out, ResInfo *res, double2 *chunk_sums) {
-    __shared__ int inv_s[64];
-    __shared__ int tau_s[64];
+    const int32_t *__restrict__ tau, const float *__restrict__ u, const Part *__restrict__ parts,
+    const Gath *__restrict__ gath, int block, int gamma, int64_t vocab, int n_vsplit, int n_chunk, int n_pick,
+    int32_t *accept_len, int32_t *out_tokens, float *alpha_out, ResInfo *res, double2 *chunk_sums) {
     __shared__ int slot_s;
     __shared__ float m_s;
     __shared__ double s_s;
-    __shared__ double red_a[4], red_b[4];
+    __shared__ double red_a[2][4], red_b[2][4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x / n_chunk, c = blockIdx.x % n_chunk;
-    if (tid < 64) inv_s[tid] = 0;  // tau is a permutation by contract; keep slot indices in range regardless
-    __syncthreads();
-    if (tid < block) {
-        const int t = tau[(size_t)b * block + tid];
-        tau_s[tid] = t;
-        if (t >= 1 && t <= block) inv_s[t - 1] = tid;
-    }
-    __syncthreads();
     if (w == 0) {
         double a, S;
-        int slot;
+        int slot, t, x;
         float M;
-        const int L = acceptance_scan(logits, probs, tokens, u, parts, inv_s, b, block, gamma, vocab, n_vsplit, &a,
-                                      &slot, &M, &S);
+        const int L = acceptance_scan(tokens, tau, u, parts, gath, b, block, gamma, n_vsplit, &a, &t, &x, &slot,
+                                      &M, &S);
         if (c == 0) {
-            if (lane < gamma && alpha_out) alpha_out[(size_t)b * gamma + lane] = (float)a;
-            if (lane < block)
-                out_tokens[(size_t)b * block + lane] = (tau_s[lane] <= L) ? tokens[(size_t)b * block + lane] : -1;
+            if (lane < block) {
+                if (alpha_out && t >= 1 && t <= gamma) alpha_out[(size_t)b * gamma + t - 1] = (float)a;
+                out_tokens[(size_t)b * block + lane] = (t <= L) ? x : -1;
+            }
             if (lane == 0) {
                 accept_len[b] = L;
                 ResInfo r;
@@ -263,33 +298,55 @@ __global__ void __launch_bounds__(256) accept_resid_kernel(
     const float *pr = probs + row * vocab;
     const int64_t v0 = (int64_t)c * kResChunk;
     const int n = (int)min((int64_t)kResChunk, vocab - v0);
-    double ra = 0.0, pa = 0.0;
+    // sums per half chunk (kPickChunk entries each): h = 0 first half, 1 second
+    double ra[2] = {0.0, 0.0}, pa[2] = {0.0, 0.0};
     if (VEC) {
+        // all loads of the chunk in flight before any use; float4 k of a
+        // thread lies in half k / 2
+        constexpr int U = kResChunk / 1024;
+        const int n4 = n >> 2;
         const float4 *l4 = reinterpret_cast<const float4 *>(lr + v0);
         const float4 *p4 = reinterpret_cast<const float4 *>(pr + v0);
-        for (int i = tid; i < (n >> 2); i += 256) {
-            const float4 x = l4[i], q = p4[i];
+        float4 xl[U], xp[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int i = tid + 256 * k;
+            xl[k] = i < n4 ? l4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            xp[k] = i < n4 ? p4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (tid + 256 * k >= n4) continue;
+            const int h = k / (U / 2);
             double r, pt;
-            masses(x.x, q.x, M, inv_sum, r, pt); ra += r; pa += pt;
-            masses(x.y, q.y, M, inv_sum, r, pt); ra += r; pa += pt;
-            masses(x.z, q.z, M, inv_sum, r, pt); ra += r; pa += pt;
-            masses(x.w, q.w, M, inv_sum, r, pt); ra += r; pa += pt;
+            masses(xl[k].x, xp[k].x, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].y, xp[k].y, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].z, xp[k].z, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].w, xp[k].w, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
         }
     } else {
-        for (int i = tid; i < n; i += 256) {
-            double r, pt;
-            masses(lr[v0 + i], pr[v0 + i], M, inv_sum, r, pt);
-            ra += r;
-            pa += pt;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll 4
+            for (int i = h * kPickChunk + tid; i < min(n, (h + 1) * kPickChunk); i += 256) {
+                double r, pt;
+                masses(lr[v0 + i], pr[v0 + i], M, inv_sum, r, pt);
+                ra[h] += r;
+                pa[h] += pt;
+            }
         }
     }
-    ra = wave_sum(ra);
-    pa = wave_sum(pa);
-    if (lane == 0) { red_a[w] = ra; red_b[w] = pa; }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        ra[h] = wave_sum(ra[h]);
+        pa[h] = wave_sum(pa[h]);
+        if (lane == 0) { red_a[h][w] = ra[h]; red_b[h][w] = pa[h]; }
+    }
     __syncthreads();
-    if (tid == 0)
-        chunk_sums[(size_t)b * n_chunk + c] =
-            make_double2(red_a[0] + red_a[1] + red_a[2] + red_a[3], red_b[0] + red_b[1] + red_b[2] + red_b[3]);
+    if (tid < 2 && 2 * c + tid < n_pick)
+        chunk_sums[(size_t)b * n_pick + 2 * c + tid] =
+            make_double2(red_a[tid][0] + red_a[tid][1] + red_a[tid][2] + red_a[tid][3],
+                         red_b[tid][0] + red_b[tid][1] + red_b[tid][2] + red_b[tid][3]);
 }
 
 // Residual pick: one workgroup per sequence finds the chunk whose running sum
@@ -310,18 +367,24 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
     __shared__ double sel_base;
     __shared__ int pick_first, pick_last, last_chunk;
     const int tid = threadIdx.x, b = blockIdx.x;
-    const ResInfo ri = res[b];
-    if (ri.slot < 0) return;
-    // thread t owns chunks [t * CPT, t * CPT + CPT)
-    double cr[CPT], ct[CPT], my_r = 0.0, my_t = 0.0;
+    // thread t owns chunks [t * CPT, t * CPT + CPT); the chunk sums are loaded
+    // beside the sequence's ResInfo (workspace memory, read before the
+    // early exit so both loads share one round trip)
+    double2 v[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int ch = tid * CPT + k;
-        const double2 v = ch < n_chunk ? chunk_sums[(size_t)b * n_chunk + ch] : make_double2(0.0, 0.0);
-        cr[k] = v.x;
-        ct[k] = v.y;
-        my_r += v.x;
-        my_t += v.y;
+        v[k] = ch < n_chunk ? chunk_sums[(size_t)b * n_chunk + ch] : make_double2(0.0, 0.0);
+    }
+    const ResInfo ri = res[b];
+    if (ri.slot < 0) return;
+    double cr[CPT], ct[CPT], my_r = 0.0, my_t = 0.0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        cr[k] = v[k].x;
+        ct[k] = v[k].y;
+        my_r += v[k].x;
+        my_t += v[k].y;
     }
     if (tid == 0) { pick_first = 0x7fffffff; pick_last = -1; last_chunk = -1; sel_chunk = 0x7fffffff; sel_base = 0.0; }
     const double ex_r = block_exclusive_scan(my_r, wave_tot);
@@ -355,22 +418,29 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
         sel_base = cand_base;
     }
     __syncthreads();
-    // the chosen chunk: thread t takes kResRun contiguous entries
+    // the chosen chunk: thread t takes kPickRun contiguous entries
     const int cc = (sel_chunk == 0x7fffffff) ? 0 : sel_chunk;
     const double base = sel_base;
-    const int64_t v0 = (int64_t)cc * kResChunk;
-    const int n = (int)min((int64_t)kResChunk, vocab - v0);
+    const int64_t v0 = (int64_t)cc * kPickChunk;
+    const int n = (int)min((int64_t)kPickChunk, vocab - v0);
     const size_t row = (size_t)b * block + ri.slot;
     const float *lr = logits + row * vocab + v0;
     const float *pr = probs + row * vocab + v0;
     const double inv_sum = 1.0 / ri.s;
-    double mass[kResRun], mine = 0.0;
+    float xl[kPickRun], xp[kPickRun];
+#pragma unroll
+    for (int k = 0; k < kPickRun; ++k) {  // every load in flight before any use
+        const int i = tid * kPickRun + k;
+        xl[k] = i < n ? lr[i] : 0.f;
+        xp[k] = i < n ? pr[i] : 0.f;
+    }
+    double mass[kPickRun], mine = 0.0;
     int lastpos = -1;
 #pragma unroll
-    for (int k = 0; k < kResRun; ++k) {
-        const int i = tid * kResRun + k;
+    for (int k = 0; k < kPickRun; ++k) {
+        const int i = tid * kPickRun + k;
         double r = 0.0, pt = 0.0;
-        if (i < n) masses(lr[i], pr[i], ri.m, inv_sum, r, pt);
+        if (i < n) masses(xl[k], xp[k], ri.m, inv_sum, r, pt);
         mass[k] = use_t ? pt : r;
         mine += mass[k];
         if (mass[k] > 0.0) lastpos = i;
@@ -379,9 +449,9 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
     double run = base + block_exclusive_scan(mine, wave_tot);
     if (run <= thr && run + mine > thr) {
 #pragma unroll
-        for (int k = 0; k < kResRun; ++k) {
+        for (int k = 0; k < kPickRun; ++k) {
             run += mass[k];
-            if (run > thr) { atomicMin(&pick_first, tid * kResRun + k); break; }
+            if (run > thr) { atomicMin(&pick_first, tid * kPickRun + k); break; }
         }
     }
     __syncthreads();
@@ -403,10 +473,12 @@ AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab) {
     p.n_vsplit = (int)vs;
     p.chunk = kResChunk;
     p.n_chunk = (int)((vocab + p.chunk - 1) / p.chunk);
+    p.n_pick = (int)((vocab + kPickChunk - 1) / kPickChunk);
     p.off_part = 0;
-    p.off_res = p.off_part + align_up((size_t)p.rows * p.n_vsplit * sizeof(Part));
+    p.off_gath = p.off_part + align_up((size_t)p.rows * p.n_vsplit * sizeof(Part));
+    p.off_res = p.off_gath + align_up((size_t)p.rows * sizeof(Gath));
     p.off_chunk = p.off_res + align_up((size_t)batch * sizeof(ResInfo));
-    p.ws_total = p.off_chunk + align_up((size_t)batch * p.n_chunk * sizeof(double2));
+    p.ws_total = p.off_chunk + align_up((size_t)batch * p.n_pick * sizeof(double2));
     return p;
 }
 
@@ -416,28 +488,31 @@ hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *
                          int32_t *out_tokens, float *alpha, void *ws, hipStream_t st) {
     char *base = (char *)ws;
     Part *parts = (Part *)(base + p.off_part);
+    Gath *gath = (Gath *)(base + p.off_gath);
     ResInfo *res = (ResInfo *)(base + p.off_res);
     double2 *chunks = (double2 *)(base + p.off_chunk);
     const unsigned g1 = (unsigned)((size_t)p.rows * p.n_vsplit);
     if ((vocab & 3) == 0)
-        hipLaunchKernelGGL(lse_partial_kernel<true>, dim3(g1), dim3(256), 0, st, logits, tau, parts, block, gamma,
-                           vocab, p.n_vsplit);
+        hipLaunchKernelGGL(lse_partial_kernel<true>, dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau, parts,
+                           gath, block, gamma, vocab, p.n_vsplit);
     else
-        hipLaunchKernelGGL(lse_partial_kernel<false>, dim3(g1), dim3(256), 0, st, logits, tau, parts, block,
-                           gamma, vocab, p.n_vsplit);
+        hipLaunchKernelGGL(lse_partial_kernel<false>, dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau,
+                           parts, gath, block, gamma, vocab, p.n_vsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)((size_t)batch * p.n_chunk));
     if ((vocab & 3) == 0)
-        hipLaunchKernelGGL(accept_resid_kernel<true>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts, block,
-                           gamma, vocab, p.n_vsplit, p.n_chunk, accept_len, out_tokens, alpha, res, chunks);
+        hipLaunchKernelGGL(accept_resid_kernel<true>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts, gath,
+                           block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, accept_len, out_tokens, alpha, res,
+                           chunks);
     else
         hipLaunchKernelGGL(accept_resid_kernel<false>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts,
-                           block, gamma, vocab, p.n_vsplit, p.n_chunk, accept_len, out_tokens, alpha, res, chunks);
+                           gath, block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, accept_len, out_tokens, alpha,
+                           res, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(residual_pick_kernel, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks, out_tokens,
-                       block, gamma, vocab, p.n_chunk);
+                       block, gamma, vocab, p.n_pick);
     return hipGetLastError();
 }
 

@@ -45,9 +45,10 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
 struct AcceptPlan {
     int rows;        // batch * block logits rows
     int n_vsplit;    // vocab splits of the normaliser pass
-    int64_t chunk;   // vocab elements per residual chunk
-    int n_chunk;
-    size_t off_part, off_res, off_chunk, ws_total;
+    int64_t chunk;   // vocab elements per residual workgroup
+    int n_chunk;     // residual workgroups per sequence
+    int n_pick;      // published residual sums per sequence (half chunks)
+    size_t off_part, off_gath, off_res, off_chunk, ws_total;
 };
 
 AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab);

@@ -85,15 +85,18 @@ __global__ void __launch_bounds__(256) rope_kernel(const T *__restrict__ q_in, c
 
 // ------------------------------------------------------- bf16 MFMA kernel
 // LDS tile layout: 64 rows (keys) x D bf16, rows of D*2 bytes, 16-byte
-// chunks XOR-swizzled per row so that both the S^T operand reads (16 B of one
-// row per lane, 8 consecutive rows per LDS cycle) and the transposed V reads
-// (8 B from 4 consecutive rows per 16-lane group) are bank-conflict free.
-// K tiles (IS_V = false): chunk ^ (row & 7), so the 8 rows that one LDS
-// cycle serves for the 16-byte S^T operand reads land in 8 distinct bank
-// groups.  V tiles (IS_V = true): chunk ^ ((row & 7) << 1) for D = 128 and
-// chunk ^ ((row & 3) << 1) for D = 64, so the two adjacent chunks that each
-// row contributes to a transposing read stay adjacent and the 4 rows of a
-// 16-lane group hit disjoint banks.
+// chunks XOR-swizzled per row so that both the S^T operand reads and the
+// transposed V reads are bank-conflict free.  The LDS serves 256 bytes (64
+// banks of 4 bytes) per cycle: 16 lanes of a 16-byte read, 32 lanes of an
+// 8-byte read.
+// K tiles (IS_V = false): the 16 lanes served together read 16 consecutive
+// rows at one logical chunk, so the swizzle gives those rows 16 distinct
+// bank groups: chunk ^ (row & 15) for D = 128 (one row = one 256-byte bank
+// line), chunk ^ ((row >> 1) & 7) for D = 64 (two rows per bank line).
+// V tiles (IS_V = true): the 32 lanes served together read 4 consecutive
+// rows x 4 logical chunks (8 bytes per lane), so the 4 rows must map that
+// chunk quad to disjoint bank groups: chunk ^ ((row & 3) << 2) for D = 128;
+// for D = 64 chunk ^ ((row & 3) << 1) keeps the 2 rows of a bank line apart.
 template <int D, bool IS_V>
 struct Tile {
     static constexpr int NCH = D / 8;             // 16-byte chunks per row
@@ -102,7 +105,8 @@ struct Tile {
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide 16 B/lane load fills
     static constexpr int LOADS = kTileKeys / ROWS_PER_LOAD;  // wave loads per tile and tensor
     __device__ static __forceinline__ int swz(int row) {
-        return IS_V ? (D == 128 ? ((row & 7) << 1) : ((row & 3) << 1)) : (row & 7);
+        if (IS_V) return D == 128 ? ((row & 3) << 2) : ((row & 3) << 1);
+        return D == 128 ? (row & 15) : ((row >> 1) & 7);
     }
     __device__ static __forceinline__ int off(int row, int chunk) {  // byte offset of a logical chunk
         return row * ROW_BYTES + ((chunk ^ swz(row)) << 4);
@@ -156,6 +160,43 @@ __device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
                  :
                  : "s"(m0), "v"(src)
                  : "memory", "m0");
+}
+
+// The same load with a uniform 64-bit base in scalar registers plus this
+// lane's 32-bit byte offset (the scalar-base address form), and the LDS
+// destination given as a wave-uniform address: no per-load vector address
+// arithmetic.
+__device__ __forceinline__ void direct_load16_s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+// Loop-invariant parts of this wave's tile loads: for load i, this lane's
+// byte offset inside a prompt tile of K and of V (row and swizzled chunk),
+// and the LDS byte offset of the rows it fills (wave-uniform).
+template <int D, int NW>
+struct LoadOffs {
+    static constexpr int N = Tile<D, false>::LOADS / NW;
+    uint32_t k[N], v[N], lds[N];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ LoadOffs<D, NW> load_offsets(int w, int lane) {
+    using TK = Tile<D, false>;
+    using TV = Tile<D, true>;
+    LoadOffs<D, NW> o;
+#pragma unroll
+    for (int i = 0; i < LoadOffs<D, NW>::N; ++i) {
+        const int r0 = (w + NW * i) * TK::ROWS_PER_LOAD;
+        const int row = r0 + lane / TK::NCH, pc = lane % TK::NCH;
+        o.k[i] = (uint32_t)((row * D + (pc ^ TK::swz(row)) * 8) * 2);
+        o.v[i] = (uint32_t)((row * D + (pc ^ TV::swz(row)) * 8) * 2);
+        o.lds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(r0 * TK::ROW_BYTES));
+    }
+    return o;
 }
 
 // Tiles that lie wholly inside the prompt take the fast path: the cache rows
@@ -231,6 +272,9 @@ __device__ __forceinline__ void rotate_pair(uint4 &lo, uint4 &hi, const float2 *
     hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
 }
 
+// (1.0, 1.0) in bf16
+constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 template <int QB>
 struct RowInfo {
     int t_row[QB];     // step label of each row's slot
@@ -238,19 +282,30 @@ struct RowInfo {
 };
 
 // Loop-invariant LDS byte offsets of this lane's MFMA operand reads.  The
-// swizzle of a row depends on row & 7 only, and every read family below
-// moves in steps of 8 rows, so the swizzled chunk is fixed per lane:
+// K swizzle depends on row & 15 and the V swizzle on row & 3 only, and each
+// read family below moves in steps of 16 (K: 32) rows, so the swizzled chunk
+// is fixed per lane:
 //   S^T operand (K, row kb*32 + l32, chunk 2s + h):  k[s] + kb * 32 * ROW_BYTES
 //   V^T operand (V, rows 16s + 4h + j/4 (+ 8), dims 32db + v_dim_lo):
 //                                          v[db] + 16 * s * ROW_BYTES (+ 8 * ROW_BYTES)
 template <int D>
 struct LdsOffs {
     int k[D / 16];
-    int v[D / 32];
+    uint32_t v[D / 32];  // absolute LDS addresses in V stage 0 (see vbase_opaque)
 };
 
+// Per-lane V read bases hold the absolute LDS address of V stage 0 and are
+// hidden from constant folding, so that each transposing read of any stage
+// is this base plus an immediate offset below 64 KB (the DS offset field);
+// without this the compiler re-forms every V address (one VALU op per read)
+// because the stages lie above 64 KB.
+__device__ __forceinline__ uint32_t vbase_opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <int D>
-__device__ __forceinline__ LdsOffs<D> lds_offsets(int lane) {
+__device__ __forceinline__ LdsOffs<D> lds_offsets(int lane, const char *v_stage0) {
     using TK = Tile<D, false>;
     using T = Tile<D, true>;
     const int h = lane >> 5, l32 = lane & 31, gq = lane >> 4, jl = lane & 15;
@@ -262,7 +317,8 @@ __device__ __forceinline__ LdsOffs<D> lds_offsets(int lane) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
         const int dim = 32 * db + v_dim_lo;
-        o.v[db] = T::off(k0, dim >> 3) + ((dim & 7) << 1);
+        o.v[db] = vbase_opaque((uint32_t)(uintptr_t)(const SV_LDS char *)v_stage0 + T::off(k0, dim >> 3) +
+                               ((dim & 7) << 1));
     }
     return o;
 }
@@ -278,7 +334,9 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                                           const RowInfo<QB> &ri, const LdsOffs<D> &lo_, const bf16x8 (*qop)[D / 16],
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
                                           char *__restrict__ kn, char *__restrict__ vn,
-                                          const float2 *__restrict__ cs, const int *__restrict__ klab) {
+                                          const float2 *__restrict__ cs, const int *__restrict__ klab,
+                                          const char *v_stage0, const LoadOffs<D, NW> &ldo,
+                                          const uint16_t *k_unit, const uint16_t *v_unit) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
@@ -305,12 +363,27 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
         }
         ring_barrier();
     }
-    // ---- refill the stage consumed in the previous step (issued on every
-    // step, so the number of loads in flight is the same on every path)
-    {
-        const int nb = (t0 + it + 2) * kTileKeys;
+    // ---- refill the stage consumed in the previous step with tile it + 2
+    // (issued on every step, so the number of loads in flight is the same on
+    // every path).  A prompt tile's loads take the scalar-base form; an
+    // active wave issues them between its S MFMAs below, one every few
+    // k-steps, so that their issue overlaps matrix work instead of queueing
+    // behind the other waves' loads right after the barrier.
+    constexpr int NL = LoadOffs<D, NW>::N;  // loads per tensor
+    const int nb = (t0 + it + 2) * kTileKeys;
+    const bool prompt_refill = nb + kTileKeys <= P;  // uniform
+    const uint16_t *kb_src = k_unit + (size_t)nb * D, *vb_src = v_unit + (size_t)nb * D;
+    const uint32_t kn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)kn, vn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)vn;
+    auto refill = [&](int i) {  // load i of 2 * NL: K loads first, then V
+        if (i < NL) direct_load16_s(kb_src, ldo.k[i], kn_lds + ldo.lds[i]);
+        else direct_load16_s(vb_src, ldo.v[i - NL], vn_lds + ldo.lds[i - NL]);
+    };
+    if (!prompt_refill) {
         load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
         load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
+    } else if (!wave_active) {
+#pragma unroll
+        for (int i = 0; i < 2 * NL; ++i) refill(i);
     }
     if (!wave_active) return;
 
@@ -322,10 +395,12 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) sacc[qb][kb][x] = 0.f;
+    constexpr int KSTEP = NS / NL;  // S MFMAs between two refill loads
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (prompt_refill && (2 * s + kb) % KSTEP == 1) refill((2 * s + kb) / KSTEP);
             const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + lo_.k[s] + kb * 32 * T::ROW_BYTES);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -371,24 +446,26 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_use);
         rescale |= alpha[qb] != 1.f;
-        float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
+            for (int x = 0; x < 16; ++x)
                 sacc[qb][kb][x] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][x], a.scale_log2, -m_use));
-                ls += sacc[qb][kb][x];
-            }
+        // P rounded to bf16 is what the PV product uses; the row sum adds the
+        // same rounded values, two per dot2 against (1, 1)
+        float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
                 const f32x16 &pp = sacc[qb][kb];
-                const uint4 w4 = make_uint4(pack_bf16x2(pp[8 * sub + 0], pp[8 * sub + 1]),
-                                            pack_bf16x2(pp[8 * sub + 2], pp[8 * sub + 3]),
-                                            pack_bf16x2(pp[8 * sub + 4], pp[8 * sub + 5]),
-                                            pack_bf16x2(pp[8 * sub + 6], pp[8 * sub + 7]));
-                pop[qb][2 * kb + sub] = __builtin_bit_cast(bf16x8, w4);
+                uint32_t pw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pw[e] = pack_bf16x2(pp[8 * sub + 2 * e], pp[8 * sub + 2 * e + 1]);
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[e]), kOnesBf16x2, ls, false);
+                }
+                pop[qb][2 * kb + sub] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
             }
         st.l_run[qb] = st.l_run[qb] * alpha[qb] + ls;
         st.m_run[qb] = m_new;
@@ -406,13 +483,15 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // row-major V tile through the transposing LDS read: in 16-lane group gq,
     // lane j = 4k + c reads row key(k) at dims dim0 + 4c, and lane i receives
     // the four keys of dim dim0 + i.
+    const uint32_t vt_off = (uint32_t)(vt - v_stage0);  // 0, 1 or 2 tile sizes
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const int o0 = lo_.v[db] + 16 * s * T::ROW_BYTES;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(vt + o0 + 8 * T::ROW_BYTES));
+            const uint32_t o0 = lo_.v[db] + vt_off + 16 * s * T::ROW_BYTES;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)o0);
+            const v4i16 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)(o0 + 8 * T::ROW_BYTES));
             const v4i16 cat[2] = {lo, hi};
             const bf16x8 va = __builtin_bit_cast(bf16x8, cat);
 #pragma unroll
@@ -530,7 +609,12 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
         ri.t_row[qb] = __shfl(tau_v, pos_idx[qb]);
         ri.is_data[qb] = rrow[qb] < B;
     }
-    const LdsOffs<D> offs = lds_offsets<D>(lane);
+    const LdsOffs<D> offs = lds_offsets<D>(lane, v_st0);
+    const LoadOffs<D, NW> ldo = load_offsets<D, NW>(w, lane);
+    // K/V cache rows of this (sequence, kv head); only dereferenced for
+    // tiles that lie wholly inside the prompt
+    const size_t unit_off = ((size_t)b * a.n_kvh + kvh) * a.prefix * D;
+    const uint16_t *k_unit = a.k_cache + unit_off, *v_unit = a.v_cache + unit_off;
     const bool wave_active = (rb * ROWS_B + w * ROWS_W) < R;
 
     RowState<D, QB> st;
@@ -546,13 +630,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 
     for (int it = 0; it < nt; it += 3) {
         tile_step<D, NW, QB>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
-                             cs_lds, klab_lds);
+                             cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
         if (it + 1 < nt)
             tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
-                                 v_st0, cs_lds, klab_lds);
+                                 v_st0, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
         if (it + 2 < nt)
             tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
-                                 v_st1, cs_lds, klab_lds);
+                                 v_st1, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 

@@ -272,6 +272,13 @@ __device__ __forceinline__ void rotate_pair(uint4 &lo, uint4 &hi, const float2 *
     hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
 }
 
+// Row stride (in float2 entries) of the cos/sin table in LDS: one entry per
+// rotate-half pair plus one of padding, so that the 32 lanes of a wave half,
+// which read the same pair index at 32 different positions, hit distinct
+// banks.
+template <int D>
+constexpr int kCsStride = D / 2 + 1;
+
 // (1.0, 1.0) in bf16
 constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -357,7 +364,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
             uint4 *plo = reinterpret_cast<uint4 *>(kt + T::off(row, cp));
             uint4 *phi = reinterpret_cast<uint4 *>(kt + T::off(row, cp + T::NCH / 2));
             uint4 lo = *plo, hi = *phi;
-            rotate_pair(lo, hi, cs + ((j - P) % B) * (D / 2) + 8 * cp);
+            rotate_pair(lo, hi, cs + ((j - P) % B) * kCsStride<D> + 8 * cp);
             *plo = lo;
             *phi = hi;
         }
@@ -528,7 +535,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
         ring_barrier();
         for (int idx = tid; idx < B * (D / 2); idx += NTH) {
             const int pr = idx / (D / 2), i = idx % (D / 2);
-            cs[idx] = rope_cs((double)P + (double)pr, invf[i]);
+            cs[pr * kCsStride<D> + i] = rope_cs((double)P + (double)pr, invf[i]);
         }
     }
     ring_barrier();
@@ -537,7 +544,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
         if (a.use_rope) {
 #pragma unroll
             for (int s = 0; s < NS / 2; ++s)
-                rotate_pair(raw[qb][s], raw[qb][s + NS / 2], cs + pos_idx[qb] * (D / 2) + 16 * s + 8 * h);
+                rotate_pair(raw[qb][s], raw[qb][s + NS / 2], cs + pos_idx[qb] * kCsStride<D> + 16 * s + 8 * h);
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -557,7 +564,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     // one LDS array per ring stage and tensor
     __shared__ __attribute__((aligned(1024))) char k_st0[T::BYTES], k_st1[T::BYTES], k_st2[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
-    __shared__ __attribute__((aligned(16))) float2 cs_lds[kMaxBlock * (D / 2)];
+    __shared__ __attribute__((aligned(16))) float2 cs_lds[kMaxBlock * kCsStride<D>];
     __shared__ double invf_lds[D / 2];
     __shared__ int klab_lds[2 * kMaxBlock + 1];
 

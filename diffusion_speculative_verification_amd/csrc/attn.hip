@@ -508,9 +508,13 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     }
 }
 
-// Prologue: start the first two tiles' direct loads, build the RoPE table
-// and the key-label table, rotate this lane's query rows.  LDS regions are
-// __restrict__ parameters (see tile_step).
+// Prologue: start the first tile's direct loads, build the RoPE table while
+// they and the query loads are in flight, then the key-label table (which
+// needs tau), rotate this lane's query rows, and only then start the second
+// tile.  The compiler cannot see the direct loads, so its wait for the query
+// registers is a full vmcnt(0): issuing the second tile after that wait
+// keeps it out of the chip-wide burst that every workgroup waits on before
+// its first tile.  LDS regions are __restrict__ parameters (see tile_step).
 template <int D, int NW, int QB>
 __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v,
                                          uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
@@ -520,15 +524,9 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     constexpr int NS = D / 16, NTH = 64 * NW;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
-    // the first two tiles (every split has at least one; a second tile past
-    // the end reads clamped rows and is never consumed)
+    // the first tile (every split has at least one)
     load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
     load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
-    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
-    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
-    // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
-    const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
-    if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
     if (a.use_rope) {
         if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
@@ -538,6 +536,9 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
             cs[pr * kCsStride<D> + i] = rope_cs((double)P + (double)pr, invf[i]);
         }
     }
+    // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
+    const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
+    if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
     ring_barrier();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -550,6 +551,10 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
         for (int s = 0; s < NS; ++s)
             qop[qb][s] = __builtin_bit_cast(bf16x8, rvalid[qb] ? raw[qb][s] : make_uint4(0, 0, 0, 0));
     }
+    // the second tile (a tile past the end reads clamped rows and is never
+    // consumed)
+    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
+    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
 }
 
 // NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles

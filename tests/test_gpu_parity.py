@@ -102,6 +102,10 @@ SMALL = synth.Case("edge", 3, 100, 8, 8, 8, 2, 128, 1000, "bf16", 1e6, "perturb"
     dict(n_qh=16, n_kvh=2, block=64, gamma=64, prefix_len=200),  # two row blocks per kv head
     dict(vocab=1001),                          # vocab not a multiple of 4
     dict(vocab=1),                             # one token: always accepted
+    dict(vocab=2050),                          # one residual workgroup, second half of 2 entries
+    dict(vocab=6144),                          # last residual workgroup's second half past the end
+    dict(vocab=6151),                          # last residual workgroup's second half of 7 entries
+    dict(vocab=8191),                          # scalar loads over several residual workgroups
     dict(batch=1, prefix_len=5000, block=16, gamma=16),  # split prefix + combine
     dict(batch=1, prefix_len=20000, n_qh=8, n_kvh=1),    # one kv head: 105 prefix splits + combine
     dict(dtype="f32", head_dim=64, n_qh=4, n_kvh=2, prefix_len=70),

@@ -10,11 +10,13 @@
 // the n_qh/n_kvh query heads of a GQA group are rows of the same workgroup,
 // so they share every K/V tile; row blocks and prefix splits of one kv head
 // are placed on one XCD so that they meet its K/V in that XCD's L2).  One
-// workgroup per CU (about 129 KB of LDS), looping over 64-key tiles of
+// workgroup per CU (about 130 KB of LDS), looping over 64-key tiles of
 // [prompt | D | D~]:
 //   - a 3-stage LDS ring of (K, V) tiles, filled by direct global->LDS loads
-//     (global_load_lds_dwordx4) two tiles ahead of the math; both tiles are
-//     row-major with XOR-swizzled 16-byte chunks;
+//     (global_load_lds_dwordx4) two tiles ahead of the math; a prompt tile's
+//     loads use a scalar tile base plus a loop-invariant lane offset and go
+//     out between the S MFMAs; both tiles are row-major with 16-byte chunks
+//     XOR-swizzled for the 64-bank LDS;
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on MFMA rows, queries
 //     on columns): each lane then owns one query's scores, so the row
 //     max/sum need one cross-lane exchange (lane ^ 32) per tile;
@@ -26,7 +28,8 @@
 //     the transposing LDS read ds_read_b64_tr_b16; O is rescaled only when
 //     the running max moves by more than 8 (log2 units);
 //   - RoPE of Q is applied on load and that of the response keys in place in
-//     the K tile, from a cos/sin table built in LDS (angles formed in float64).
+//     the K tile, from a cos/sin table built in LDS (angles formed and
+//     reduced in float64, hardware sine/cosine on the reduced revolutions).
 // Long prefixes with few (sequence, kv head) units are split over
 // workgroups (flash-decoding style) and merged by attn_combine_kernel.
 //

@@ -79,6 +79,9 @@ class Oracle:
         lib.svo_residual.argtypes = [P, P, i64, dbl, P, P, P]
         lib.svo_residual.restype = i64
         lib.svo_accept.argtypes = [P, P, P, P, P, i32, i32, i32, i64, P, P, P, P]
+        lib.svo_coupled_choice.argtypes = [P, P, i64, ctypes.c_float]
+        lib.svo_coupled_choice.restype = i64
+        lib.svo_accept_coupled.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P]
         lib.svo_set_threads.argtypes = [i32]
         self.lib = lib
 
@@ -168,6 +171,35 @@ class Oracle:
         return L, ot, al, rs
 
 
+    def coupled_choice(self, l, g, temperature: float) -> int:
+        """Target choice of one slot under shared-noise verification ("SPOT"):
+        argmax_v fmaf(l[v], 1/T, g[v]) in float32 (T > 0), argmax_v l[v] (T = 0)."""
+        l = _c(l, np.float32)
+        inv_t = np.float32(1.0) / np.float32(temperature) if temperature > 0 else np.float32(0.0)
+        gp = None if temperature == 0 else _c(g, np.float32)
+        if gp is not None:
+            assert gp.shape == l.shape
+        return int(self.lib.svo_coupled_choice(_p(l), _p(gp), l.shape[0], float(inv_t)))
+
+    def accept_coupled(self, logits, gumbel, tokens, tau, gamma: int, temperature: float):
+        """Shared-noise (T > 0) or greedy (T = 0) verification of a batch ("SPOT").
+
+        logits/gumbel [n][B][V] (gumbel may be None when T = 0), tokens/tau [n][B].
+        Returns (accept_len[n], out_tokens[n][B], target_tokens[n][B]).
+        """
+        logits, tokens, tau = _c(logits, np.float32), _c(tokens, np.int32), _c(tau, np.int32)
+        n, B, V = logits.shape
+        g = None if gumbel is None else _c(gumbel, np.float32)
+        if g is not None:
+            assert g.shape == (n, B, V)
+        L = np.empty(n, np.int32)
+        ot = np.empty((n, B), np.int32)
+        tt = np.empty((n, B), np.int32)
+        _check(self.lib.svo_accept_coupled(_p(logits), _p(g), _p(tokens), _p(tau), n, B, gamma, V,
+                                           float(np.float32(temperature)), _p(L), _p(ot), _p(tt)))
+        return L, ot, tt
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -184,3 +216,5 @@ def attention(*a, **k): return default().attention(*a, **k)
 def softmax(l): return default().softmax(l)
 def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)
+def coupled_choice(l, g, temperature): return default().coupled_choice(l, g, temperature)
+def accept_coupled(*a, **k): return default().accept_coupled(*a, **k)

@@ -21,6 +21,14 @@
  *     distribution (P_ver - P_draft)^+).
  *   - The Portuguese SimSD summary (gist.science), sections 1-4, which
  *     restate the layout, mask and RoPE rule.
+ *   - "SPOT: Enhancing Speculative Decoding for Diffusion Language Models
+ *     via Commit-Order Prediction": 前置知识 "Gumbel-Max 技巧与随机耦合"
+ *     (argmax of log-probability plus Gumbel noise samples the distribution;
+ *     a noise table shared by draft and target couples the two samples) and
+ *     核心创新 / 方法步骤详情 (noise indexed by absolute output position; given
+ *     the noise the target transition is deterministic; an edge is accepted
+ *     when the draft state equals the target's; otherwise the target's own
+ *     result is committed; T = 0 is the greedy transition).
  * Readings where the pages are silent (each is listed in the design doc):
  *   prompt carries step label 0 and counts as data; D~_k shares tau(k) with
  *   D_k; positions are 0..P-1 for the prompt and P+k for both D_k and D~_k;
@@ -330,6 +338,88 @@ int svo_accept(const float *logits, const float *probs, const int32_t *tokens,
             ob[rs] = (int32_t)svo_residual(lk, pk, V, (double)ub[gamma], NULL, NULL, NULL);
         }
         if (resample_slot) resample_slot[b] = rs;
+        if (o != order) free(o);
+    }
+    return err;
+}
+
+/*
+ * Target choice of one slot under shared-noise verification ("SPOT", 前置知识
+ * "Gumbel-Max 技巧与随机耦合"; 方法步骤详情: given the noise table the target
+ * transition is a deterministic function).  At temperature T > 0 the choice
+ * is argmax_v (l[v] / T + g[v]) with g the slot's row of the noise table;
+ * T = 0 is the greedy choice argmax_v l[v].  This argmax decides an integer,
+ * so it is taken in the kernel's precision: the score is one float32 fused
+ * multiply-add fmaf(l[v], inv_t, g[v]) with inv_t = 1.0f / T rounded to
+ * float32, and equal scores go to the smallest v.  inv_t <= 0 selects the
+ * greedy choice (g is not read and may be NULL).
+ */
+int64_t svo_coupled_choice(const float *l, const float *g, int64_t V, float inv_t) {
+    int64_t best = 0;
+    float bs = (inv_t > 0.f) ? fmaf(l[0], inv_t, g[0]) : l[0];
+    for (int64_t v = 1; v < V; ++v) {
+        const float sc = (inv_t > 0.f) ? fmaf(l[v], inv_t, g[v]) : l[v];
+        if (sc > bs) { bs = sc; best = v; }
+    }
+    return best;
+}
+
+/*
+ * Shared-noise verification of a batch ("SPOT", 核心创新 "耦合噪声验证" and
+ * 方法步骤详情 验证; the draft order and slot layout of "SimSD", 关键设计 1 and
+ * 4).  Draft step r = 1..gamma verifies the slot o_r with tau(o_r) = r: it is
+ * accepted iff the draft token equals the target's own choice at that slot
+ * (the states after the step are equal; the commit position is fixed by
+ * tau).  L = number of leading accepted steps; at the first rejection the
+ * target's own choice is committed.
+ *   logits [batch][B][V], gumbel [batch][B][V] (the noise-table row of each
+ *   slot's absolute position; may be NULL when temperature == 0), tokens and
+ *   tau [batch][B].  temperature > 0: coupled sampling; == 0: greedy.
+ * Outputs: accept_len[batch]; out_tokens[batch][B] = draft token where
+ *   tau <= L, the target's choice where tau == L+1 (only if L < gamma), -1
+ *   elsewhere; target_tokens[batch][B] (may be NULL) = the target's choice at
+ *   every verified slot (tau <= gamma), -1 elsewhere.
+ * Returns 0, or a negative code for the first bad sequence.
+ */
+int svo_accept_coupled(const float *logits, const float *gumbel, const int32_t *tokens,
+                       const int32_t *tau, int batch, int B, int gamma, int64_t V, float temperature,
+                       int32_t *accept_len, int32_t *out_tokens, int32_t *target_tokens) {
+    if (batch < 0 || B < 1 || gamma < 1 || gamma > B || V < 1 || !(temperature >= 0.f)) return SVO_BAD_ARG;
+    if (temperature > 0.f && !gumbel) return SVO_BAD_ARG;
+    const float inv_t = (temperature > 0.f) ? 1.0f / temperature : 0.f;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *tb = tau + (size_t)b * B;
+        const int32_t *xb = tokens + (size_t)b * B;
+        int32_t *ob = out_tokens + (size_t)b * B;
+        if (!tau_is_permutation(tb, B)) {
+#pragma omp critical
+            err = SVO_BAD_TAU;
+            continue;
+        }
+        int order[64 + 1];
+        int *o = (B <= 64) ? order : (int *)malloc(sizeof(int) * ((size_t)B + 1));
+        for (int k = 0; k < B; ++k) o[tb[k]] = k;   /* o[r] = slot decoded at step r */
+        int64_t choice[64];
+        int64_t *c = (B <= 64) ? choice : (int64_t *)malloc(sizeof(int64_t) * (size_t)B);
+        for (int k = 0; k < B; ++k) {
+            c[k] = -1;
+            if (tb[k] > gamma) continue;   /* not verified in this call */
+            const size_t row = (size_t)b * B + k;
+            c[k] = svo_coupled_choice(logits + row * V, gumbel ? gumbel + row * V : NULL, V, inv_t);
+        }
+        int L = gamma;
+        for (int r = 1; r <= gamma; ++r) {
+            const int k = o[r];
+            if ((int64_t)xb[k] != c[k]) { L = r - 1; break; }
+        }
+        accept_len[b] = L;
+        for (int k = 0; k < B; ++k) ob[k] = (tb[k] <= L) ? xb[k] : -1;
+        if (L < gamma) ob[o[L + 1]] = (int32_t)c[o[L + 1]];
+        if (target_tokens)
+            for (int k = 0; k < B; ++k) target_tokens[(size_t)b * B + k] = (int32_t)c[k];
+        if (c != choice) free(c);
         if (o != order) free(o);
     }
     return err;

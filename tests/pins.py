@@ -511,8 +511,134 @@ def all_accept_pins(o, exact=True):
         pin_accept_exact_distribution(o, N=1000)
 
 
+# ----------------------------------------------- shared-noise verification
+def gumbel(r, shape):
+    """Standard Gumbel noise, -log(-log U), U uniform on (0, 1)."""
+    u = r.random(shape)
+    u = np.where(u <= 0.0, np.finfo(np.float64).tiny, u)
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
+def pin_coupled_greedy(o):
+    """T = 0 is the greedy transition: the choice is the first maximal logit
+    (numpy's argmax returns the first occurrence), ties included."""
+    r = rng(40)
+    for V in (1, 7, 1000):
+        for _ in range(5):
+            l = r.standard_normal(V).astype(np.float32)
+            assert o.coupled_choice(l, None, 0.0) == int(np.argmax(l))
+    l = np.array([0.5, 2.0, -1.0, 2.0, 2.0], np.float32)
+    assert o.coupled_choice(l, None, 0.0) == 1
+
+
+def pin_coupled_gumbel_max_law(o, N=30000):
+    """Gumbel-max: argmax_v (l_v / T + G_v) with iid standard Gumbel G is a
+    sample of softmax(l / T).  Two temperatures, so that T and 1/T, the sign
+    of the noise and argmax vs argmin are all distinguished."""
+    r = rng(41)
+    l = np.array([0.3, -1.2, 1.1, 0.0, 0.6], np.float32)
+    for T in (0.5, 2.0):
+        counts = np.zeros(l.shape[0])
+        for g in gumbel(r, (N, l.shape[0])):
+            counts[o.coupled_choice(l, g, T)] += 1
+        z = l.astype(np.float64) / np.float64(np.float32(T))
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        sd = np.sqrt(p * (1 - p) / N)
+        assert (np.abs(counts / N - p) < 4.5 * sd + 1e-12).all(), (T, counts / N, p)
+
+
+def pin_coupled_coupling_bounds(o, N=30000):
+    """Shared noise couples two Gumbel-max samples: with delta = D_TV(p, q),
+    P[choice under p == choice under q] is at least (1 - delta)/(1 + delta)
+    (the bound the SPOT page quotes) and at most 1 - delta (no coupling does
+    better)."""
+    r = rng(42)
+    V = 8
+    for scale in (0.3, 1.0):
+        lp = r.standard_normal(V).astype(np.float32)
+        lq = (lp + scale * r.standard_normal(V)).astype(np.float32)
+        p, _, _ = o.softmax(lp)
+        q, _, _ = o.softmax(lq)
+        delta = 0.5 * np.abs(p - q).sum()
+        agree = 0
+        for g in gumbel(r, (N, V)):
+            agree += o.coupled_choice(lp, g, 1.0) == o.coupled_choice(lq, g, 1.0)
+        rate = agree / N
+        sd = np.sqrt(0.25 / N)
+        assert rate >= (1 - delta) / (1 + delta) - 4.5 * sd, (rate, delta)
+        assert rate <= 1 - delta + 4.5 * sd, (rate, delta)
+
+
+def pin_coupled_accept_closed_form(o):
+    """Draft tokens built to match the target's choice for exactly k leading
+    steps (draft order given by tau): L = k, the draft tokens are kept for
+    steps 1..k, the target's own choice is committed at step k+1, later steps
+    and steps past gamma stay -1; matching every step accepts all gamma with
+    no extra token."""
+    r = rng(43)
+    B, V = 6, 40
+    for T in (0.0, 0.7):
+        for gamma in (B, 4):
+            for k in range(gamma + 1):
+                logits = (r.standard_normal((1, B, V)) * 2).astype(np.float32)
+                noise = gumbel(r, (1, B, V))
+                tau = random_tau(B, 500 + 7 * k + gamma)[None]
+                choice = np.array([o.coupled_choice(logits[0, j], noise[0, j], T) for j in range(B)])
+                toks = choice.copy()
+                step_slot = {int(tau[0, j]): j for j in range(B)}
+                if k < gamma:
+                    j = step_slot[k + 1]
+                    toks[j] = (choice[j] + 1) % V   # the first mismatch
+                for s in range(k + 2, B + 1):      # later steps: anything
+                    toks[step_slot[s]] = int(r.integers(V))
+                L, ot, tt = o.accept_coupled(logits, noise, toks[None].astype(np.int32), tau, gamma, T)
+                assert int(L[0]) == k, (T, gamma, k, int(L[0]))
+                for j in range(B):
+                    t = int(tau[0, j])
+                    assert tt[0, j] == (choice[j] if t <= gamma else -1)
+                    if t <= k:
+                        assert ot[0, j] == toks[j]
+                    elif t == k + 1 and k < gamma:
+                        assert ot[0, j] == choice[j] and ot[0, j] != toks[j]
+                    else:
+                        assert ot[0, j] == -1
+
+
+def pin_coupled_preserves_target_law(o, N=20000):
+    """The committed token at a verified slot follows the target's sampling
+    law softmax(l / T) whatever the draft proposes (the step either accepts a
+    draft equal to the target's choice or commits that choice): here the
+    draft is a shared-noise sample of a different distribution."""
+    r = rng(44)
+    V, T = 6, 1.5
+    lt = np.array([0.2, 1.4, -0.7, 0.9, 0.0, -1.5], np.float32)
+    ld = np.array([1.6, -0.3, 0.4, -1.0, 0.8, 0.1], np.float32)
+    noise = gumbel(r, (N, 1, V))
+    inv_t = np.float32(1.0) / np.float32(T)
+    draft = np.argmax(ld[None, None, :] * inv_t + noise, axis=2).astype(np.int32)
+    L, ot, tt = o.accept_coupled(np.broadcast_to(lt, (N, 1, V)), noise, draft,
+                                 np.ones((N, 1), np.int32), 1, T)
+    counts = np.bincount(ot[:, 0], minlength=V)
+    z = lt.astype(np.float64) / np.float64(np.float32(T))
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    sd = np.sqrt(p * (1 - p) / N)
+    assert (np.abs(counts / N - p) < 4.5 * sd).all(), (counts / N, p)
+    assert 0 < L.mean() < 1  # both outcomes occur
+
+
+def all_coupled_pins(o):
+    pin_coupled_greedy(o)
+    pin_coupled_gumbel_max_law(o)
+    pin_coupled_coupling_bounds(o)
+    pin_coupled_accept_closed_form(o)
+    pin_coupled_preserves_target_law(o)
+
+
 def all_pins(o):
     all_mask_pins(o)
     all_rope_pins(o)
     all_attention_pins(o)
     all_accept_pins(o)
+    all_coupled_pins(o)

@@ -35,6 +35,12 @@ MUTANTS = [
     ("resample mass operands swapped", "double mass = use_t ? pt : pt - (double)pphi[v];", "double mass = use_t ? pt : (double)pphi[v] - pt;"),
     ("resample at wrong slot", "rs = o[L + 1];", "rs = o[L > 0 ? L : 1];"),
     ("resample uses step uniform", "(double)ub[gamma], NULL", "(double)ub[0], NULL"),
+    ("coupled noise subtracted", "? fmaf(l[v], inv_t, g[v]) : l[v];", "? fmaf(l[v], inv_t, -g[v]) : l[v];"),
+    ("coupled ties to the largest index", "if (sc > bs) { bs = sc; best = v; }", "if (sc >= bs) { bs = sc; best = v; }"),
+    ("coupled temperature multiplies", "? 1.0f / temperature : 0.f;", "? temperature : 0.f;"),
+    ("coupled prefix off by one", "if ((int64_t)xb[k] != c[k]) { L = r - 1; break; }", "if ((int64_t)xb[k] != c[k]) { L = r; break; }"),
+    ("coupled rejection commits the draft", "ob[o[L + 1]] = (int32_t)c[o[L + 1]];", "ob[o[L + 1]] = xb[o[L + 1]];"),
+    ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 
 

@@ -97,3 +97,23 @@ def test_accept_monte_carlo(o):
     sel = L >= 1
     cnt2 = np.bincount(ot[sel, 0], minlength=V)
     assert chisquare(cnt2, pt[0] * sel.sum()).pvalue > 1e-4
+
+
+def test_coupled_greedy(o):
+    pins.pin_coupled_greedy(o)
+
+
+def test_coupled_gumbel_max_law(o):
+    pins.pin_coupled_gumbel_max_law(o)
+
+
+def test_coupled_coupling_bounds(o):
+    pins.pin_coupled_coupling_bounds(o)
+
+
+def test_coupled_accept_closed_form(o):
+    pins.pin_coupled_accept_closed_form(o)
+
+
+def test_coupled_preserves_target_law(o):
+    pins.pin_coupled_preserves_target_law(o)

@@ -28,9 +28,10 @@ MUTANTS = [
     ("unnormalised weights", "const double w = sc[j] / den;", "const double w = sc[j];"),
     ("ratio inverted", "double a = (pd > 0.0) ? pt / pd : 1.0;", "double a = (pd > 0.0) ? pd / pt : 1.0;"),
     ("target prob unnormalised", "const double pt = exp((double)lk[x] - m) / s;", "const double pt = exp((double)lk[x] - m);"),
-    ("slot order instead of draft order", "const int k = o[r];", "const int k = r - 1;"),
-    ("prefix off by one", "L = r - 1;", "L = r;"),
-    ("assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;", "ob[k] = (tb[k] < L) ? xb[k] : -1;"),
+    ("slot order instead of draft order", "const int k = o[r];\n            const float *lk", "const int k = r - 1;\n            const float *lk"),
+    ("prefix off by one", "< a)) L = r - 1;", "< a)) L = r;"),
+    ("assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;\n        int rs = -1;",
+     "ob[k] = (tb[k] < L) ? xb[k] : -1;\n        int rs = -1;"),
     ("residual operands swapped", "const double r = pt - (double)pphi[v];", "const double r = (double)pphi[v] - pt;"),
     ("resample mass operands swapped", "double mass = use_t ? pt : pt - (double)pphi[v];", "double mass = use_t ? pt : (double)pphi[v] - pt;"),
     ("resample at wrong slot", "rs = o[L + 1];", "rs = o[L > 0 ? L : 1];"),
@@ -40,6 +41,8 @@ MUTANTS = [
     ("coupled temperature multiplies", "? 1.0f / temperature : 0.f;", "? temperature : 0.f;"),
     ("coupled prefix off by one", "if ((int64_t)xb[k] != c[k]) { L = r - 1; break; }", "if ((int64_t)xb[k] != c[k]) { L = r; break; }"),
     ("coupled rejection commits the draft", "ob[o[L + 1]] = (int32_t)c[o[L + 1]];", "ob[o[L + 1]] = xb[o[L + 1]];"),
+    ("coupled assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;\n        if (L < gamma)",
+     "ob[k] = (tb[k] < L) ? xb[k] : -1;\n        if (L < gamma)"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

@@ -53,6 +53,10 @@ def load(path: str | None = None):
     lib.spec_verify_accept_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept.restype = I
     lib.spec_verify_accept.argtypes = [V, V, V, V, V, I, I, I, I64, V, V, V, V, SZ, V]
+    lib.spec_verify_accept_coupled_workspace_size.restype = SZ
+    lib.spec_verify_accept_coupled_workspace_size.argtypes = [I, I, I, I64]
+    lib.spec_verify_accept_coupled.restype = I
+    lib.spec_verify_accept_coupled.argtypes = [V, V, V, V, I, I, I, I64, F, V, V, V, V, SZ, V]
     if path is None:
         _lib = lib
     return lib
@@ -115,3 +119,16 @@ def spec_verify_accept(target_logits, draft_probs, draft_tokens, tau, uniforms, 
                                      _ptr(uniforms), batch, block, gamma, vocab, _ptr(accept_len),
                                      _ptr(out_tokens), _ptr(alpha), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream)))
+
+
+def spec_verify_accept_coupled_workspace_size(batch, block, gamma, vocab) -> int:
+    return int(load().spec_verify_accept_coupled_workspace_size(batch, block, gamma, vocab))
+
+
+def spec_verify_accept_coupled(target_logits, gumbel, draft_tokens, tau, batch, block, gamma, vocab, temperature,
+                               accept_len, out_tokens, target_tokens, workspace, workspace_bytes,
+                               stream=None) -> None:
+    _check(load().spec_verify_accept_coupled(_ptr(target_logits), _ptr(gumbel), _ptr(draft_tokens), _ptr(tau),
+                                             batch, block, gamma, vocab, float(temperature), _ptr(accept_len),
+                                             _ptr(out_tokens), _ptr(target_tokens), _ptr(workspace),
+                                             int(workspace_bytes), _stream(stream)))

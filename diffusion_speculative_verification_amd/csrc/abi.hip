@@ -113,4 +113,38 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs, con
                                         (hipStream_t)stream));
 }
 
+size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab > (1ll << 21))
+        return 0;
+    return sv::coupled_plan(batch, block, gamma, vocab).ws_total;
+}
+
+int spec_verify_accept_coupled(const float *target_logits, const float *gumbel, const int32_t *draft_tokens,
+                               const int32_t *tau, int batch, int block, int gamma, int64_t vocab,
+                               float temperature, int32_t *accept_len, int32_t *out_tokens,
+                               int32_t *target_tokens, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab > (1ll << 21))
+        return SV_E_SHAPE;
+    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!(temperature >= 0.f) || !isfinite(temperature)) return SV_E_SHAPE;
+    if (!target_logits || !draft_tokens || !tau || !accept_len || !out_tokens) return SV_E_NULL;
+    if (temperature > 0.f && !gumbel) return SV_E_NULL;
+    if (!aligned16(target_logits) || (gumbel && !aligned16(gumbel)) || !aligned16(draft_tokens) ||
+        !aligned16(tau) || !aligned16(accept_len) || !aligned16(out_tokens) ||
+        (target_tokens && !aligned16(target_tokens)))
+        return SV_E_ALIGN;
+    const sv::CoupledPlan p = sv::coupled_plan(batch, block, gamma, vocab);
+    if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
+    if (!aligned16(workspace)) return SV_E_ALIGN;
+    // 1/T rounded to float32 once, here: the kernels and the definition use
+    // the same reciprocal
+    const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.f;
+    if (temperature > 0.f && !isfinite(inv_t)) return SV_E_SHAPE;
+    return map_launch(sv::launch_coupled(p, target_logits, temperature > 0.f ? gumbel : nullptr, draft_tokens,
+                                         tau, batch, block, gamma, vocab, inv_t, accept_len, out_tokens,
+                                         target_tokens, workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -58,4 +58,17 @@ hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *
                          int block, int gamma, int64_t vocab, int32_t *accept_len,
                          int32_t *out_tokens, float *alpha, void *ws, hipStream_t st);
 
+struct CoupledPlan {
+    int rows;        // batch * block logits rows
+    int n_vsplit;    // vocab splits of the streaming argmax
+    size_t ws_total;
+};
+
+CoupledPlan coupled_plan(int batch, int block, int gamma, int64_t vocab);
+
+hipError_t launch_coupled(const CoupledPlan &p, const float *logits, const float *noise, const int32_t *tokens,
+                          const int32_t *tau, int batch, int block, int gamma, int64_t vocab, float inv_t,
+                          int32_t *accept_len, int32_t *out_tokens, int32_t *target_tokens, void *ws,
+                          hipStream_t st);
+
 }  // namespace sv

@@ -55,6 +55,17 @@ class StepBuffers:
             n = sv.spec_verify_accept_workspace_size(c.batch, c.block, c.gamma, c.vocab)
             self.acc_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.acc_ws_bytes = n
+        if "coupled" in parts:
+            if not hasattr(self, "target_logits"):
+                self.target_logits = up(inputs["target_logits"])
+            self.gumbel = up(inputs["gumbel"])
+            self.coupled_tokens = up(inputs["coupled_tokens"])
+            self.cpl_accept_len = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.cpl_out_tokens = torch.empty((c.batch, c.block), dtype=torch.int32, device=device)
+            self.cpl_target_tokens = torch.empty((c.batch, c.block), dtype=torch.int32, device=device)
+            n = sv.spec_verify_accept_coupled_workspace_size(c.batch, c.block, c.gamma, c.vocab)
+            self.cpl_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.cpl_ws_bytes = n
 
     def attn(self, rope_theta=None, stream=None, q=None, k_new=None):
         c = self.case
@@ -69,6 +80,15 @@ class StepBuffers:
         sv.spec_verify_accept(self.target_logits, self.draft_probs, self.draft_tokens, self.tau, self.uniforms,
                               c.batch, c.block, c.gamma, c.vocab, self.accept_len, self.out_tokens, self.alpha,
                               self.acc_ws, self.acc_ws_bytes, stream)
+
+    def accept_coupled(self, stream=None, temperature=None):
+        """Shared-noise (T > 0) or greedy (T = 0) verification of the batch."""
+        c = self.case
+        T = c.temperature if temperature is None else temperature
+        sv.spec_verify_accept_coupled(self.target_logits, self.gumbel if T > 0 else None, self.coupled_tokens,
+                                      self.tau, c.batch, c.block, c.gamma, c.vocab, T, self.cpl_accept_len,
+                                      self.cpl_out_tokens, self.cpl_target_tokens, self.cpl_ws, self.cpl_ws_bytes,
+                                      stream)
 
     def step(self, stream=None):
         """One verification step: attention with fused copy-aligned RoPE,

@@ -26,6 +26,9 @@ numpy default_rng(SeedSequence([s, t, b]))):
       perturb model: target + N(0, 1)
   t=8 draft sampling uniforms [B]
   t=9 acceptance/resample uniforms [gamma+1]  U[0,1) fp32
+  t=10 shared-noise rows [B][V]: standard Gumbel -log(-log U), U uniform on
+      (0,1), fp32 -- the rows of the noise table at the slots' absolute
+      positions ("SPOT", 前置知识 "Gumbel-Max 技巧与随机耦合")
 bf16 cases round Q/K/V and the caches to bf16 (round-to-nearest-even) and keep
 them as float32 arrays holding exactly bf16-representable values.
 
@@ -33,6 +36,10 @@ The synthetic drafter: p_phi = softmax(draft logits) computed in float64 and
 stored as float32; each draft token is drawn from the float64 p_phi by
 inverse CDF with its own uniform.  This is input synthesis (the drafter is not
 part of the verification step).
+
+For shared-noise verification the synthetic drafter samples with the same
+noise rows: its token at slot k is argmax_v (draft logit / T + G[k][v])
+(float32, T = case.temperature), or argmax_v draft logit when T = 0.
 """
 from __future__ import annotations
 
@@ -63,6 +70,7 @@ class Case:
     draft_var: float = 1.0
     identity_every: int = 0
     seed: int = 0
+    temperature: float = 1.0  # shared-noise verification (0: greedy)
 
     @property
     def rows(self) -> int:
@@ -136,6 +144,23 @@ def _logits_and_draft(case: Case, b: int, want_logits: bool = True):
     return tgt32, probs32, tok
 
 
+def _coupled_noise_and_draft(case: Case, b: int):
+    """Shared-noise rows of the B slots and the shared-noise drafter's tokens."""
+    B, V = case.block, case.vocab
+    tgt = _rng(case, 6, b).standard_normal((B, V), dtype=np.float64) * np.sqrt(case.target_var)
+    noise = _rng(case, 7, b).standard_normal((B, V), dtype=np.float64)
+    drf = (tgt + noise * np.sqrt(case.draft_var)) if case.logit_model == "perturb" else noise * np.sqrt(case.draft_var)
+    u = _rng(case, 10, b).random((B, V))
+    np.maximum(u, np.finfo(np.float64).tiny, out=u)
+    g = (-np.log(-np.log(u))).astype(np.float32)
+    if case.temperature > 0:
+        inv_t = np.float32(1.0) / np.float32(case.temperature)
+        score = drf.astype(np.float32) * inv_t + g
+    else:
+        score = drf
+    return g, np.argmax(score, axis=1).astype(np.int32)
+
+
 def _uniforms(case: Case, b: int) -> np.ndarray:
     return _rng(case, 9, b).random(case.gamma + 1, dtype=np.float32)
 
@@ -146,7 +171,8 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
     Returns a dict of float32/int32 numpy arrays with a leading batch axis:
     q [n][2B][Hq][d], k_new/v_new [n][2B][Hkv][d], k_cache/v_cache
     [n][Hkv][P][d], tau [n][B], target_logits/draft_probs [n][B][V],
-    draft_tokens [n][B], uniforms [n][gamma+1].
+    draft_tokens [n][B], uniforms [n][gamma+1]; with "coupled" in parts also
+    target_logits, gumbel [n][B][V] and coupled_tokens [n][B].
     """
     seqs = list(range(case.batch)) if seqs is None else list(seqs)
     n = len(seqs)
@@ -188,4 +214,22 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
 
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill_acc, range(n)))
+    if "coupled" in parts:
+        V = case.vocab
+        need_logits = "target_logits" not in out
+        if need_logits:
+            out["target_logits"] = np.empty((n, B, V), np.float32)
+        out["gumbel"] = np.empty((n, B, V), np.float32)
+        out["coupled_tokens"] = np.empty((n, B), np.int32)
+
+        def fill_cpl(i):
+            b = seqs[i]
+            if need_logits:
+                out["target_logits"][i] = _logits_and_draft(case, b)[0]
+            g, k = _coupled_noise_and_draft(case, b)
+            out["gumbel"][i] = g
+            out["coupled_tokens"][i] = k
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill_cpl, range(n)))
     return out

@@ -139,6 +139,45 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs,
                        int32_t *out_tokens, float *alpha, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* Bytes of workspace spec_verify_accept_coupled needs for these sizes. */
+size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab);
+
+/*
+ * Shared-noise (temperature > 0) or greedy (temperature == 0) verification
+ * (page "SPOT: Enhancing Speculative Decoding for Diffusion Language Models
+ * via Commit-Order Prediction", 前置知识 "Gumbel-Max 技巧与随机耦合" and
+ * 核心创新 / 方法步骤详情: a Gumbel noise table indexed by absolute output
+ * position is shared by draft and target; given the noise the target's
+ * transition is deterministic, a step is accepted when the draft's state
+ * equals the target's, otherwise the target's own result is committed).
+ *   target_logits [batch][block][vocab] float32: target logits of each slot
+ *   gumbel        [batch][block][vocab] float32: each slot's row of the
+ *                 shared noise table (standard Gumbel noise at the slot's
+ *                 absolute output position -- the noise the drafter sampled
+ *                 with); not read, and may be NULL, when temperature == 0
+ *   draft_tokens, tau [batch][block] int32 (tau: step labels 1..block)
+ *   temperature   >= 0 and finite
+ * The target's choice at a verified slot (tau <= gamma) is
+ * argmax_v fmaf(l[v], 1/T, g[v]), computed in float32 with 1/T rounded to
+ * float32 (T > 0), or argmax_v l[v] (T == 0); equal scores go to the smallest
+ * v.  Draft step r = 1..gamma (the slot with tau = r) is accepted iff its
+ * draft token equals that choice; L = number of leading accepted steps.
+ * Outputs:
+ *   accept_len [batch]: L (0..gamma)
+ *   out_tokens [batch][block]: the draft token where tau <= L, the target's
+ *     choice where tau == L+1 (only when L < gamma), -1 elsewhere
+ *   target_tokens [batch][block] (may be NULL): the target's choice where
+ *     tau <= gamma, -1 elsewhere
+ * Logits and noise are finite (a precondition).  Limits as for
+ * spec_verify_accept; SV_E_SHAPE for a negative or non-finite temperature,
+ * SV_E_NULL for a NULL gumbel at temperature > 0.
+ */
+int spec_verify_accept_coupled(const float *target_logits, const float *gumbel,
+                               const int32_t *draft_tokens, const int32_t *tau, int batch, int block,
+                               int gamma, int64_t vocab, float temperature, int32_t *accept_len,
+                               int32_t *out_tokens, int32_t *target_tokens, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
 
@@ -95,6 +95,31 @@ def test_accept_argument_checks(lib):
     assert accept(lib, u=A + 4) == sv.SV_E_ALIGN
     assert accept(lib, ws=None) == sv.SV_E_WORKSPACE
     assert accept(lib, ws_bytes=8) == sv.SV_E_WORKSPACE
+
+
+def coupled(lib, **kw):
+    args = dict(tl=A, g=A, dt=A, tau=A, batch=2, block=8, gamma=8, vocab=512, T=1.0, L=A, ot=A, tt=A, ws=A,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.spec_verify_accept_coupled(args["tl"], args["g"], args["dt"], args["tau"], args["batch"],
+                                          args["block"], args["gamma"], args["vocab"], args["T"], args["L"],
+                                          args["ot"], args["tt"], args["ws"], args["ws_bytes"], None)
+
+
+def test_coupled_argument_checks(lib):
+    assert sv.spec_verify_accept_coupled_workspace_size(32, 32, 32, 151936) > 0
+    assert sv.spec_verify_accept_coupled_workspace_size(32, 32, 33, 151936) == 0
+    assert coupled(lib, tl=None) == sv.SV_E_NULL
+    assert coupled(lib, g=None) == sv.SV_E_NULL            # noise needed at T > 0
+    assert coupled(lib, g=None, T=0.0, ws=None) == sv.SV_E_WORKSPACE  # greedy: noise not needed
+    assert coupled(lib, T=-1.0) == sv.SV_E_SHAPE
+    assert coupled(lib, T=float("inf")) == sv.SV_E_SHAPE
+    assert coupled(lib, T=float("nan")) == sv.SV_E_SHAPE
+    assert coupled(lib, T=1e-45) == sv.SV_E_SHAPE          # 1/T overflows float32
+    assert coupled(lib, gamma=9) == sv.SV_E_SHAPE
+    assert coupled(lib, g=A + 4) == sv.SV_E_ALIGN
+    assert coupled(lib, tt=A + 4) == sv.SV_E_ALIGN
+    assert coupled(lib, ws_bytes=4) == sv.SV_E_WORKSPACE
 
 
 def test_rope_argument_checks(lib):

@@ -17,6 +17,10 @@ last-level cache.
 Prints ONE JSON line (rank 0, N = 1).  Also reports the roofline of the
 dominant call (timed live with HIP events on the launch stream) and the CPU
 oracle timed on this host over the same workload.
+
+--verify coupled | greedy replaces the epilogue by shared-noise verification
+(spec_verify_accept_coupled at --temperature, default 1) or its greedy form
+(T = 0); the default, rejection, is the headline step.
 """
 from __future__ import annotations
 
@@ -62,6 +66,16 @@ def accept_bytes(c, n_rejecting: int) -> float:
     return 4.0 * c.batch * c.gamma * V + n_rejecting * 2 * 4.0 * V + small
 
 
+def coupled_bytes(c, greedy: bool) -> float:
+    """Algorithmic HBM bytes of one shared-noise verification call: the
+    float32 target logits of every verified slot once, the float32 noise row
+    of every verified slot once (not read when greedy), plus tau, draft
+    tokens and the outputs."""
+    rows = 4.0 * c.batch * c.gamma * c.vocab
+    small = c.batch * (c.block * 4 * 4 + 4)
+    return rows * (1 if greedy else 2) + small
+
+
 def measured_traffic(call: str):
     """HBM bytes per launch of `call` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration),
@@ -81,7 +95,7 @@ def measured_traffic(call: str):
     return None
 
 
-def cpu_baseline(case, inp) -> dict:
+def cpu_baseline(case, inp, verify="rejection", temperature=1.0) -> dict:
     """The CPU oracle on this host over the same workload (one step)."""
     import oracle
     o = oracle.Oracle()
@@ -92,8 +106,12 @@ def cpu_baseline(case, inp) -> dict:
                     inp["tau"][b], case.theta)
     t_attn = time.perf_counter() - t
     t = time.perf_counter()
-    o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"], inp["uniforms"],
-             case.gamma)
+    if verify == "rejection":
+        o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"], inp["uniforms"],
+                 case.gamma)
+    else:
+        o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None, inp["coupled_tokens"],
+                         inp["tau"], case.gamma, temperature)
     t_acc = time.perf_counter() - t
     total = t_attn + t_acc
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
@@ -109,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default="rejection",
+                    help="epilogue: rejection sampling (headline), shared-noise or greedy verification")
+    ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -132,12 +153,24 @@ def main():
     from diffusion_speculative_verification_amd.device import StepBuffers
 
     case = synth.config_by_name(args.config)
-    inp = synth.make_inputs(case)
-    sets = [StepBuffers(case, inp), StepBuffers(case, inp)]
+    verify = args.verify
+    T = 0.0 if verify == "greedy" else args.temperature
+    parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
+    if verify != "rejection":
+        case = case.with_(temperature=T)
+    inp = synth.make_inputs(case, parts=parts)
+    sets = [StepBuffers(case, inp, parts=parts), StepBuffers(case, inp, parts=parts)]
     stream = torch.cuda.current_stream()
 
+    def epilogue(s):
+        if verify == "rejection":
+            s.accept()
+        else:
+            s.accept_coupled(temperature=T)
+
     for i in range(args.warmup):
-        sets[i & 1].step()
+        sets[i & 1].attn()
+        epilogue(sets[i & 1])
     torch.cuda.synchronize()
 
     K = args.steps
@@ -149,7 +182,7 @@ def main():
         ev[i][0].record(stream)
         s.attn()
         ev[i][1].record(stream)
-        s.accept()
+        epilogue(s)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -158,13 +191,14 @@ def main():
     ms_step = total_ms / K
     attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
     acc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
-    L = sets[0].accept_len.cpu()
+    L = (sets[0].accept_len if verify == "rejection" else sets[0].cpl_accept_len).cpu()
     n_rej = int((L < case.gamma).sum())
     slots = case.batch * case.gamma
     value = slots / (ms_step * 1e-3)
 
     a_bytes, a_flops = attn_bytes(case), attn_flops(case)
-    c_bytes = accept_bytes(case, n_rej)
+    c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
+    acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
     rl_attn = {"bound": "hbm", "achieved": a_bytes / (attn_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "tflops": a_flops / (attn_ms * 1e-3) / 1e12, "bf16_peak_tflops": BF16_PEAK_TFLOPS,
                "ms": attn_ms, "bytes": a_bytes}
@@ -172,20 +206,21 @@ def main():
               "ms": acc_ms, "bytes": c_bytes}
     for r in (rl_attn, rl_acc):
         r["frac"] = r["achieved"] / r["peak"]
-    dom = ("spec_verify_accept", rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
+    dom = (acc_call, rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
     roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
         c_bytes / (HBM_PEAK_GBS * 1e9)
     # traffic only applies to the headline workload the counters were taken on
     headline = case.name == "headline"
     rl_attn["traffic"] = measured_traffic("spec_verify_attn") if headline else None
-    rl_acc["traffic"] = measured_traffic("spec_verify_accept") if headline else None
+    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "")) \
+        if headline else None
     roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
                 "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
                 "traffic_unit": "bytes/launch", "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp)
+        cpu = cpu_baseline(case, inp, verify, T)
 
     out = {
         "metric": METRIC,
@@ -202,7 +237,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{case.name} verify step: batch {case.batch}, prefix {case.prefix_len}, "
                                f"B=gamma={case.block}, {case.n_qh}/{case.n_kvh} heads, head_dim {case.head_dim}, "
-                               f"vocab {case.vocab}, {case.dtype} attention, fp32 logits",
+                               f"vocab {case.vocab}, {case.dtype} attention, fp32 logits" +
+                               ("" if verify == "rejection" else
+                                f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification"),
+                   "verify": verify, "temperature": None if verify == "rejection" else T,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
                    "parallelism": "single GPU"},

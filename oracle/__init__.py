@@ -82,6 +82,7 @@ class Oracle:
         lib.svo_coupled_choice.argtypes = [P, P, i64, ctypes.c_float]
         lib.svo_coupled_choice.restype = i64
         lib.svo_accept_coupled.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P]
+        lib.svo_route.argtypes = [P, P, i32, i32, i32, i64, i32, dbl, P, P]
         lib.svo_set_threads.argtypes = [i32]
         self.lib = lib
 
@@ -199,6 +200,18 @@ class Oracle:
                                            float(np.float32(temperature)), _p(L), _p(ot), _p(tt)))
         return L, ot, tt
 
+    def route(self, probs, tau, gamma: int, estimator: str, param: float):
+        """S2D2 verify-routing estimator of a batch: probs [n][B][V], tau [n][B];
+        estimator "margin" (param = threshold) or "entropy" (param = beta).
+        Returns (khat[n] float64, alpha_hat[n][gamma] float64, draft order)."""
+        probs, tau = _c(probs, np.float32), _c(tau, np.int32)
+        n, B, V = probs.shape
+        kh = np.empty(n, np.float64)
+        ah = np.empty((n, gamma), np.float64)
+        est = {"margin": 0, "entropy": 1}[estimator]
+        _check(self.lib.svo_route(_p(probs), _p(tau), n, B, gamma, V, est, float(param), _p(kh), _p(ah)))
+        return kh, ah
+
 
 def default() -> Oracle:
     global _default
@@ -218,3 +231,4 @@ def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)
 def coupled_choice(l, g, temperature): return default().coupled_choice(l, g, temperature)
 def accept_coupled(*a, **k): return default().accept_coupled(*a, **k)
+def route(*a, **k): return default().route(*a, **k)

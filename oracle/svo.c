@@ -29,6 +29,10 @@
  *     the noise the target transition is deterministic; an edge is accepted
  *     when the draft state equals the target's; otherwise the target's own
  *     result is committed; T = 0 is the greedy transition).
+ *   - "S2D2": 方法步骤详情 (4), the routing decision: the expected accepted
+ *     prefix length K = sum_k prod_{i<=k} alpha_i with a margin-based
+ *     (indicator of margin >= threshold) or entropy-based (exp(-beta H~))
+ *     estimate of each alpha_i.
  * Readings where the pages are silent (each is listed in the design doc):
  *   prompt carries step label 0 and counts as data; D~_k shares tau(k) with
  *   D_k; positions are 0..P-1 for the prompt and P+k for both D_k and D~_k;
@@ -420,6 +424,69 @@ int svo_accept_coupled(const float *logits, const float *gumbel, const int32_t *
         if (target_tokens)
             for (int k = 0; k < B; ++k) target_tokens[(size_t)b * B + k] = (int32_t)c[k];
         if (c != choice) free(c);
+        if (o != order) free(o);
+    }
+    return err;
+}
+
+/*
+ * Verify-routing estimator of one batch ("S2D2", 方法步骤详情 (4): the expected
+ * accepted prefix length K = sum_{k=1}^{L} prod_{i=1}^{k} alpha_i, with
+ * alpha_i estimated from the draft distribution either by its margin,
+ * 1[m_i >= tau_margin], or by its entropy, exp(-beta * H~_i)).
+ * Per slot, with p the slot's draft distribution (float64 arithmetic):
+ *   m  = p_(1) - p_(2), the two largest entries (m = p_(1) when V = 1);
+ *   H~ = -(sum_v p_v ln p_v) / ln V, terms with p_v = 0 vanish (H~ = 0 when
+ *        V = 1).
+ * The steps are taken in draft order r = 1..gamma (slot o_r with tau(o_r) =
+ * r), the positions the verification would check, so
+ *   khat = sum_{k=1}^{gamma} prod_{r=1}^{k} alpha_{o_r}.
+ * estimator 0: margin with param = tau_margin; 1: entropy with param = beta.
+ * Outputs khat[batch] and alpha_hat[batch][gamma] (draft order; may be NULL).
+ */
+int svo_route(const float *probs, const int32_t *tau, int batch, int B, int gamma, int64_t V,
+              int estimator, double param, double *khat, double *alpha_hat) {
+    if (batch < 0 || B < 1 || gamma < 1 || gamma > B || V < 1 || (estimator != 0 && estimator != 1))
+        return SVO_BAD_ARG;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *tb = tau + (size_t)b * B;
+        if (!tau_is_permutation(tb, B)) {
+#pragma omp critical
+            err = SVO_BAD_TAU;
+            continue;
+        }
+        int order[64 + 1];
+        int *o = (B <= 64) ? order : (int *)malloc(sizeof(int) * ((size_t)B + 1));
+        for (int k = 0; k < B; ++k) o[tb[k]] = k;   /* o[r] = slot decoded at step r */
+        double prod = 1.0, sum = 0.0;
+        for (int r = 1; r <= gamma; ++r) {
+            const float *p = probs + ((size_t)b * B + o[r]) * V;
+            double a;
+            if (estimator == 0) {
+                double p1 = -1.0, p2 = 0.0;
+                for (int64_t v = 0; v < V; ++v) {
+                    const double x = (double)p[v];
+                    if (x > p1) { p2 = p1; p1 = x; }
+                    else if (x > p2) p2 = x;
+                }
+                if (p2 < 0.0) p2 = 0.0;
+                a = (p1 - p2 >= param) ? 1.0 : 0.0;
+            } else {
+                double h = 0.0;
+                for (int64_t v = 0; v < V; ++v) {
+                    const double x = (double)p[v];
+                    if (x > 0.0) h -= x * log(x);
+                }
+                const double hn = (V > 1) ? h / log((double)V) : 0.0;
+                a = exp(-param * hn);
+            }
+            if (alpha_hat) alpha_hat[(size_t)b * gamma + (r - 1)] = a;
+            prod *= a;
+            sum += prod;
+        }
+        khat[b] = sum;
         if (o != order) free(o);
     }
     return err;

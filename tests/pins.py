@@ -636,9 +636,104 @@ def all_coupled_pins(o):
     pin_coupled_preserves_target_law(o)
 
 
+# ------------------------------------------------ verify-routing estimator
+def pin_route_closed_forms(o):
+    """Uniform rows have normalised entropy 1, so alpha = exp(-beta) and K is
+    the geometric sum; one-hot rows have margin 1 and entropy 0, so K = gamma
+    for both estimators; a two-point row has entropy -q ln q - (1-q) ln(1-q)."""
+    B, V, gamma = 5, 16, 5
+    tau = random_tau(B, 60)[None]
+    for beta in (0.3, 1.7):
+        kh, ah = o.route(np.full((1, B, V), 1.0 / V, np.float32), tau, gamma, "entropy", beta)
+        a = np.exp(-beta)
+        assert np.abs(ah - a).max() < 1e-12
+        assert abs(kh[0] - a * (1 - a ** gamma) / (1 - a)) < 1e-12
+    onehot = np.zeros((1, B, V), np.float32)
+    onehot[0, np.arange(B), (np.arange(B) * 3) % V] = 1.0
+    for est, prm in (("margin", 0.9), ("entropy", 5.0)):
+        kh, ah = o.route(onehot, tau, gamma, est, prm)
+        assert kh[0] == gamma and (ah == 1).all()
+    q = np.float32(0.3)
+    two = np.zeros((1, 1, V), np.float32)
+    two[0, 0, 3], two[0, 0, 9] = q, np.float32(1) - q
+    qd = float(q)
+    h = -(qd * np.log(qd) + (1 - qd) * np.log(1 - qd)) / np.log(V)
+    kh, ah = o.route(two, np.ones((1, 1), np.int32), 1, "entropy", 2.0)
+    assert abs(ah[0, 0] - np.exp(-2.0 * h)) < 1e-9
+
+
+def pin_route_margin_counts(o, seed=61):
+    """Margin estimator: alpha is 1 while the draft margin p_(1) - p_(2)
+    reaches the threshold, so K counts the leading steps in draft order that
+    do; rows are built with known margins and shuffled positions."""
+    r = rng(seed)
+    n, B, V, thr = 40, 7, 12, 0.25
+    probs = np.zeros((n, B, V), np.float32)
+    margins = r.choice([0.1, 0.2, 0.3, 0.6], size=(n, B))
+    for b in range(n):
+        for k in range(B):
+            top, rest = 0.5 + margins[b, k] / 2, 0.5 - margins[b, k] / 2
+            row = np.zeros(V)
+            idx = r.permutation(V)
+            row[idx[0]] = top
+            row[idx[1]] = rest * 0.99
+            row[idx[2]] = rest * 0.01
+            probs[b, k] = row
+    tau = np.stack([random_tau(B, 700 + b) for b in range(n)])
+    for gamma in (B, 4):
+        kh, ah = o.route(probs, tau, gamma, "margin", thr)
+        for b in range(n):
+            m = [float(probs[b, int(np.where(tau[b] == s)[0][0])].max()) -
+                 float(np.sort(probs[b, int(np.where(tau[b] == s)[0][0])])[-2]) for s in range(1, gamma + 1)]
+            lead = next((i for i, x in enumerate(m) if not x >= thr), gamma)
+            assert kh[b] == lead, (b, kh[b], lead, m)
+
+
+def pin_route_entropy_library(o, seed=62):
+    """The entropy estimator against scipy's entropy terms -x ln x (entr,
+    which also maps 0 to 0) of the same rows, without renormalising."""
+    from scipy.special import entr
+    r = rng(seed)
+    n, B, V, beta = 6, 4, 300, 0.8
+    probs = r.dirichlet(np.full(V, 0.3), (n, B)).astype(np.float32)
+    probs[0, 0, :10] = 0.0  # zero entries contribute nothing
+    tau = np.stack([random_tau(B, 800 + b) for b in range(n)])
+    kh, ah = o.route(probs, tau, B, "entropy", beta)
+    for b in range(n):
+        for s in range(B):
+            k = int(np.where(tau[b] == s + 1)[0][0])
+            ref = np.exp(-beta * entr(probs[b, k].astype(np.float64)).sum() / np.log(V))
+            assert abs(ah[b, s] - ref) < 1e-12, (b, s, ah[b, s], ref)
+
+
+def pin_route_expected_prefix(o, seed=63):
+    """K is the expected accepted prefix length when step r is accepted
+    independently with probability alpha_r: enumerate all 2^gamma outcomes."""
+    r = rng(seed)
+    B, V, gamma = 4, 20, 4
+    probs = r.dirichlet(np.full(V, 0.5), (1, B)).astype(np.float32)
+    tau = random_tau(B, 900)[None]
+    kh, ah = o.route(probs, tau, gamma, "entropy", 1.3)
+    a = ah[0]
+    e = 0.0
+    for bits in itertools.product((0, 1), repeat=gamma):
+        pr = np.prod([a[i] if bits[i] else 1 - a[i] for i in range(gamma)])
+        L = next((i for i, x in enumerate(bits) if not x), gamma)
+        e += pr * L
+    assert abs(kh[0] - e) < 1e-12, (kh[0], e)
+
+
+def all_route_pins(o):
+    pin_route_closed_forms(o)
+    pin_route_margin_counts(o)
+    pin_route_entropy_library(o)
+    pin_route_expected_prefix(o)
+
+
 def all_pins(o):
     all_mask_pins(o)
     all_rope_pins(o)
     all_attention_pins(o)
     all_accept_pins(o)
     all_coupled_pins(o)
+    all_route_pins(o)

@@ -43,6 +43,14 @@ MUTANTS = [
     ("coupled rejection commits the draft", "ob[o[L + 1]] = (int32_t)c[o[L + 1]];", "ob[o[L + 1]] = xb[o[L + 1]];"),
     ("coupled assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;\n        if (L < gamma)",
      "ob[k] = (tb[k] < L) ? xb[k] : -1;\n        if (L < gamma)"),
+    ("route margin of the top entry only", "a = (p1 - p2 >= param) ? 1.0 : 0.0;", "a = (p1 >= param) ? 1.0 : 0.0;"),
+    ("route entropy not normalised", "const double hn = (V > 1) ? h / log((double)V) : 0.0;",
+     "const double hn = (V > 1) ? h : 0.0;"),
+    ("route entropy sign", "a = exp(-param * hn);", "a = exp(param * hn);"),
+    ("route slot order", "const float *p = probs + ((size_t)b * B + o[r]) * V;",
+     "const float *p = probs + ((size_t)b * B + (r - 1)) * V;"),
+    ("route sums alphas", "sum += prod;", "sum += a;"),
+    ("route second entry not tracked", "else if (x > p2) p2 = x;", ";"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

@@ -117,3 +117,19 @@ def test_coupled_accept_closed_form(o):
 
 def test_coupled_preserves_target_law(o):
     pins.pin_coupled_preserves_target_law(o)
+
+
+def test_route_closed_forms(o):
+    pins.pin_route_closed_forms(o)
+
+
+def test_route_margin_counts(o):
+    pins.pin_route_margin_counts(o)
+
+
+def test_route_entropy_library(o):
+    pins.pin_route_entropy_library(o)
+
+
+def test_route_expected_prefix(o):
+    pins.pin_route_expected_prefix(o)

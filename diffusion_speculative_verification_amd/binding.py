@@ -57,6 +57,10 @@ def load(path: str | None = None):
     lib.spec_verify_accept_coupled_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept_coupled.restype = I
     lib.spec_verify_accept_coupled.argtypes = [V, V, V, V, I, I, I, I64, F, V, V, V, V, SZ, V]
+    lib.spec_verify_route_workspace_size.restype = SZ
+    lib.spec_verify_route_workspace_size.argtypes = [I, I, I, I64]
+    lib.spec_verify_route.restype = I
+    lib.spec_verify_route.argtypes = [V, V, I, I, I, I64, I, D, V, V, V, SZ, V]
     if path is None:
         _lib = lib
     return lib
@@ -132,3 +136,17 @@ def spec_verify_accept_coupled(target_logits, gumbel, draft_tokens, tau, batch, 
                                              batch, block, gamma, vocab, float(temperature), _ptr(accept_len),
                                              _ptr(out_tokens), _ptr(target_tokens), _ptr(workspace),
                                              int(workspace_bytes), _stream(stream)))
+
+
+SV_ROUTE_MARGIN, SV_ROUTE_ENTROPY = 0, 1
+
+
+def spec_verify_route_workspace_size(batch, block, gamma, vocab) -> int:
+    return int(load().spec_verify_route_workspace_size(batch, block, gamma, vocab))
+
+
+def spec_verify_route(draft_probs, tau, batch, block, gamma, vocab, estimator, param, khat, alpha_hat, workspace,
+                      workspace_bytes, stream=None) -> None:
+    _check(load().spec_verify_route(_ptr(draft_probs), _ptr(tau), batch, block, gamma, vocab, int(estimator),
+                                    float(param), _ptr(khat), _ptr(alpha_hat), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream)))

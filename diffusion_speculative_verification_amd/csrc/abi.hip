@@ -147,4 +147,30 @@ int spec_verify_accept_coupled(const float *target_logits, const float *gumbel, 
                                          target_tokens, workspace, (hipStream_t)stream));
 }
 
+size_t spec_verify_route_workspace_size(int batch, int block, int gamma, int64_t vocab) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab > (1ll << 21))
+        return 0;
+    return sv::route_plan(batch, block, gamma, vocab).ws_total;
+}
+
+int spec_verify_route(const float *draft_probs, const int32_t *tau, int batch, int block, int gamma,
+                      int64_t vocab, int estimator, double param, float *khat, float *alpha_hat, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab > (1ll << 21))
+        return SV_E_SHAPE;
+    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (estimator != SV_ROUTE_MARGIN && estimator != SV_ROUTE_ENTROPY) return SV_E_UNSUPPORTED;
+    if (!isfinite(param)) return SV_E_SHAPE;
+    if (!draft_probs || !tau || !khat) return SV_E_NULL;
+    if (!aligned16(draft_probs) || !aligned16(tau) || !aligned16(khat) || (alpha_hat && !aligned16(alpha_hat)))
+        return SV_E_ALIGN;
+    const sv::RoutePlan p = sv::route_plan(batch, block, gamma, vocab);
+    if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
+    if (!aligned16(workspace)) return SV_E_ALIGN;
+    return map_launch(sv::launch_route(p, draft_probs, tau, batch, block, gamma, vocab, estimator, param, khat,
+                                       alpha_hat, workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

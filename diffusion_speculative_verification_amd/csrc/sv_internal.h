@@ -71,4 +71,16 @@ hipError_t launch_coupled(const CoupledPlan &p, const float *logits, const float
                           int32_t *accept_len, int32_t *out_tokens, int32_t *target_tokens, void *ws,
                           hipStream_t st);
 
+struct RoutePlan {
+    int rows;        // batch * block draft rows
+    int n_vsplit;    // vocab splits of the streaming reduction
+    size_t ws_total;
+};
+
+RoutePlan route_plan(int batch, int block, int gamma, int64_t vocab);
+
+hipError_t launch_route(const RoutePlan &p, const float *probs, const int32_t *tau, int batch, int block,
+                        int gamma, int64_t vocab, int estimator, double param, float *khat, float *alpha_hat,
+                        void *ws, hipStream_t st);
+
 }  // namespace sv

@@ -55,6 +55,14 @@ class StepBuffers:
             n = sv.spec_verify_accept_workspace_size(c.batch, c.block, c.gamma, c.vocab)
             self.acc_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.acc_ws_bytes = n
+        if "route" in parts:
+            if not hasattr(self, "draft_probs"):
+                self.draft_probs = up(inputs["draft_probs"])
+            self.khat = torch.empty(c.batch, dtype=torch.float32, device=device)
+            self.alpha_hat = torch.empty((c.batch, c.gamma), dtype=torch.float32, device=device)
+            n = sv.spec_verify_route_workspace_size(c.batch, c.block, c.gamma, c.vocab)
+            self.route_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.route_ws_bytes = n
         if "coupled" in parts:
             if not hasattr(self, "target_logits"):
                 self.target_logits = up(inputs["target_logits"])
@@ -89,6 +97,13 @@ class StepBuffers:
                                       self.tau, c.batch, c.block, c.gamma, c.vocab, T, self.cpl_accept_len,
                                       self.cpl_out_tokens, self.cpl_target_tokens, self.cpl_ws, self.cpl_ws_bytes,
                                       stream)
+
+    def route(self, estimator: str, param: float, stream=None):
+        """S2D2 verify-routing estimate K of every sequence (margin or entropy)."""
+        c = self.case
+        est = {"margin": sv.SV_ROUTE_MARGIN, "entropy": sv.SV_ROUTE_ENTROPY}[estimator]
+        sv.spec_verify_route(self.draft_probs, self.tau, c.batch, c.block, c.gamma, c.vocab, est, param, self.khat,
+                             self.alpha_hat, self.route_ws, self.route_ws_bytes, stream)
 
     def step(self, stream=None):
         """One verification step: attention with fused copy-aligned RoPE,

@@ -61,6 +61,9 @@ enum {
 
 enum { SV_F32 = 0, SV_BF16 = 1 };
 
+/* verify-routing estimators of spec_verify_route */
+enum { SV_ROUTE_MARGIN = 0, SV_ROUTE_ENTROPY = 1 };
+
 /* Returns SPEC_VERIFY_ABI_VERSION of the built library. */
 int spec_verify_abi_version(void);
 
@@ -177,6 +180,34 @@ int spec_verify_accept_coupled(const float *target_logits, const float *gumbel,
                                int gamma, int64_t vocab, float temperature, int32_t *accept_len,
                                int32_t *out_tokens, int32_t *target_tokens, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace spec_verify_route needs for these sizes. */
+size_t spec_verify_route_workspace_size(int batch, int block, int gamma, int64_t vocab);
+
+/*
+ * Verify-routing estimator (page "S2D2: Fast Decoding for Diffusion LLMs via
+ * Training-Free Self-Speculation", 方法步骤详情 (4): the expected accepted
+ * prefix length K = sum_k prod_{i<=k} alpha_i decides whether verifying is
+ * worth a forward; alpha_i is estimated from the draft distribution by its
+ * margin or its entropy).
+ *   draft_probs [batch][block][vocab] float32: the draft distribution of each
+ *               slot (entries >= 0)
+ *   tau         [batch][block] int32 step labels 1..block
+ *   estimator   SV_ROUTE_MARGIN: alpha = 1 if p_(1) - p_(2) >= param (the two
+ *               largest entries, difference exact in float64), else 0;
+ *               SV_ROUTE_ENTROPY: alpha = exp(-param * H / ln vocab) with
+ *               H = -sum_v p_v ln p_v (0 when vocab == 1; entries below the
+ *               smallest normal float count as 0)
+ *   param       the margin threshold or beta; finite
+ * Steps are taken in draft order r = 1..gamma (the slot with tau = r):
+ *   khat [batch] float32: sum_{k=1}^{gamma} prod_{r=1}^{k} alpha_r
+ *   alpha_hat [batch][gamma] float32 (may be NULL): alpha_r in draft order
+ * Limits as for spec_verify_accept; SV_E_UNSUPPORTED for an unknown
+ * estimator, SV_E_SHAPE for a non-finite param.
+ */
+int spec_verify_route(const float *draft_probs, const int32_t *tau, int batch, int block, int gamma,
+                      int64_t vocab, int estimator, double param, float *khat, float *alpha_hat,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
 
@@ -120,6 +120,27 @@ def test_coupled_argument_checks(lib):
     assert coupled(lib, g=A + 4) == sv.SV_E_ALIGN
     assert coupled(lib, tt=A + 4) == sv.SV_E_ALIGN
     assert coupled(lib, ws_bytes=4) == sv.SV_E_WORKSPACE
+
+
+def route(lib, **kw):
+    args = dict(dp=A, tau=A, batch=2, block=8, gamma=8, vocab=512, est=1, param=1.0, kh=A, ah=A, ws=A,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.spec_verify_route(args["dp"], args["tau"], args["batch"], args["block"], args["gamma"],
+                                 args["vocab"], args["est"], args["param"], args["kh"], args["ah"], args["ws"],
+                                 args["ws_bytes"], None)
+
+
+def test_route_argument_checks(lib):
+    assert sv.spec_verify_route_workspace_size(32, 32, 32, 151936) > 0
+    assert sv.spec_verify_route_workspace_size(32, 32, 0, 151936) == 0
+    assert route(lib, dp=None) == sv.SV_E_NULL
+    assert route(lib, kh=None) == sv.SV_E_NULL
+    assert route(lib, est=2) == sv.SV_E_UNSUPPORTED
+    assert route(lib, param=float("nan")) == sv.SV_E_SHAPE
+    assert route(lib, gamma=9) == sv.SV_E_SHAPE
+    assert route(lib, ah=A + 4) == sv.SV_E_ALIGN
+    assert route(lib, ws=None) == sv.SV_E_WORKSPACE
 
 
 def test_rope_argument_checks(lib):

@@ -20,7 +20,9 @@ oracle timed on this host over the same workload.
 
 --verify coupled | greedy replaces the epilogue by shared-noise verification
 (spec_verify_accept_coupled at --temperature, default 1) or its greedy form
-(T = 0); the default, rejection, is the headline step.
+(T = 0); the default, rejection, is the headline step.  --route margin |
+entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
+--route-param) in front of each step.
 """
 from __future__ import annotations
 
@@ -76,6 +78,12 @@ def coupled_bytes(c, greedy: bool) -> float:
     return rows * (1 if greedy else 2) + small
 
 
+def route_bytes(c) -> float:
+    """Algorithmic HBM bytes of one routing call: the float32 draft
+    distribution of every verified slot once, plus tau and the outputs."""
+    return 4.0 * c.batch * c.gamma * c.vocab + c.batch * (c.block * 4 + c.gamma * 4 + 4)
+
+
 def measured_traffic(call: str):
     """HBM bytes per launch of `call` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration),
@@ -95,11 +103,15 @@ def measured_traffic(call: str):
     return None
 
 
-def cpu_baseline(case, inp, verify="rejection", temperature=1.0) -> dict:
+def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0) -> dict:
     """The CPU oracle on this host over the same workload (one step)."""
     import oracle
     o = oracle.Oracle()
     threads = o.max_threads()
+    t = time.perf_counter()
+    if route != "none":
+        o.route(inp["draft_probs"], inp["tau"], case.gamma, route, rparam)
+    t_route = time.perf_counter() - t
     t = time.perf_counter()
     for b in range(case.batch):
         o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
@@ -113,10 +125,11 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0) -> dict:
         o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None, inp["coupled_tokens"],
                          inp["tau"], case.gamma, temperature)
     t_acc = time.perf_counter() - t
-    total = t_attn + t_acc
+    total = t_route + t_attn + t_acc
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of the same workload ({case.batch} sequences): attention "
-                      f"{t_attn:.2f} s + accept {t_acc:.2f} s on {threads} OpenMP threads "
+            "sample": f"one full step of the same workload ({case.batch} sequences): "
+                      + (f"routing {t_route:.2f} s + " if route != "none" else "") +
+                      f"attention {t_attn:.2f} s + accept {t_acc:.2f} s on {threads} OpenMP threads "
                       f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
 
 
@@ -130,6 +143,10 @@ def main():
     ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default="rejection",
                     help="epilogue: rejection sampling (headline), shared-noise or greedy verification")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
+    ap.add_argument("--route", choices=("none", "margin", "entropy"), default="none",
+                    help="add the S2D2 verify-routing estimate in front of each step")
+    ap.add_argument("--route-param", type=float, default=None,
+                    help="margin threshold (default 0.05) or entropy beta (default 1.0)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -156,9 +173,14 @@ def main():
     verify = args.verify
     T = 0.0 if verify == "greedy" else args.temperature
     parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
+    route = args.route
+    rparam = args.route_param if args.route_param is not None else (0.05 if route == "margin" else 1.0)
     if verify != "rejection":
         case = case.with_(temperature=T)
-    inp = synth.make_inputs(case, parts=parts)
+    gen_parts = parts + (("accept",) if route != "none" and "accept" not in parts else ())
+    inp = synth.make_inputs(case, parts=gen_parts)
+    if route != "none":
+        parts = parts + ("route",)
     sets = [StepBuffers(case, inp, parts=parts), StepBuffers(case, inp, parts=parts)]
     stream = torch.cuda.current_stream()
 
@@ -169,16 +191,21 @@ def main():
             s.accept_coupled(temperature=T)
 
     for i in range(args.warmup):
+        if route != "none":
+            sets[i & 1].route(route, rparam)
         sets[i & 1].attn()
         epilogue(sets[i & 1])
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
         s = sets[i & 1]
+        ev[i][3].record(stream)
+        if route != "none":
+            s.route(route, rparam)
         ev[i][0].record(stream)
         s.attn()
         ev[i][1].record(stream)
@@ -187,7 +214,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    total_ms = ev[0][3].elapsed_time(ev[K - 1][2])
+    route_ms = sum(ev[i][3].elapsed_time(ev[i][0]) for i in range(K)) / K if route != "none" else 0.0
     ms_step = total_ms / K
     attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
     acc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
@@ -207,8 +235,17 @@ def main():
     for r in (rl_attn, rl_acc):
         r["frac"] = r["achieved"] / r["peak"]
     dom = (acc_call, rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
+    rl_route = None
+    if route != "none":
+        r_bytes = route_bytes(case)
+        rl_route = {"bound": "hbm", "achieved": r_bytes / (route_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "ms": route_ms, "bytes": r_bytes, "estimator": route, "param": rparam}
+        rl_route["frac"] = rl_route["achieved"] / rl_route["peak"]
+        rl_route["traffic"] = measured_traffic("spec_verify_route") if case.name == "headline" else None
+        if route_ms > max(acc_ms, attn_ms):
+            dom = ("spec_verify_route", rl_route)
     roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
-        c_bytes / (HBM_PEAK_GBS * 1e9)
+        c_bytes / (HBM_PEAK_GBS * 1e9) + (route_bytes(case) / (HBM_PEAK_GBS * 1e9) if route != "none" else 0.0)
     # traffic only applies to the headline workload the counters were taken on
     headline = case.name == "headline"
     rl_attn["traffic"] = measured_traffic("spec_verify_attn") if headline else None
@@ -220,7 +257,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp, verify, T)
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam)
 
     out = {
         "metric": METRIC,
@@ -239,7 +276,9 @@ def main():
                                f"B=gamma={case.block}, {case.n_qh}/{case.n_kvh} heads, head_dim {case.head_dim}, "
                                f"vocab {case.vocab}, {case.dtype} attention, fp32 logits" +
                                ("" if verify == "rejection" else
-                                f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification"),
+                                f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification") +
+                               ("" if route == "none" else f"; S2D2 routing estimate ({route}, {rparam:g}) first"),
+                   "route": None if route == "none" else {"estimator": route, "param": rparam},
                    "verify": verify, "temperature": None if verify == "rejection" else T,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
@@ -249,6 +288,8 @@ def main():
         "detail": {
             "attn": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_attn.items()},
             "accept": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_acc.items()},
+            "route": None if rl_route is None else
+            {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_route.items()},
             "step_roofline_us": round(roof_step_s * 1e6, 2),
             "frac_of_step_roofline": round(roof_step_s / (ms_step * 1e-3), 4),
             "wall_s": round(wall, 4),

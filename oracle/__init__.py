@@ -83,6 +83,7 @@ class Oracle:
         lib.svo_coupled_choice.restype = i64
         lib.svo_accept_coupled.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P]
         lib.svo_route.argtypes = [P, P, i32, i32, i32, i64, i32, dbl, P, P]
+        lib.svo_attn_copies.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, dbl, P]
         lib.svo_set_threads.argtypes = [i32]
         self.lib = lib
 
@@ -130,6 +131,25 @@ class Oracle:
         out = np.empty((R, Hq, d), np.float64)
         _check(self.lib.svo_attn(_p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(tau),
                                  B, P, Hq, Hkv, d, float(theta), float(scale), _p(out)))
+        return out
+
+    def attention_copies(self, q, k_new, v_new, k_cache, v_cache, n_copies: int, theta: float,
+                         scale: float = 0.0) -> np.ndarray:
+        """Multi-copy verification attention of one sequence ("SPOT": the root and
+        draft states as copies of the block) -> float64 [C*L][Hq][d].
+
+        q [C*L][Hq][d], k_new/v_new [C*L][Hkv][d] copy-major (pre-RoPE when
+        theta > 0), k_cache/v_cache [Hkv][P][d]."""
+        q, k_new, v_new = _c(q, np.float32), _c(k_new, np.float32), _c(v_new, np.float32)
+        k_cache, v_cache = _c(k_cache, np.float32), _c(v_cache, np.float32)
+        R, Hq, d = q.shape
+        assert R % n_copies == 0
+        L = R // n_copies
+        Hkv, P = k_cache.shape[0], k_cache.shape[1]
+        assert k_new.shape == (R, Hkv, d) and v_new.shape == (R, Hkv, d)
+        out = np.empty((R, Hq, d), np.float64)
+        _check(self.lib.svo_attn_copies(_p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), L, n_copies, P,
+                                        Hq, Hkv, d, float(theta), float(scale), _p(out)))
         return out
 
     def softmax(self, l):
@@ -226,6 +246,7 @@ def max_threads(): return default().max_threads()
 def mask(tau, P): return default().mask(tau, P)
 def rope(x, pos, theta): return default().rope(x, pos, theta)
 def attention(*a, **k): return default().attention(*a, **k)
+def attention_copies(*a, **k): return default().attention_copies(*a, **k)
 def softmax(l): return default().softmax(l)
 def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)

@@ -150,15 +150,60 @@ void svo_rope(double *x, int64_t n, int heads, int d, const double *pos, double 
  * theta <= 0 the inputs are taken as already rotated.  scale <= 0 means
  * 1/sqrt(d).  Keys: prompt, then the 2B response keys, masked by svo_mask.
  */
+static int attn_dense(const float *q, const float *k_new, const float *v_new,
+                      const float *k_cache, const float *v_cache, const uint8_t *M,
+                      int R, int B, int P, int Hq, int Hkv, int d, double theta, double scale,
+                      double *out);
+
 int svo_attn(const float *q, const float *k_new, const float *v_new,
              const float *k_cache, const float *v_cache, const int32_t *tau,
              int B, int P, int Hq, int Hkv, int d, double theta, double scale,
              double *out) {
     if (B < 1 || P < 0 || Hq < 1 || Hkv < 1 || d < 2 || (d & 1) || Hq % Hkv) return SVO_BAD_ARG;
-    const int R = 2 * B, ncol = P + 2 * B, g = Hq / Hkv;
+    const int R = 2 * B, ncol = P + 2 * B;
     uint8_t *M = (uint8_t *)malloc((size_t)R * ncol);
     int rc = svo_mask(B, P, tau, M);
     if (rc) { free(M); return rc; }
+    rc = attn_dense(q, k_new, v_new, k_cache, v_cache, M, R, B, P, Hq, Hkv, d, theta, scale, out);
+    free(M);
+    return rc;
+}
+
+/*
+ * Multi-copy verification attention of ONE sequence ("SPOT", 方法步骤详情 /
+ * 核心方法 第三步: the target runs one batched forward over the root and all
+ * draft states, (1+D)L positions, each state a copy of the block; 前置知识
+ * "块扩散语言模型": attention is bidirectional inside a block and causal
+ * across blocks).  Row r belongs to copy r / L and sits at position
+ * P + (r mod L) (every copy is the same block); it sees every prompt key and
+ * the L keys of its own copy, none of another copy's.
+ *   q [C*L][Hq][d], k_new/v_new [C*L][Hkv][d] (copy-major, pre-RoPE if
+ *   theta > 0), k_cache/v_cache [Hkv][P][d], out [C*L][Hq][d] float64.
+ */
+int svo_attn_copies(const float *q, const float *k_new, const float *v_new,
+                    const float *k_cache, const float *v_cache, int L, int C, int P, int Hq,
+                    int Hkv, int d, double theta, double scale, double *out) {
+    if (L < 1 || C < 1 || P < 0 || Hq < 1 || Hkv < 1 || d < 2 || (d & 1) || Hq % Hkv) return SVO_BAD_ARG;
+    const int R = C * L, ncol = P + R;
+    uint8_t *M = (uint8_t *)malloc((size_t)R * ncol);
+    for (int i = 0; i < R; ++i)
+        for (int j = 0; j < ncol; ++j)
+            M[(size_t)i * ncol + j] = (uint8_t)(j < P || (j - P) / L == i / L);
+    const int rc = attn_dense(q, k_new, v_new, k_cache, v_cache, M, R, L, P, Hq, Hkv, d, theta, scale, out);
+    free(M);
+    return rc;
+}
+
+/*
+ * Attention of R response rows under a dense visibility matrix M[R][P + R]
+ * (prompt columns first); row r and response key r sit at position
+ * P + (r mod B).
+ */
+static int attn_dense(const float *q, const float *k_new, const float *v_new,
+                      const float *k_cache, const float *v_cache, const uint8_t *M,
+                      int R, int B, int P, int Hq, int Hkv, int d, double theta, double scale,
+                      double *out) {
+    const int ncol = P + R, g = Hq / Hkv;
     double *qd = (double *)malloc(sizeof(double) * (size_t)R * Hq * d);
     double *kd = (double *)malloc(sizeof(double) * (size_t)R * Hkv * d);
     double *pos = (double *)malloc(sizeof(double) * (size_t)R);
@@ -217,7 +262,7 @@ int svo_attn(const float *q, const float *k_new, const float *v_new,
         }
         free(sc);
     }
-    free(M); free(qd); free(kd); free(pos);
+    free(qd); free(kd); free(pos);
     return SVO_OK;
 }
 

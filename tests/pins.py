@@ -636,6 +636,72 @@ def all_coupled_pins(o):
     pin_coupled_preserves_target_law(o)
 
 
+# ---------------------------------------------- multi-copy verification
+def tiny_copy_inputs(seed, L=6, C=3, P=10, Hq=4, Hkv=2, d=16):
+    r = rng(seed)
+    R = C * L
+    return dict(
+        q=r.standard_normal((R, Hq, d)).astype(np.float32),
+        k_new=r.standard_normal((R, Hkv, d)).astype(np.float32),
+        v_new=r.standard_normal((R, Hkv, d)).astype(np.float32),
+        k_cache=r.standard_normal((Hkv, P, d)).astype(np.float32),
+        v_cache=r.standard_normal((Hkv, P, d)).astype(np.float32),
+    )
+
+
+def pin_copies_single_textbook(o, theta=1e4):
+    """One copy is a plain block: each row is ordinary unmasked attention over
+    [prompt ; the block], the block rotated at positions P + i."""
+    inp = tiny_copy_inputs(70, C=1)
+    L, Hq, d = inp["q"].shape
+    Hkv, P = inp["k_cache"].shape[0], inp["k_cache"].shape[1]
+    out = o.attention_copies(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], 1, theta)
+    pos = P + np.arange(L, dtype=np.float64)
+    qr = o.rope(inp["q"], pos, theta)
+    kr = o.rope(inp["k_new"], pos, theta)
+    g = Hq // Hkv
+    for i in range(L):
+        for h in range(Hq):
+            kv = h // g
+            K = np.concatenate([inp["k_cache"][kv].astype(np.float64), kr[:, kv]])
+            V = np.concatenate([inp["v_cache"][kv].astype(np.float64), inp["v_new"][:, kv].astype(np.float64)])
+            ref = textbook_attention(qr[i, h], K, V, 1 / np.sqrt(d))
+            assert np.abs(out[i, h] - ref).max() < 1e-12
+
+
+def pin_copies_decompose(o, theta=1e4):
+    """Each copy's rows equal a one-copy run on that copy's rows alone; a
+    change to one copy leaves every other copy bit-identical; permuting the
+    copies permutes the output."""
+    L, C = 5, 4
+    inp = tiny_copy_inputs(71, L=L, C=C, P=7)
+    args = (inp["k_cache"], inp["v_cache"])
+    out = o.attention_copies(inp["q"], inp["k_new"], inp["v_new"], *args, C, theta)
+    for c in range(C):
+        sl = slice(c * L, (c + 1) * L)
+        one = o.attention_copies(inp["q"][sl], inp["k_new"][sl], inp["v_new"][sl], *args, 1, theta)
+        assert np.array_equal(out[sl], one), c
+    k2, v2 = inp["k_new"].copy(), inp["v_new"].copy()
+    k2[L:2 * L] += 1.0
+    v2[L:2 * L] -= 2.0
+    out2 = o.attention_copies(inp["q"], k2, v2, *args, C, theta)
+    for c in range(C):
+        sl = slice(c * L, (c + 1) * L)
+        if c == 1:
+            assert np.abs(out2[sl] - out[sl]).max() > 1e-3
+        else:
+            assert np.array_equal(out2[sl], out[sl]), c
+    perm = np.array([2, 0, 3, 1])
+    rows = np.concatenate([np.arange(c * L, (c + 1) * L) for c in perm])
+    out3 = o.attention_copies(inp["q"][rows], inp["k_new"][rows], inp["v_new"][rows], *args, C, theta)
+    assert np.array_equal(out3, out[rows])
+
+
+def all_copies_pins(o):
+    pin_copies_single_textbook(o)
+    pin_copies_decompose(o)
+
+
 # ------------------------------------------------ verify-routing estimator
 def pin_route_closed_forms(o):
     """Uniform rows have normalised entropy 1, so alpha = exp(-beta) and K is
@@ -737,3 +803,4 @@ def all_pins(o):
     all_accept_pins(o)
     all_coupled_pins(o)
     all_route_pins(o)
+    all_copies_pins(o)

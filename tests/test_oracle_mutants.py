@@ -51,6 +51,8 @@ MUTANTS = [
      "const float *p = probs + ((size_t)b * B + (r - 1)) * V;"),
     ("route sums alphas", "sum += prod;", "sum += a;"),
     ("route second entry not tracked", "else if (x > p2) p2 = x;", ";"),
+    ("copies see earlier copies", "(uint8_t)(j < P || (j - P) / L == i / L);", "(uint8_t)(j < P || (j - P) / L <= i / L);"),
+    ("copies indexed by position", "(uint8_t)(j < P || (j - P) / L == i / L);", "(uint8_t)(j < P || (j - P) % L == i % L);"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

@@ -133,3 +133,11 @@ def test_route_entropy_library(o):
 
 def test_route_expected_prefix(o):
     pins.pin_route_expected_prefix(o)
+
+
+def test_copies_single_textbook(o):
+    pins.pin_copies_single_textbook(o)
+
+
+def test_copies_decompose(o):
+    pins.pin_copies_decompose(o)

@@ -57,6 +57,10 @@ def load(path: str | None = None):
     lib.spec_verify_accept_coupled_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept_coupled.restype = I
     lib.spec_verify_accept_coupled.argtypes = [V, V, V, V, I, I, I, I64, F, V, V, V, V, SZ, V]
+    lib.spec_verify_attn_copies_workspace_size.restype = SZ
+    lib.spec_verify_attn_copies_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.spec_verify_attn_copies.restype = I
+    lib.spec_verify_attn_copies.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, I, D, F, V, SZ, V]
     lib.spec_verify_route_workspace_size.restype = SZ
     lib.spec_verify_route_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_route.restype = I
@@ -150,3 +154,17 @@ def spec_verify_route(draft_probs, tau, batch, block, gamma, vocab, estimator, p
     _check(load().spec_verify_route(_ptr(draft_probs), _ptr(tau), batch, block, gamma, vocab, int(estimator),
                                     float(param), _ptr(khat), _ptr(alpha_hat), _ptr(workspace),
                                     int(workspace_bytes), _stream(stream)))
+
+
+def spec_verify_attn_copies_workspace_size(dtype, batch, block, n_copies, prefix_len, n_qh, n_kvh, head_dim) -> int:
+    return int(load().spec_verify_attn_copies_workspace_size(dtype, batch, block, n_copies, prefix_len, n_qh, n_kvh,
+                                                             head_dim))
+
+
+def spec_verify_attn_copies(q, k_new, v_new, k_cache, v_cache, out, dtype, batch, block, n_copies, prefix_len, n_qh,
+                            n_kvh, head_dim, rope_theta, softmax_scale, workspace, workspace_bytes,
+                            stream=None) -> None:
+    _check(load().spec_verify_attn_copies(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                          dtype, batch, block, n_copies, prefix_len, n_qh, n_kvh, head_dim,
+                                          float(rope_theta), float(softmax_scale), _ptr(workspace),
+                                          int(workspace_bytes), _stream(stream)))

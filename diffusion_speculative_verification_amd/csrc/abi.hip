@@ -59,7 +59,7 @@ int spec_verify_rope(const void *q_in, const void *k_in, void *q_out, void *k_ou
 size_t spec_verify_attn_workspace_size(int dtype, int batch, int block, int prefix_len, int n_qh, int n_kvh,
                                        int head_dim) {
     if (check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, prefix_len)) return 0;
-    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim};
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim, 2 * block, 0};
     return sv::attn_plan(s).ws_total;
 }
 
@@ -75,13 +75,52 @@ int spec_verify_attn(const void *q, const void *k_new, const void *v_new, const 
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(tau))
         return SV_E_ALIGN;
     if (prefix_len > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return SV_E_ALIGN;
-    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim};
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim, 2 * block, 0};
     const sv::AttnPlan p = sv::attn_plan(s);
     const bool need_ws = (dtype == SV_BF16) ? p.n_split > 1 : rope_theta > 0;
     if (need_ws && (!workspace || workspace_bytes < p.ws_total)) return SV_E_WORKSPACE;
     if (need_ws && !aligned16(workspace)) return SV_E_ALIGN;
     const float scale = softmax_scale > 0 ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
     return map_launch(sv::launch_attn(s, p, q, k_new, v_new, k_cache, v_cache, tau, out, rope_theta, scale,
+                                      workspace, (hipStream_t)stream));
+}
+
+namespace {
+int check_copies(int dtype, int batch, int block, int n_copies, int n_qh, int n_kvh, int head_dim, int prefix) {
+    if (dtype != SV_BF16) return SV_E_UNSUPPORTED;
+    int rc = check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, prefix);
+    if (rc) return rc;
+    if (n_copies < 1 || (long long)n_copies * block > sv::kMaxResp) return SV_E_SHAPE;
+    if ((long long)batch * n_copies * block * n_qh > (1ll << 30)) return SV_E_SHAPE;
+    if ((long long)prefix + (long long)n_copies * block > (1ll << 30)) return SV_E_SHAPE;
+    return SV_OK;
+}
+}  // namespace
+
+size_t spec_verify_attn_copies_workspace_size(int dtype, int batch, int block, int n_copies, int prefix_len,
+                                              int n_qh, int n_kvh, int head_dim) {
+    if (check_copies(dtype, batch, block, n_copies, n_qh, n_kvh, head_dim, prefix_len)) return 0;
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim, n_copies * block, 1};
+    return sv::attn_plan(s).ws_total;
+}
+
+int spec_verify_attn_copies(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                            const void *v_cache, void *out, int dtype, int batch, int block, int n_copies,
+                            int prefix_len, int n_qh, int n_kvh, int head_dim, double rope_theta,
+                            float softmax_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_copies(dtype, batch, block, n_copies, n_qh, n_kvh, head_dim, prefix_len);
+    if (rc) return rc;
+    if (!q || !k_new || !v_new || !out) return SV_E_NULL;
+    if (prefix_len > 0 && (!k_cache || !v_cache)) return SV_E_NULL;
+    if (!isfinite(rope_theta) || !isfinite(softmax_scale)) return SV_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return SV_E_ALIGN;
+    if (prefix_len > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return SV_E_ALIGN;
+    sv::AttnShape s{dtype, batch, block, prefix_len, n_qh, n_kvh, head_dim, n_copies * block, 1};
+    const sv::AttnPlan p = sv::attn_plan(s);
+    if (p.n_split > 1 && (!workspace || workspace_bytes < p.ws_total)) return SV_E_WORKSPACE;
+    if (p.n_split > 1 && !aligned16(workspace)) return SV_E_ALIGN;
+    const float scale = softmax_scale > 0 ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+    return map_launch(sv::launch_attn(s, p, q, k_new, v_new, k_cache, v_cache, nullptr, out, rope_theta, scale,
                                       workspace, (hipStream_t)stream));
 }
 

@@ -123,6 +123,7 @@ struct BfArgs {
     float *ws_o;    // split partials [split][batch][2B][Hq][D]
     float2 *ws_ml;  // [split][batch][2B][Hq] (running max in log2 units, sum)
     int batch, block, prefix, n_qh, n_kvh, n_rb, n_split, tiles_per_split, n_tiles;
+    int n_resp;  // response rows (and keys) per sequence: 2B, or copies * block
     int use_rope;
     double log2_theta;
     float scale_log2;  // softmax scale * log2(e)
@@ -131,7 +132,7 @@ struct BfArgs {
 template <int D>
 __device__ __forceinline__ const uint16_t *key_row(const BfArgs &a, const uint16_t *cache,
                                                    const uint16_t *fresh, int b, int kvh, int j) {
-    const int R = 2 * a.block;
+    const int R = a.n_resp;
     if (j >= a.prefix + R) j = a.prefix + R - 1;  // padding rows of the last tile: any valid row
     if (j < a.prefix) return cache + (((size_t)b * a.n_kvh + kvh) * a.prefix + j) * D;
     return fresh + (((size_t)b * R + (j - a.prefix)) * a.n_kvh + kvh) * D;
@@ -287,7 +288,7 @@ constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int QB>
 struct RowInfo {
-    int t_row[QB];     // step label of each row's slot
+    int t_row[QB];     // step label of each row's slot (copies: the row's copy)
     bool is_data[QB];  // D row (true) or D~ row
 };
 
@@ -339,7 +340,7 @@ __device__ __forceinline__ LdsOffs<D> lds_offsets(int lane, const char *v_stage0
 // prove that the refill in flight never aliases this step's reads.  Each
 // lane owns QB query rows (one per 32-row MFMA block); every K and V operand
 // read from LDS feeds QB MFMAs.
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, int MASK>
 __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t0, int nt, int it, bool wave_active,
                                           const RowInfo<QB> &ri, const LdsOffs<D> &lo_, const bf16x8 (*qop)[D / 16],
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
@@ -351,7 +352,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
-    const int B = a.block, P = a.prefix, Nk = P + 2 * B;
+    const int B = a.block, P = a.prefix, Nk = P + a.n_resp;
     const int base = (t0 + it) * kTileKeys;
     const int jend = min(Nk, (t0 + nt) * kTileKeys);
     // the LPT most recent loads are the refill issued one step ago (tile
@@ -426,11 +427,14 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;  // < 0: prompt key
-                const int lab = klab[max(0, min(c, 2 * kMaxBlock))];
+                const int lab = klab[max(0, min(c, MASK == 0 ? 2 * kMaxBlock : kMaxResp))];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    // bitwise, so that the select stays a select (no branches)
-                    const bool vis = (c < 0) | ((lab >= 0) & visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1));
+                    // bitwise, so that the select stays a select (no branches);
+                    // copies: a key is visible to the rows of its own copy
+                    const bool vis = MASK == 0
+                        ? ((c < 0) | ((lab >= 0) & visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1)))
+                        : ((c < 0) | (lab == ri.t_row[qb]));
                     sacc[qb][kb][x] = vis ? sacc[qb][kb][x] : -INFINITY;
                 }
             }
@@ -518,7 +522,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 // registers is a full vmcnt(0): issuing the second tile after that wait
 // keeps it out of the chip-wide burst that every workgroup waits on before
 // its first tile.  LDS regions are __restrict__ parameters (see tile_step).
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, int MASK>
 __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v,
                                          uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
                                          bf16x8 (*qop)[D / 16], char *__restrict__ k0, char *__restrict__ v0,
@@ -539,9 +543,14 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
             cs[pr * kCsStride<D> + i] = rope_cs((double)P + (double)pr, invf[i]);
         }
     }
-    // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
-    const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
-    if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
+    if constexpr (MASK == 0) {
+        // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
+        const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
+        if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
+    } else {
+        // copies: the copy index of each response key; -1 past them
+        for (int c = tid; c <= kMaxResp; c += NTH) klab[c] = (c < a.n_resp) ? c / B : -1;
+    }
     ring_barrier();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -562,7 +571,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
 
 // NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles
 // fed by direct global->LDS loads.
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, int MASK>
 __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16;
@@ -574,10 +583,10 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
     __shared__ __attribute__((aligned(16))) float2 cs_lds[kMaxBlock * kCsStride<D>];
     __shared__ double invf_lds[D / 2];
-    __shared__ int klab_lds[2 * kMaxBlock + 1];
+    __shared__ int klab_lds[kMaxResp + 1];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const int B = a.block, R2 = 2 * B, g = a.n_qh / a.n_kvh, R = g * R2;
+    const int B = a.block, R2 = a.n_resp, g = a.n_qh / a.n_kvh, R = g * R2;
 
     // workgroup -> (b, kvh, rb, split); consecutive logical ids land on one
     // XCD when the grid divides by 8, so row blocks / splits of one kv head
@@ -598,7 +607,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     // ---- tau (lane k of every wave holds tau[k]) and this lane's query rows:
     // their loads go out before the tiles' so that waiting for them does not
     // drain the tile loads
-    const int tau_v = a.tau[(size_t)b * B + min(lane, B - 1)];
+    const int tau_v = MASK == 0 ? a.tau[(size_t)b * B + min(lane, B - 1)] : 0;
     bool rvalid[QB];
     int rrow[QB], qhead[QB], pos_idx[QB];
     uint4 raw[QB][NS];
@@ -616,13 +625,18 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     }
     const int jend = min(a.prefix + R2, t1 * kTileKeys);
     bf16x8 qop[QB][NS];
-    prologue<D, NW, QB>(a, b, kvh, t0, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
+    prologue<D, NW, QB, MASK>(a, b, kvh, t0, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
                         invf_lds, klab_lds);
     RowInfo<QB> ri;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        ri.t_row[qb] = __shfl(tau_v, pos_idx[qb]);
-        ri.is_data[qb] = rrow[qb] < B;
+        if constexpr (MASK == 0) {
+            ri.t_row[qb] = __shfl(tau_v, pos_idx[qb]);
+            ri.is_data[qb] = rrow[qb] < B;
+        } else {
+            ri.t_row[qb] = rrow[qb] / B;  // the row's copy
+            ri.is_data[qb] = false;
+        }
     }
     const LdsOffs<D> offs = lds_offsets<D>(lane, v_st0);
     const LoadOffs<D, NW> ldo = load_offsets<D, NW>(w, lane);
@@ -644,13 +658,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     }
 
     for (int it = 0; it < nt; it += 3) {
-        tile_step<D, NW, QB>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
+        tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
                              cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
         if (it + 1 < nt)
-            tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
+            tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
                                  v_st0, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
         if (it + 2 < nt)
-            tile_step<D, NW, QB>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
+            tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
                                  v_st1, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
@@ -807,12 +821,12 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float *__restrict__
 AttnPlan attn_plan(const AttnShape &s) {
     AttnPlan p{};
     const int g = s.n_qh / s.n_kvh;
-    p.rows = g * 2 * s.block;
+    p.rows = g * s.n_resp;
     // 32 query rows per wave; 8 waves when a kv head has more than 128 rows
     p.qb = 1;
     p.nw = p.rows > 128 ? 8 : 4;
     p.n_rb = (p.rows + 32 * p.qb * p.nw - 1) / (32 * p.qb * p.nw);
-    const int nk = s.prefix + 2 * s.block;
+    const int nk = s.prefix + s.n_resp;
     p.n_tiles = (nk + kTileKeys - 1) / kTileKeys;
     p.n_split = 1;
     p.tiles_per_split = p.n_tiles;
@@ -828,7 +842,7 @@ AttnPlan attn_plan(const AttnShape &s) {
             }
         }
         if (p.n_split > 1) {
-            const size_t rows = (size_t)p.n_split * s.batch * 2 * s.block * s.n_qh;
+            const size_t rows = (size_t)p.n_split * s.batch * s.n_resp * s.n_qh;
             p.ws_partial_o = align_up(rows * s.head_dim * sizeof(float));
             p.ws_partial_ml = align_up(rows * sizeof(float2));
         }
@@ -864,7 +878,7 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
                        const void *v_new, const void *k_cache, const void *v_cache,
                        const int32_t *tau, void *out, double theta, float scale, void *ws,
                        hipStream_t st) {
-    const int R2 = 2 * s.block;
+    const int R2 = s.n_resp;
     if (s.dtype == 1) {
         BfArgs a{};
         a.q = (const uint16_t *)q;
@@ -885,15 +899,23 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.n_split = p.n_split;
         a.tiles_per_split = p.tiles_per_split;
         a.n_tiles = p.n_tiles;
+        a.n_resp = s.n_resp;
         a.use_rope = theta > 0 ? 1 : 0;
         a.log2_theta = theta > 0 ? log2(theta) : 0.0;
         a.scale_log2 = scale * kLog2e;
         const unsigned grid = (unsigned)((size_t)s.batch * s.n_kvh * p.n_rb * p.n_split);
         const dim3 blk(64 * p.nw);
-        if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1>), dim3(grid), blk, 0, st, a);
-        else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1>), dim3(grid), blk, 0, st, a);
-        else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1>), dim3(grid), blk, 0, st, a);
-        else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1>), dim3(grid), blk, 0, st, a);
+        if (s.mask == 0) {
+            if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 0>), dim3(grid), blk, 0, st, a);
+            else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1, 0>), dim3(grid), blk, 0, st, a);
+            else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 0>), dim3(grid), blk, 0, st, a);
+            else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1, 0>), dim3(grid), blk, 0, st, a);
+        } else {
+            if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 1>), dim3(grid), blk, 0, st, a);
+            else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1, 1>), dim3(grid), blk, 0, st, a);
+            else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 1>), dim3(grid), blk, 0, st, a);
+            else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1, 1>), dim3(grid), blk, 0, st, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.n_split == 1) return e;
         const size_t rows_total = (size_t)s.batch * R2 * s.n_qh;

@@ -9,12 +9,15 @@ namespace sv {
 
 constexpr int kTileKeys = 64;        // keys per attention tile
 constexpr int kMaxBlock = 64;        // largest block size B
+constexpr int kMaxResp = 1024;       // largest number of response rows (copies * block)
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct AttnShape {
     int dtype, batch, block, prefix, n_qh, n_kvh, head_dim;
+    int n_resp;  // response rows per sequence: 2 * block (paired layout) or copies * block
+    int mask;    // 0: temporal mask from tau; 1: copies, each bidirectional over its own block
 };
 
 struct AttnPlan {

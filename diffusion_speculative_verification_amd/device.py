@@ -55,6 +55,18 @@ class StepBuffers:
             n = sv.spec_verify_accept_workspace_size(c.batch, c.block, c.gamma, c.vocab)
             self.acc_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.acc_ws_bytes = n
+        if "copies" in parts:
+            if not hasattr(self, "k_cache"):
+                self.k_cache = up(inputs["k_cache"], dt)
+                self.v_cache = up(inputs["v_cache"], dt)
+            self.q_c = up(inputs["q_c"], dt)
+            self.k_new_c = up(inputs["k_new_c"], dt)
+            self.v_new_c = up(inputs["v_new_c"], dt)
+            self.out_c = torch.empty_like(self.q_c)
+            n = sv.spec_verify_attn_copies_workspace_size(self.dtype_code, c.batch, c.block, c.n_copies, c.prefix_len,
+                                                          c.n_qh, c.n_kvh, c.head_dim)
+            self.copies_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.copies_ws_bytes = n
         if "route" in parts:
             if not hasattr(self, "draft_probs"):
                 self.draft_probs = up(inputs["draft_probs"])
@@ -97,6 +109,14 @@ class StepBuffers:
                                       self.tau, c.batch, c.block, c.gamma, c.vocab, T, self.cpl_accept_len,
                                       self.cpl_out_tokens, self.cpl_target_tokens, self.cpl_ws, self.cpl_ws_bytes,
                                       stream)
+
+    def attn_copies(self, rope_theta=None, stream=None):
+        """Multi-copy verification attention: the root and draft states of the block."""
+        c = self.case
+        theta = c.theta if rope_theta is None else rope_theta
+        sv.spec_verify_attn_copies(self.q_c, self.k_new_c, self.v_new_c, self.k_cache, self.v_cache, self.out_c,
+                                   self.dtype_code, c.batch, c.block, c.n_copies, c.prefix_len, c.n_qh, c.n_kvh,
+                                   c.head_dim, theta, 0.0, self.copies_ws, self.copies_ws_bytes, stream)
 
     def route(self, estimator: str, param: float, stream=None):
         """S2D2 verify-routing estimate K of every sequence (margin or entropy)."""

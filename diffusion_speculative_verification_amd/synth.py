@@ -29,6 +29,8 @@ numpy default_rng(SeedSequence([s, t, b]))):
   t=10 shared-noise rows [B][V]: standard Gumbel -log(-log U), U uniform on
       (0,1), fp32 -- the rows of the noise table at the slots' absolute
       positions ("SPOT", 前置知识 "Gumbel-Max 技巧与随机耦合")
+  t=11 Q, t=12 K_new, t=13 V_new of the multi-copy layout: [C*B][heads][d]
+      iid N(0,1), copy-major (the root and draft states of the block)
 bf16 cases round Q/K/V and the caches to bf16 (round-to-nearest-even) and keep
 them as float32 arrays holding exactly bf16-representable values.
 
@@ -71,6 +73,7 @@ class Case:
     identity_every: int = 0
     seed: int = 0
     temperature: float = 1.0  # shared-noise verification (0: greedy)
+    n_copies: int = 9          # multi-copy verification: root + 8 draft states
 
     @property
     def rows(self) -> int:
@@ -172,7 +175,9 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
     q [n][2B][Hq][d], k_new/v_new [n][2B][Hkv][d], k_cache/v_cache
     [n][Hkv][P][d], tau [n][B], target_logits/draft_probs [n][B][V],
     draft_tokens [n][B], uniforms [n][gamma+1]; with "coupled" in parts also
-    target_logits, gumbel [n][B][V] and coupled_tokens [n][B].
+    target_logits, gumbel [n][B][V] and coupled_tokens [n][B]; with "copies"
+    also q_c [n][C*B][Hq][d], k_new_c/v_new_c [n][C*B][Hkv][d] (C =
+    case.n_copies) and the caches.
     """
     seqs = list(range(case.batch)) if seqs is None else list(seqs)
     n = len(seqs)
@@ -214,6 +219,29 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
 
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill_acc, range(n)))
+    if "copies" in parts:
+        C, Rc = case.n_copies, case.n_copies * case.block
+        out["q_c"] = np.empty((n, Rc, case.n_qh, d), np.float32)
+        out["k_new_c"] = np.empty((n, Rc, case.n_kvh, d), np.float32)
+        out["v_new_c"] = np.empty((n, Rc, case.n_kvh, d), np.float32)
+        if "k_cache" not in out:
+            out["k_cache"] = np.empty((n, case.n_kvh, P, d), np.float32)
+            out["v_cache"] = np.empty((n, case.n_kvh, P, d), np.float32)
+            need_cache = True
+        else:
+            need_cache = False
+
+        def fill_copies(i):
+            b = seqs[i]
+            out["q_c"][i] = _normal(case, 11, b, (Rc, case.n_qh, d))
+            out["k_new_c"][i] = _normal(case, 12, b, (Rc, case.n_kvh, d))
+            out["v_new_c"][i] = _normal(case, 13, b, (Rc, case.n_kvh, d))
+            if need_cache:
+                out["k_cache"][i] = _normal(case, 3, b, (case.n_kvh, P, d))
+                out["v_cache"][i] = _normal(case, 4, b, (case.n_kvh, P, d))
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill_copies, range(n)))
     if "coupled" in parts:
         V = case.vocab
         need_logits = "target_logits" not in out

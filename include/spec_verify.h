@@ -109,6 +109,35 @@ int spec_verify_attn(const void *q, const void *k_new, const void *v_new, const 
                      double rope_theta, float softmax_scale, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Bytes of workspace spec_verify_attn_copies needs for these sizes. */
+size_t spec_verify_attn_copies_workspace_size(int dtype, int batch, int block, int n_copies, int prefix_len,
+                                              int n_qh, int n_kvh, int head_dim);
+
+/*
+ * Multi-copy verification attention (page "SPOT: Enhancing Speculative
+ * Decoding for Diffusion Language Models via Commit-Order Prediction",
+ * 核心方法 第三步 and 方法步骤详情: the target runs one batched forward over the
+ * root state and the draft states, (1+D)L positions, each state a copy of
+ * the block; 前置知识 "块扩散语言模型": attention is bidirectional inside a
+ * block and causal across blocks).
+ *   q      [batch][n_copies*block][n_qh][head_dim], copy-major (row r belongs
+ *          to copy r / block)
+ *   k_new, v_new [batch][n_copies*block][n_kvh][head_dim]
+ *   k_cache, v_cache [batch][n_kvh][prefix_len][head_dim] (prompt keys already
+ *          rotated; may be NULL when prefix_len == 0)
+ *   out    [batch][n_copies*block][n_qh][head_dim]
+ * Row r of copy c sees every prompt key and the block keys of copy c only.
+ * Rows and keys of every copy sit at positions prefix_len + (r mod block)
+ * (all copies are the same block); rope_theta > 0 rotates q and k_new on the
+ * fly as spec_verify_attn does, <= 0 takes them as rotated.  dtype SV_BF16
+ * only (SV_E_UNSUPPORTED otherwise); 1 <= n_copies, n_copies * block <= 1024;
+ * other limits and conventions as spec_verify_attn.
+ */
+int spec_verify_attn_copies(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                            const void *v_cache, void *out, int dtype, int batch, int block, int n_copies,
+                            int prefix_len, int n_qh, int n_kvh, int head_dim, double rope_theta,
+                            float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace spec_verify_accept needs for these sizes. */
 size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab);
 

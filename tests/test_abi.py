@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
 
@@ -141,6 +141,29 @@ def test_route_argument_checks(lib):
     assert route(lib, gamma=9) == sv.SV_E_SHAPE
     assert route(lib, ah=A + 4) == sv.SV_E_ALIGN
     assert route(lib, ws=None) == sv.SV_E_WORKSPACE
+
+
+def test_copies_argument_checks(lib):
+    f = lib.spec_verify_attn_copies
+    ok = dict(q=A, k=A, v=A, kc=A, vc=A, o=A, dt=1, b=1, L=32, C=9, P=64, hq=4, hkv=4, d=128, th=1e6, sc=0.0,
+              ws=A, wb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["o"], a["dt"], a["b"], a["L"], a["C"], a["P"], a["hq"],
+                 a["hkv"], a["d"], a["th"], a["sc"], a["ws"], a["wb"], None)
+    assert sv.spec_verify_attn_copies_workspace_size(1, 1, 32, 9, 2048, 4, 4, 128) > 0   # prefix split
+    assert sv.spec_verify_attn_copies_workspace_size(1, 64, 32, 9, 2048, 32, 8, 128) == 0  # enough workgroups
+    assert sv.spec_verify_attn_copies_workspace_size(1, 1, 32, 33, 64, 4, 4, 128) == 0  # 33 * 32 > 1024
+    assert call(P=2048, wb=0) == sv.SV_E_WORKSPACE
+    assert call(q=None) == sv.SV_E_NULL
+    assert call(kc=None) == sv.SV_E_NULL
+    assert call(dt=0) == sv.SV_E_UNSUPPORTED
+    assert call(C=0) == sv.SV_E_SHAPE
+    assert call(C=33) == sv.SV_E_SHAPE
+    assert call(L=65, C=2) == sv.SV_E_SHAPE
+    assert call(o=A + 8) == sv.SV_E_ALIGN
 
 
 def test_rope_argument_checks(lib):

@@ -22,7 +22,11 @@ oracle timed on this host over the same workload.
 (spec_verify_accept_coupled at --temperature, default 1) or its greedy form
 (T = 0); the default, rejection, is the headline step.  --route margin |
 entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
---route-param) in front of each step.
+--route-param) in front of each step.  --copies C runs SPOT's multi-copy
+verification step instead: attention over C copies of the block (the root
+state and D = C - 1 draft states, spec_verify_attn_copies) followed by
+shared-noise (or, with --verify greedy, greedy) verification of the D draft
+steps; gamma = D.
 """
 from __future__ import annotations
 
@@ -41,20 +45,24 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-def attn_bytes(c) -> float:
+def attn_bytes(c, copies: int = 0) -> float:
     """Algorithmic HBM bytes of one attention call: prompt K/V cache, Q,
-    response K/V and the output, each read or written once."""
+    response K/V and the output, each read or written once (2B response rows,
+    or copies * B for the multi-copy layout)."""
     e = 2 if c.dtype == "bf16" else 4
-    R = 2 * c.block
+    R = copies * c.block if copies else 2 * c.block
     return e * (2 * c.batch * c.n_kvh * c.prefix_len * c.head_dim
                 + c.batch * R * c.n_qh * c.head_dim * 2
                 + 2 * c.batch * R * c.n_kvh * c.head_dim)
 
 
-def attn_flops(c) -> float:
+def attn_flops(c, copies: int = 0) -> float:
     """Algorithmic FLOPs: every response row attends to exactly P + B keys
-    (QK^T and PV, 2 flops per multiply-add)."""
-    return 4.0 * c.batch * 2 * c.block * c.n_qh * c.head_dim * (c.prefix_len + c.block)
+    (QK^T and PV, 2 flops per multiply-add): the paired layout's D rows see
+    P + (keys of earlier steps and their own), its mask rows as many, and
+    every copy row sees the prompt and its own copy's B keys."""
+    R = copies * c.block if copies else 2 * c.block
+    return 4.0 * c.batch * R * c.n_qh * c.head_dim * (c.prefix_len + c.block)
 
 
 def accept_bytes(c, n_rejecting: int) -> float:
@@ -103,8 +111,11 @@ def measured_traffic(call: str):
     return None
 
 
-def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0) -> dict:
-    """The CPU oracle on this host over the same workload (one step)."""
+def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
+                 attn_budget_s=20.0) -> dict:
+    """The CPU oracle on this host over the same workload (one step).  The
+    attention is timed over the first sequences of the batch until
+    `attn_budget_s` has passed and scaled to the whole batch."""
     import oracle
     o = oracle.Oracle()
     threads = o.max_threads()
@@ -113,10 +124,18 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
         o.route(inp["draft_probs"], inp["tau"], case.gamma, route, rparam)
     t_route = time.perf_counter() - t
     t = time.perf_counter()
+    n_seq = 0
     for b in range(case.batch):
-        o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
-                    inp["tau"][b], case.theta)
-    t_attn = time.perf_counter() - t
+        if copies:
+            o.attention_copies(inp["q_c"][b], inp["k_new_c"][b], inp["v_new_c"][b], inp["k_cache"][b],
+                               inp["v_cache"][b], copies, case.theta)
+        else:
+            o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
+                        inp["tau"][b], case.theta)
+        n_seq += 1
+        if time.perf_counter() - t > attn_budget_s:
+            break
+    t_attn = (time.perf_counter() - t) * case.batch / n_seq
     t = time.perf_counter()
     if verify == "rejection":
         o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"], inp["uniforms"],
@@ -126,10 +145,12 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
                          inp["tau"], case.gamma, temperature)
     t_acc = time.perf_counter() - t
     total = t_route + t_attn + t_acc
+    attn_what = (f"attention {t_attn:.2f} s" if n_seq == case.batch else
+                 f"attention {t_attn:.2f} s (timed on {n_seq} of {case.batch} sequences, scaled)")
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of the same workload ({case.batch} sequences): "
+            "sample": f"one step of the same workload ({case.batch} sequences): "
                       + (f"routing {t_route:.2f} s + " if route != "none" else "") +
-                      f"attention {t_attn:.2f} s + accept {t_acc:.2f} s on {threads} OpenMP threads "
+                      f"{attn_what} + accept {t_acc:.2f} s on {threads} OpenMP threads "
                       f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
 
 
@@ -140,8 +161,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default="rejection",
-                    help="epilogue: rejection sampling (headline), shared-noise or greedy verification")
+    ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default=None,
+                    help="epilogue: rejection sampling (headline), shared-noise or greedy verification "
+                         "(default: rejection; coupled with --copies)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="SPOT multi-copy verification over C copies of the block (root + C-1 draft states)")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
     ap.add_argument("--route", choices=("none", "margin", "entropy"), default="none",
                     help="add the S2D2 verify-routing estimate in front of each step")
@@ -170,9 +194,21 @@ def main():
     from diffusion_speculative_verification_amd.device import StepBuffers
 
     case = synth.config_by_name(args.config)
-    verify = args.verify
+    copies = args.copies
+    verify = args.verify or ("coupled" if copies else "rejection")
+    if copies:
+        if verify == "rejection" or args.route != "none":
+            print("--copies verifies by state equality (--verify coupled or greedy), without routing", file=sys.stderr)
+            sys.exit(2)
+        if not 2 <= copies <= case.block + 1 or copies * case.block > 1024:
+            print(f"--copies must lie in [2, {min(case.block + 1, 1024 // case.block)}] for block {case.block}",
+                  file=sys.stderr)
+            sys.exit(2)
+        case = case.with_(n_copies=copies, gamma=copies - 1)
     T = 0.0 if verify == "greedy" else args.temperature
     parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
+    if copies:
+        parts = ("copies", "coupled")
     route = args.route
     rparam = args.route_param if args.route_param is not None else (0.05 if route == "margin" else 1.0)
     if verify != "rejection":
@@ -184,6 +220,12 @@ def main():
     sets = [StepBuffers(case, inp, parts=parts), StepBuffers(case, inp, parts=parts)]
     stream = torch.cuda.current_stream()
 
+    def attend(s):
+        if copies:
+            s.attn_copies()
+        else:
+            s.attn()
+
     def epilogue(s):
         if verify == "rejection":
             s.accept()
@@ -193,7 +235,7 @@ def main():
     for i in range(args.warmup):
         if route != "none":
             sets[i & 1].route(route, rparam)
-        sets[i & 1].attn()
+        attend(sets[i & 1])
         epilogue(sets[i & 1])
     torch.cuda.synchronize()
 
@@ -207,7 +249,7 @@ def main():
         if route != "none":
             s.route(route, rparam)
         ev[i][0].record(stream)
-        s.attn()
+        attend(s)
         ev[i][1].record(stream)
         epilogue(s)
         ev[i][2].record(stream)
@@ -224,17 +266,26 @@ def main():
     slots = case.batch * case.gamma
     value = slots / (ms_step * 1e-3)
 
-    a_bytes, a_flops = attn_bytes(case), attn_flops(case)
+    a_bytes, a_flops = attn_bytes(case, copies), attn_flops(case, copies)
+    attn_call = "spec_verify_attn_copies" if copies else "spec_verify_attn"
     c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
     acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
-    rl_attn = {"bound": "hbm", "achieved": a_bytes / (attn_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "tflops": a_flops / (attn_ms * 1e-3) / 1e12, "bf16_peak_tflops": BF16_PEAK_TFLOPS,
-               "ms": attn_ms, "bytes": a_bytes}
+    # the attention is bound by whichever of HBM bytes and bf16 MFMA flops
+    # takes longer at peak (the multi-copy layout does B-fold more flops per
+    # prompt byte and crosses into the MFMA-bound side)
+    if a_flops / (BF16_PEAK_TFLOPS * 1e12) > a_bytes / (HBM_PEAK_GBS * 1e9):
+        rl_attn = {"bound": "mfma", "achieved": a_flops / (attn_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s", "gbs": a_bytes / (attn_ms * 1e-3) / 1e9, "ms": attn_ms, "bytes": a_bytes,
+                   "flops": a_flops}
+    else:
+        rl_attn = {"bound": "hbm", "achieved": a_bytes / (attn_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "tflops": a_flops / (attn_ms * 1e-3) / 1e12, "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+                   "ms": attn_ms, "bytes": a_bytes}
     rl_acc = {"bound": "hbm", "achieved": c_bytes / (acc_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
               "ms": acc_ms, "bytes": c_bytes}
     for r in (rl_attn, rl_acc):
         r["frac"] = r["achieved"] / r["peak"]
-    dom = (acc_call, rl_acc) if acc_ms >= attn_ms else ("spec_verify_attn", rl_attn)
+    dom = (acc_call, rl_acc) if acc_ms >= attn_ms else (attn_call, rl_attn)
     rl_route = None
     if route != "none":
         r_bytes = route_bytes(case)
@@ -248,8 +299,9 @@ def main():
         c_bytes / (HBM_PEAK_GBS * 1e9) + (route_bytes(case) / (HBM_PEAK_GBS * 1e9) if route != "none" else 0.0)
     # traffic only applies to the headline workload the counters were taken on
     headline = case.name == "headline"
-    rl_attn["traffic"] = measured_traffic("spec_verify_attn") if headline else None
-    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "")) \
+    tag = f"_c{copies}" if copies else ""
+    rl_attn["traffic"] = measured_traffic(attn_call + tag) if headline else None
+    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") + tag) \
         if headline else None
     roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
                 "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
@@ -257,7 +309,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp, verify, T, route, rparam)
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies)
 
     out = {
         "metric": METRIC,
@@ -272,14 +324,18 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{case.name} verify step: batch {case.batch}, prefix {case.prefix_len}, "
-                               f"B=gamma={case.block}, {case.n_qh}/{case.n_kvh} heads, head_dim {case.head_dim}, "
+        "config": {"workload": (f"{case.name} SPOT multi-copy verify step: {copies} copies (root + D={copies - 1} "
+                                f"draft states), gamma=D" if copies else f"{case.name} verify step") +
+                               f": batch {case.batch}, prefix {case.prefix_len}, "
+                               f"B={case.block}, gamma={case.gamma}, {case.n_qh}/{case.n_kvh} heads, "
+                               f"head_dim {case.head_dim}, "
                                f"vocab {case.vocab}, {case.dtype} attention, fp32 logits" +
                                ("" if verify == "rejection" else
                                 f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification") +
                                ("" if route == "none" else f"; S2D2 routing estimate ({route}, {rparam:g}) first"),
                    "route": None if route == "none" else {"estimator": route, "param": rparam},
                    "verify": verify, "temperature": None if verify == "rejection" else T,
+                   "copies": copies or None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
                    "parallelism": "single GPU"},

@@ -152,30 +152,47 @@ __device__ __forceinline__ uint16_t u4_elem(const uint4 &v, int e) {
 // ROWS_PER_LOAD; lane l writes physical chunk l % NCH of its row and
 // therefore fetches the logical chunk that the swizzle places there.
 // One wave-wide direct global->LDS load: lane l's 16 bytes at `src` land at
-// LDS address lds_dst + 16 * l, with the non-temporal hint (K/V tiles are
-// streamed: each is read once per workgroup).  Issued as inline assembly so that the
+// LDS address lds_dst + 16 * l, with the non-temporal hint when NT.  The
+// paired layout reads each K/V tile once per workgroup and streams it (NT);
+// in the multi-copy layout several row blocks of one kv head read the same
+// prompt tiles at about the same time on one XCD, and plain loads let the
+// later ones hit in L2.  Issued as inline assembly so that the
 // compiler's wait insertion does not treat later LDS reads of other ring
 // stages as dependent on it: every wait on these loads is explicit
 // (wait_vmcnt), and no compiler-visible global load is issued while tile
 // loads are in flight inside the tile loop.
+template <bool NT>
 __device__ __forceinline__ void direct_load16(const void *src, char *lds_dst) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SV_LDS char *)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :
-                 : "s"(m0), "v"(src)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                     :
+                     : "s"(m0), "v"(src)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(m0), "v"(src)
+                     : "memory", "m0");
 }
 
 // The same load with a uniform 64-bit base in scalar registers plus this
 // lane's 32-bit byte offset (the scalar-base address form), and the LDS
 // destination given as a wave-uniform address: no per-load vector address
 // arithmetic.
+template <bool NT>
 __device__ __forceinline__ void direct_load16_s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 :
-                 : "s"(m0), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(m0), "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0), "v"(voff), "s"(sbase)
+                     : "memory", "m0");
 }
 
 // Loop-invariant parts of this wave's tile loads: for load i, this lane's
@@ -209,7 +226,7 @@ __device__ __forceinline__ LoadOffs<D, NW> load_offsets(int w, int lane) {
 // there, keys at or past `jend` (the end of this workgroup's key range) read
 // the row jend - 1 instead: such rows are never used, and re-reading one row
 // keeps them in cache.
-template <int D, int NW, bool IS_V>
+template <int D, int NW, bool IS_V, bool NT>
 __device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache, const uint16_t *fresh,
                                           int b, int kvh, int base, int jend, char *lds_tile, int w, int lane) {
     using T = Tile<D, IS_V>;
@@ -222,7 +239,7 @@ __device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache
         const int q = pc ^ T::swz(row);
         const uint16_t *src = fast ? tile + row * D + q * 8
                                    : key_row<D>(a, cache, fresh, b, kvh, min(base + row, jend - 1)) + q * 8;
-        direct_load16(src, lds_tile + r0 * T::ROW_BYTES);
+        direct_load16<NT>(src, lds_tile + r0 * T::ROW_BYTES);
     }
 }
 
@@ -290,6 +307,7 @@ template <int QB>
 struct RowInfo {
     int t_row[QB];     // step label of each row's slot (copies: the row's copy)
     bool is_data[QB];  // D row (true) or D~ row
+    int c_lo, c_hi;    // copies: the range of copies this wave's rows belong to
 };
 
 // Loop-invariant LDS byte offsets of this lane's MFMA operand reads.  The
@@ -381,23 +399,34 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // k-steps, so that their issue overlaps matrix work instead of queueing
     // behind the other waves' loads right after the barrier.
     constexpr int NL = LoadOffs<D, NW>::N;  // loads per tensor
+    constexpr bool kNt = MASK == 0;         // see direct_load16
     const int nb = (t0 + it + 2) * kTileKeys;
     const bool prompt_refill = nb + kTileKeys <= P;  // uniform
     const uint16_t *kb_src = k_unit + (size_t)nb * D, *vb_src = v_unit + (size_t)nb * D;
     const uint32_t kn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)kn, vn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)vn;
     auto refill = [&](int i) {  // load i of 2 * NL: K loads first, then V
-        if (i < NL) direct_load16_s(kb_src, ldo.k[i], kn_lds + ldo.lds[i]);
-        else direct_load16_s(vb_src, ldo.v[i - NL], vn_lds + ldo.lds[i - NL]);
+        if (i < NL) direct_load16_s<kNt>(kb_src, ldo.k[i], kn_lds + ldo.lds[i]);
+        else direct_load16_s<kNt>(vb_src, ldo.v[i - NL], vn_lds + ldo.lds[i - NL]);
     };
     if (!prompt_refill) {
-        load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
-        load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
+        load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, nb, jend, kn, w, lane);
+        load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, nb, jend, vn, w, lane);
     } else if (!wave_active) {
 #pragma unroll
         for (int i = 0; i < 2 * NL; ++i) refill(i);
     }
     if (!wave_active) return;
 
+    // ---- copies: a tile of response keys none of whose copies has a row in
+    // this wave is wholly masked for it and leaves its state unchanged (all
+    // its probabilities are 0, the running max stays), so the wave skips it.
+    // Tiles holding prompt keys are always live.
+    if constexpr (MASK == 1) {
+        const int c0 = base - P;  // first response key of the tile
+        if (c0 >= 0 && !(c0 < a.n_resp && c0 / B <= ri.c_hi &&
+                         min(c0 + kTileKeys - 1, a.n_resp - 1) / B >= ri.c_lo))
+            return;
+    }
     // ---- S^T = K Q^T (keys x queries): 2 key blocks of 32 per query block
     f32x16 sacc[QB][2];
 #pragma unroll
@@ -532,8 +561,9 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)
-    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
-    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
+    constexpr bool kNt = MASK == 0;
+    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
+    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
     if (a.use_rope) {
         if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
@@ -565,8 +595,8 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     }
     // the second tile (a tile past the end reads clamped rows and is never
     // consumed)
-    load_tile<D, NW, false>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
-    load_tile<D, NW, true>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
+    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
+    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
 }
 
 // NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles
@@ -636,6 +666,18 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
         } else {
             ri.t_row[qb] = rrow[qb] / B;  // the row's copy
             ri.is_data[qb] = false;
+        }
+    }
+    ri.c_lo = 0;
+    ri.c_hi = R2 / B - 1;
+    if constexpr (MASK == 1) {
+        // rows rho0 .. rho1 of this wave; one head's rows are contiguous in
+        // copy order, a wave that crosses into the next head keeps all copies
+        const int rho0 = __builtin_amdgcn_readfirstlane(rb * ROWS_B + w * ROWS_W);
+        const int rho1 = min(rho0 + ROWS_W, R) - 1;
+        if (rho0 < R && rho0 / R2 == rho1 / R2) {
+            ri.c_lo = (rho0 % R2) / B;
+            ri.c_hi = (rho1 % R2) / B;
         }
     }
     const LdsOffs<D> offs = lds_offsets<D>(lane, v_st0);

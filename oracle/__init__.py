@@ -22,6 +22,14 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 value (ties to even), kept as float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
 SRC = os.path.join(_HERE, "svo.c")
 LIB = os.path.join(_HERE, "libsvo.so")
 _lock = threading.Lock()
@@ -84,6 +92,9 @@ class Oracle:
         lib.svo_accept_coupled.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P]
         lib.svo_route.argtypes = [P, P, i32, i32, i32, i64, i32, dbl, P, P]
         lib.svo_attn_copies.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, dbl, P]
+        lib.svo_gather_prefix.argtypes = [P, P, i32, i32, i32, i32, i32, P]
+        lib.svo_commit.argtypes = [P, P, i32, i32, i32, P, P, P]
+        lib.svo_kv_append.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, dbl, P, P, P]
         lib.svo_set_threads.argtypes = [i32]
         self.lib = lib
 
@@ -151,6 +162,87 @@ class Oracle:
         _check(self.lib.svo_attn_copies(_p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), L, n_copies, P,
                                         Hq, Hkv, d, float(theta), float(scale), _p(out)))
         return out
+
+    def gather_prefix(self, pages, table_row, P: int, page_size: int) -> np.ndarray:
+        """Prompt rows 0..P-1 of one sequence from a paged cache -> float32 [Hkv][P][d].
+
+        pages [n_pages][Hkv][page_size][d]; row j sits at row j % page_size of
+        page table_row[j // page_size]."""
+        pages, table_row = _c(pages, np.float32), _c(table_row, np.int32)
+        n_pages, Hkv, ps, d = pages.shape
+        assert ps == page_size
+        out = np.empty((Hkv, P, d), np.float32)
+        _check(self.lib.svo_gather_prefix(_p(pages), _p(table_row), P, page_size, n_pages, Hkv, d, _p(out)))
+        return out
+
+    def attention_paged(self, q, k_new, v_new, k_pages, v_pages, block_table, prefix_lens, tau, page_size: int,
+                        theta: float, n_copies: int = 0, scale: float = 0.0) -> np.ndarray:
+        """Verification attention of a batch whose prompt caches are paged (or
+        contiguous with a row stride, block_table None) and of per-sequence
+        lengths -> float64 [batch][R][Hq][d].  Each sequence is the one-sequence
+        oracle (paired layout with tau, or n_copies copies) over its own prompt
+        rows, gathered by gather_prefix."""
+        out = []
+        for b in range(q.shape[0]):
+            P = int(prefix_lens[b])
+            if block_table is None:   # contiguous [batch][Hkv][stride][d]
+                kc = _c(k_pages[b][:, :P], np.float32)
+                vc = _c(v_pages[b][:, :P], np.float32)
+            else:
+                kc = self.gather_prefix(k_pages, block_table[b], P, page_size)
+                vc = self.gather_prefix(v_pages, block_table[b], P, page_size)
+            if n_copies == 0:
+                out.append(self.attention(q[b], k_new[b], v_new[b], kc, vc, tau[b], theta, scale))
+            else:
+                out.append(self.attention_copies(q[b], k_new[b], v_new[b], kc, vc, n_copies, theta, scale))
+        return np.stack(out) if out else np.zeros((0,) + q.shape[1:], np.float64)
+
+    def commit(self, out_tokens, block_tokens, gamma: int):
+        """Commit step (SimSD 关键设计 4) -> (block_tokens after, remaining R,
+        state (0 continue / 1 fall back to denoising / 2 finished), n_append)."""
+        out_tokens = _c(out_tokens, np.int32)
+        bt = np.array(block_tokens, dtype=np.int32, copy=True)
+        n, B = out_tokens.shape
+        rem, state, napp = (np.empty(n, np.int32) for _ in range(3))
+        _check(self.lib.svo_commit(_p(out_tokens), _p(bt), n, B, gamma, _p(rem), _p(state), _p(napp)))
+        return bt, rem, state, napp
+
+    def kv_append(self, k_rows, v_rows, n_append, k_pages, v_pages, block_table, prefix_lens, page_size: int,
+                  theta: float, round_bf16: bool = True):
+        """Append each sequence's first n_append[b] rows to its prompt cache at
+        positions prefix_lens[b] + i (keys rotated there when theta > 0) ->
+        (k_pages, v_pages, prefix_lens, status), new arrays.
+
+        k_rows/v_rows [batch][stride][Hkv][d]; pages [n_pages][Hkv][page_size][d]
+        with block_table [batch][max_pages], or contiguous [batch][Hkv][stride][d]
+        with block_table None (page_size = the row stride).  Stored keys are
+        rounded to bfloat16 (nearest, ties to even) when round_bf16, as a bf16
+        cache holds them; values are stored as given."""
+        k_rows, v_rows = _c(k_rows, np.float32), _c(v_rows, np.float32)
+        n_append = _c(n_append, np.int32)
+        pl = np.array(prefix_lens, dtype=np.int32, copy=True)
+        p0 = pl.copy()
+        n, S, Hkv, d = k_rows.shape
+        cap = page_size * (block_table.shape[1] if block_table is not None else 1)
+        ko, vo = np.zeros((n, S, Hkv, d), np.float64), np.zeros((n, S, Hkv, d), np.float64)
+        st = np.empty(n, np.int32)
+        _check(self.lib.svo_kv_append(_p(k_rows), _p(v_rows), S, _p(n_append), _p(pl), n, cap, Hkv, d,
+                                      float(theta), _p(ko), _p(vo), _p(st)))
+        kp, vp = np.array(k_pages, np.float32, copy=True), np.array(v_pages, np.float32, copy=True)
+        ks = ko.astype(np.float32)
+        if round_bf16:
+            ks = _round_bf16(ks)
+        for b in range(n):
+            if st[b]:
+                continue
+            for i in range(int(n_append[b])):
+                j = int(p0[b]) + i
+                if block_table is None:
+                    kp[b, :, j], vp[b, :, j] = ks[b, i], vo[b, i]
+                else:
+                    pg = int(block_table[b][j // page_size])
+                    kp[pg, :, j % page_size], vp[pg, :, j % page_size] = ks[b, i], vo[b, i]
+        return kp, vp, pl, st
 
     def softmax(self, l):
         """Float64 softmax of one logits row -> (p, m, s)."""
@@ -247,6 +339,10 @@ def mask(tau, P): return default().mask(tau, P)
 def rope(x, pos, theta): return default().rope(x, pos, theta)
 def attention(*a, **k): return default().attention(*a, **k)
 def attention_copies(*a, **k): return default().attention_copies(*a, **k)
+def attention_paged(*a, **k): return default().attention_paged(*a, **k)
+def gather_prefix(*a, **k): return default().gather_prefix(*a, **k)
+def commit(*a, **k): return default().commit(*a, **k)
+def kv_append(*a, **k): return default().kv_append(*a, **k)
 def softmax(l): return default().softmax(l)
 def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)

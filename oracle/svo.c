@@ -33,6 +33,12 @@
  *     prefix length K = sum_k prod_{i<=k} alpha_i with a margin-based
  *     (indicator of margin >= threshold) or entropy-based (exp(-beta H~))
  *     estimate of each alpha_i.
+ *   - "SimSD", 关键设计 4 (a block with fewer undecoded positions than the
+ *     draft length is finished by ordinary denoising) and 损失函数 / 训练策略
+ *     (the prompt's K/V are cached), with the block-diffusion prior of
+ *     "SPOT", 前置知识 (finished blocks join the cached prefix): the commit
+ *     step, the cache append and the paged prompt cache at the end of this
+ *     file.
  * Readings where the pages are silent (each is listed in the design doc):
  *   prompt carries step label 0 and counts as data; D~_k shares tau(k) with
  *   D_k; positions are 0..P-1 for the prompt and P+k for both D_k and D~_k;
@@ -535,4 +541,101 @@ int svo_route(const float *probs, const int32_t *tau, int batch, int B, int gamm
         if (o != order) free(o);
     }
     return err;
+}
+
+/*
+ * Prompt rows of ONE sequence from its cache, for callers that keep the
+ * prompt K (or V) in pages.  The pages say only that the prompt's K/V are
+ * cached ("SimSD", 损失函数 / 训练策略: a KV cache makes the prefix cost
+ * linear; the block-diffusion prior in "SPOT", 前置知识: finished blocks are
+ * cached and later blocks attend to them).  Paging is this build's storage
+ * reading of that cache: row j of the sequence is row j % page_size of page
+ * table_row[j / page_size], pages laid out [n_pages][Hkv][page_size][d].
+ * out [Hkv][P][d].  Returns SVO_BAD_ARG for a page id outside [0, n_pages).
+ */
+int svo_gather_prefix(const float *pages, const int32_t *table_row, int P, int page_size, int n_pages,
+                      int Hkv, int d, float *out) {
+    if (P < 0 || page_size < 1 || n_pages < 1 || Hkv < 1 || d < 1) return SVO_BAD_ARG;
+    for (int j = 0; j < P; ++j) {
+        const int pg = table_row[j / page_size];
+        if (pg < 0 || pg >= n_pages) return SVO_BAD_ARG;
+        for (int h = 0; h < Hkv; ++h)
+            memcpy(out + ((size_t)h * P + j) * d,
+                   pages + (((size_t)pg * Hkv + h) * page_size + j % page_size) * d, sizeof(float) * d);
+    }
+    return SVO_OK;
+}
+
+/*
+ * Commit step of one verification round, per sequence ("SimSD", 关键设计 4:
+ * the accepted prefix is kept, the first rejected position is resampled in
+ * place, the rest is discarded; when fewer undecoded positions R remain in
+ * the block than the draft length gamma, the block is finished by ordinary
+ * target denoising).
+ *   out_tokens   [batch][B]: the verification output, the committed token of
+ *                each slot or -1 (accepted slots and the resampled slot carry
+ *                a token).
+ *   block_tokens [batch][B], in/out: the block's tokens, -1 where still
+ *                masked; every committed token is written into its slot.
+ *   remaining [batch] = R, the masked slots left after the commit;
+ *   state [batch] = 2 when R == 0 (the block is finished and joins the
+ *   prefix), 1 when 0 < R < gamma (fall back to target denoising), else 0;
+ *   n_append [batch] = B when the block is finished (its B rows are appended
+ *   to the prompt cache), else 0.
+ */
+int svo_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int B, int gamma,
+               int32_t *remaining, int32_t *state, int32_t *n_append) {
+    if (batch < 0 || B < 1 || gamma < 1 || gamma > B) return SVO_BAD_ARG;
+    for (int b = 0; b < batch; ++b) {
+        int R = 0;
+        for (int k = 0; k < B; ++k) {
+            const size_t i = (size_t)b * B + k;
+            if (out_tokens[i] >= 0) block_tokens[i] = out_tokens[i];
+            if (block_tokens[i] < 0) ++R;
+        }
+        remaining[b] = R;
+        state[b] = (R == 0) ? 2 : (R < gamma ? 1 : 0);
+        n_append[b] = (R == 0) ? B : 0;
+    }
+    return SVO_OK;
+}
+
+/*
+ * Append rows to the prompt cache of each sequence (the cache of
+ * svo_gather_prefix; the finished block joins the prefix).  Sequence b
+ * appends rows 0 .. n_append[b]-1 of its source rows (k_rows / v_rows
+ * [batch][src_stride][Hkv][d]) at positions prefix_lens[b] + i, then
+ * prefix_lens[b] += n_append[b].  With theta > 0 the key of row i is rotated
+ * at its position prefix_lens[b] + i before it is stored (the cache holds
+ * rotated keys, as the attention's prompt keys are).  k_out / v_out receive
+ * the stored rows as float64 [batch][src_stride][Hkv][d] (rows past
+ * n_append[b] untouched) and pages are not written here: the caller places
+ * row i of sequence b at page table[b][(P_b + i) / page_size], row
+ * (P_b + i) % page_size.  status[b] = 1 (and nothing appended) when the
+ * rows would pass `capacity` rows (max_pages * page_size for a paged cache,
+ * the row stride for a contiguous one), else 0.
+ */
+int svo_kv_append(const float *k_rows, const float *v_rows, int src_stride, const int32_t *n_append,
+                  int32_t *prefix_lens, int batch, int capacity, int Hkv, int d, double theta,
+                  double *k_out, double *v_out, int32_t *status) {
+    if (batch < 0 || src_stride < 1 || Hkv < 1 || d < 2 || (d & 1) || capacity < 0) return SVO_BAD_ARG;
+    for (int b = 0; b < batch; ++b) {
+        const int n = n_append[b], P = prefix_lens[b];
+        if (n < 0 || n > src_stride || P < 0) return SVO_BAD_ARG;
+        if ((long long)P + n > capacity) { status[b] = 1; continue; }
+        status[b] = 0;
+        for (int i = 0; i < n; ++i) {
+            const size_t row = ((size_t)b * src_stride + i) * Hkv * d;
+            for (int e = 0; e < Hkv * d; ++e) {
+                k_out[row + e] = (double)k_rows[row + e];
+                v_out[row + e] = (double)v_rows[row + e];
+            }
+            if (theta > 0) {
+                const double pos = (double)P + (double)i;
+                svo_rope(k_out + row, 1, Hkv, d, &pos, theta);
+            }
+        }
+        prefix_lens[b] = P + n;
+    }
+    return SVO_OK;
 }

@@ -804,3 +804,156 @@ def all_pins(o):
     all_coupled_pins(o)
     all_route_pins(o)
     all_copies_pins(o)
+    all_cache_pins(o)
+
+
+# ---------------------------------------------------------------- paged cache, commit, append
+def _paged_from_contiguous(cache, page_size, n_pages, perm):
+    """Page a contiguous [Hkv][P][d] cache by reshaping it into page blocks:
+    block k (rows k*ps .. k*ps+ps-1) goes to page perm[k]; other pages hold NaN."""
+    Hkv, P, d = cache.shape
+    npg = -(-P // page_size)
+    padded = np.full((Hkv, npg * page_size, d), np.nan, np.float32)
+    padded[:, :P] = cache
+    blocks = padded.reshape(Hkv, npg, page_size, d).transpose(1, 0, 2, 3)
+    pages = np.full((n_pages, Hkv, page_size, d), np.nan, np.float32)
+    pages[perm[:npg]] = blocks
+    return pages
+
+
+def pin_gather_roundtrip(o):
+    """Gathering a cache paged by a reshape into page blocks gives it back."""
+    r = np.random.default_rng(110)
+    for P, ps in ((13, 4), (16, 4), (1, 8), (0, 4), (9, 1)):
+        cache = r.standard_normal((3, P, 5)).astype(np.float32)
+        n_pages = -(-P // ps) + 3
+        perm = r.permutation(n_pages).astype(np.int32)
+        pages = _paged_from_contiguous(cache, ps, n_pages, perm)
+        g = o.gather_prefix(pages, perm, P, ps)
+        assert np.array_equal(g, cache), (P, ps)
+
+
+def pin_paged_attention_lengths(o, theta=1e4):
+    """Per-sequence prompt lengths over a paged cache: each sequence equals the
+    one-sequence attention over its own P_b prompt rows; rows past P_b (NaN in
+    the pages) are never read."""
+    r = np.random.default_rng(111)
+    B, Hq, Hkv, d, ps = 3, 4, 2, 8, 4
+    lens = np.array([10, 0, 7], np.int32)
+    Pmax = 12
+    n_pages = 3 * (Pmax // ps) + 1
+    perm = r.permutation(n_pages).astype(np.int32)
+    table = perm[:3 * (Pmax // ps)].reshape(3, Pmax // ps)
+    kc = r.standard_normal((3, Hkv, Pmax, d)).astype(np.float32)
+    vc = r.standard_normal((3, Hkv, Pmax, d)).astype(np.float32)
+    kp = np.full((n_pages, Hkv, ps, d), np.nan, np.float32)
+    vp = np.full((n_pages, Hkv, ps, d), np.nan, np.float32)
+    for b in range(3):
+        for k in range(-(-int(lens[b]) // ps)):
+            rows = slice(k * ps, min((k + 1) * ps, int(lens[b])))
+            n = rows.stop - rows.start
+            kp[table[b, k], :, :n] = kc[b][:, rows]
+            vp[table[b, k], :, :n] = vc[b][:, rows]
+    q = r.standard_normal((3, 2 * B, Hq, d)).astype(np.float32)
+    kn = r.standard_normal((3, 2 * B, Hkv, d)).astype(np.float32)
+    vn = r.standard_normal((3, 2 * B, Hkv, d)).astype(np.float32)
+    tau = np.stack([r.permutation(B) + 1 for _ in range(3)]).astype(np.int32)
+    out = o.attention_paged(q, kn, vn, kp, vp, table, lens, tau, ps, theta)
+    assert np.isfinite(out).all()
+    for b in range(3):
+        P = int(lens[b])
+        ref = o.attention(q[b], kn[b], vn[b], kc[b][:, :P], vc[b][:, :P], tau[b], theta)
+        assert np.array_equal(out[b], ref), b
+
+
+def pin_commit_golden(o):
+    g = json.load(open(os.path.join(GOLDEN, "commit_tiny.json")))
+    bt, rem, state, napp = o.commit(np.array(g["out_tokens"], np.int32), np.array(g["block_before"], np.int32),
+                                    g["gamma"])
+    assert bt.tolist() == g["block_after"]
+    assert rem.tolist() == g["remaining"]
+    assert state.tolist() == g["state"]
+    assert napp.tolist() == g["n_append"]
+
+
+def pin_commit_invariants(o):
+    """Committed slots take the committed token, other slots keep theirs; R is
+    the number of masked slots left; the state is decided by R against gamma at
+    every boundary (R = 0, gamma - 1, gamma)."""
+    r = np.random.default_rng(112)
+    B, gamma, n = 8, 4, 400
+    before = np.where(r.random((n, B)) < 0.5, r.integers(0, 50, (n, B)), -1).astype(np.int32)
+    out = np.where(r.random((n, B)) < 0.3, r.integers(0, 50, (n, B)), -1).astype(np.int32)
+    bt, rem, state, napp = o.commit(out, before, gamma)
+    for b in range(n):
+        for k in range(B):
+            assert bt[b, k] == (out[b, k] if out[b, k] >= 0 else before[b, k])
+        R = int((bt[b] == -1).sum())
+        assert rem[b] == R
+        assert state[b] == {True: 2, False: 1 if R < gamma else 0}[R == 0]
+        assert napp[b] == (B if R == 0 else 0)
+    seen = {int(x) for x in rem}
+    assert {0, gamma - 1, gamma} <= seen, seen
+
+
+def pin_append_roundtrip(o):
+    """Appending n rows at P_b and gathering P_b + n rows gives the old prompt
+    followed by the rows (theta = 0: stored as given); nothing else changes;
+    an append that would pass the capacity changes nothing; one that fits
+    exactly is made."""
+    r = np.random.default_rng(113)
+    Hkv, d, ps, mp, n_pages, S = 2, 4, 4, 4, 16, 6
+    table = r.permutation(n_pages)[:3 * mp].reshape(3, mp).astype(np.int32)
+    kp = r.standard_normal((n_pages, Hkv, ps, d)).astype(np.float32)
+    vp = r.standard_normal((n_pages, Hkv, ps, d)).astype(np.float32)
+    lens = np.array([5, 10, 16], np.int32)       # capacity 16: the third is full
+    nap = np.array([6, 6, 1], np.int32)          # 10 + 6 = 16 fits exactly; 16 + 1 does not
+    kr = r.standard_normal((3, S, Hkv, d)).astype(np.float32)
+    vr = r.standard_normal((3, S, Hkv, d)).astype(np.float32)
+    kp2, vp2, lens2, st = o.kv_append(kr, vr, nap, kp, vp, table, lens, ps, 0.0, round_bf16=False)
+    assert st.tolist() == [0, 0, 1]
+    assert lens2.tolist() == [11, 16, 16]
+    changed = 0
+    for b in range(3):
+        P, P2 = int(lens[b]), int(lens2[b])
+        for pages, pages2, rows in ((kp, kp2, kr), (vp, vp2, vr)):
+            g0 = o.gather_prefix(pages, table[b], P, ps)
+            g1 = o.gather_prefix(pages2, table[b], P2, ps)
+            assert np.array_equal(g1[:, :P], g0)
+            assert np.array_equal(g1[:, P:P2], rows[b][:P2 - P].transpose(1, 0, 2))
+        changed += (P2 - P) * Hkv * d
+    assert int((kp2 != kp).sum()) == changed and int((vp2 != vp).sum()) == changed
+
+
+def pin_append_rotation(o):
+    """With theta > 0 an appended key is rotated at its position P_b + i: the
+    unit vector on dims (i, i + d/2) becomes (cos, sin) of P_b + i times the
+    pair's frequency theta^(-2i/d); stored rounded to bfloat16 (contiguous
+    cache, row stride 12)."""
+    theta, d, S = 100.0, 4, 3
+    lens = np.array([0, 7], np.int32)
+    for i in range(d // 2):
+        kr = np.zeros((2, S, 1, d), np.float32)
+        kr[:, :, 0, i] = 1.0
+        vr = np.zeros_like(kr)
+        kc = np.zeros((2, 1, 12, d), np.float32)
+        kc2, _, lens2, st = o.kv_append(kr, vr, np.array([3, 3], np.int32), kc, kc.copy(), None, lens, 12, theta)
+        assert st.tolist() == [0, 0] and lens2.tolist() == [3, 10]
+        w = theta ** (-2.0 * i / d)
+        for b in range(2):
+            for j in range(3):
+                p = lens[b] + j
+                got = kc2[b, 0, p]
+                want = np.zeros(d)
+                want[i], want[i + d // 2] = np.cos(p * w), np.sin(p * w)
+                ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+                assert (np.abs(got - want) <= ulp + 1e-30).all(), (i, b, j, got, want)
+
+
+def all_cache_pins(o):
+    pin_gather_roundtrip(o)
+    pin_paged_attention_lengths(o)
+    pin_commit_golden(o)
+    pin_commit_invariants(o)
+    pin_append_roundtrip(o)
+    pin_append_rotation(o)

@@ -53,6 +53,14 @@ MUTANTS = [
     ("route second entry not tracked", "else if (x > p2) p2 = x;", ";"),
     ("copies see earlier copies", "(uint8_t)(j < P || (j - P) / L == i / L);", "(uint8_t)(j < P || (j - P) / L <= i / L);"),
     ("copies indexed by position", "(uint8_t)(j < P || (j - P) / L == i / L);", "(uint8_t)(j < P || (j - P) % L == i % L);"),
+    ("gather page from the row in page", "const int pg = table_row[j / page_size];", "const int pg = table_row[j % page_size];"),
+    ("gather row from the page index", "j % page_size) * d, sizeof(float) * d);", "j / page_size) * d, sizeof(float) * d);"),
+    ("commit skips token 0", "if (out_tokens[i] >= 0) block_tokens[i] = out_tokens[i];", "if (out_tokens[i] > 0) block_tokens[i] = out_tokens[i];"),
+    ("commit fallback at R == gamma", "state[b] = (R == 0) ? 2 : (R < gamma ? 1 : 0);", "state[b] = (R == 0) ? 2 : (R <= gamma ? 1 : 0);"),
+    ("commit appends unfinished blocks", "n_append[b] = (R == 0) ? B : 0;", "n_append[b] = B - R;"),
+    ("append rotates at the row index", "const double pos = (double)P + (double)i;", "const double pos = (double)i;"),
+    ("append leaves the length", "prefix_lens[b] = P + n;", "prefix_lens[b] = P;"),
+    ("append refuses an exact fit", "if ((long long)P + n > capacity) { status[b] = 1; continue; }", "if ((long long)P + n >= capacity) { status[b] = 1; continue; }"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

@@ -141,3 +141,27 @@ def test_copies_single_textbook(o):
 
 def test_copies_decompose(o):
     pins.pin_copies_decompose(o)
+
+
+def test_gather_roundtrip(o):
+    pins.pin_gather_roundtrip(o)
+
+
+def test_paged_attention_lengths(o):
+    pins.pin_paged_attention_lengths(o)
+
+
+def test_commit_golden(o):
+    pins.pin_commit_golden(o)
+
+
+def test_commit_invariants(o):
+    pins.pin_commit_invariants(o)
+
+
+def test_append_roundtrip(o):
+    pins.pin_append_roundtrip(o)
+
+
+def test_append_rotation(o):
+    pins.pin_append_rotation(o)

@@ -61,6 +61,15 @@ def load(path: str | None = None):
     lib.spec_verify_attn_copies_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
     lib.spec_verify_attn_copies.restype = I
     lib.spec_verify_attn_copies.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, I, D, F, V, SZ, V]
+    lib.spec_verify_attn_paged_workspace_size.restype = SZ
+    lib.spec_verify_attn_paged_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.spec_verify_attn_paged.restype = I
+    lib.spec_verify_attn_paged.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, I, I, I, D, F, V,
+                                           SZ, V]
+    lib.spec_verify_commit.restype = I
+    lib.spec_verify_commit.argtypes = [V, V, I, I, I, V, V, V, V]
+    lib.spec_verify_kv_append.restype = I
+    lib.spec_verify_kv_append.argtypes = [V, V, I, V, V, V, V, V, V, I, I, I, I, I, I, I, D, V]
     lib.spec_verify_route_workspace_size.restype = SZ
     lib.spec_verify_route_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_route.restype = I
@@ -168,3 +177,33 @@ def spec_verify_attn_copies(q, k_new, v_new, k_cache, v_cache, out, dtype, batch
                                           dtype, batch, block, n_copies, prefix_len, n_qh, n_kvh, head_dim,
                                           float(rope_theta), float(softmax_scale), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream)))
+
+
+def spec_verify_attn_paged_workspace_size(dtype, batch, block, n_copies, max_prefix, n_qh, n_kvh, head_dim) -> int:
+    return int(load().spec_verify_attn_paged_workspace_size(dtype, batch, block, n_copies, max_prefix, n_qh, n_kvh,
+                                                            head_dim))
+
+
+def spec_verify_attn_paged(q, k_new, v_new, k_pages, v_pages, block_table, prefix_lens, tau, out, dtype, batch,
+                           block, n_copies, max_prefix, page_size, max_pages, n_pages, n_qh, n_kvh, head_dim,
+                           rope_theta, softmax_scale, workspace, workspace_bytes, stream=None) -> None:
+    _check(load().spec_verify_attn_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                         _ptr(block_table), _ptr(prefix_lens), _ptr(tau), _ptr(out), dtype, batch,
+                                         block, n_copies, max_prefix, page_size, max_pages, n_pages, n_qh, n_kvh,
+                                         head_dim, float(rope_theta), float(softmax_scale), _ptr(workspace),
+                                         int(workspace_bytes), _stream(stream)))
+
+
+def spec_verify_commit(out_tokens, block_tokens, batch, block, gamma, remaining, state, n_append,
+                       stream=None) -> None:
+    _check(load().spec_verify_commit(_ptr(out_tokens), _ptr(block_tokens), batch, block, gamma, _ptr(remaining),
+                                     _ptr(state), _ptr(n_append), _stream(stream)))
+
+
+def spec_verify_kv_append(k_rows, v_rows, src_stride, n_append, k_pages, v_pages, block_table, prefix_lens, status,
+                          dtype, batch, page_size, max_pages, n_pages, n_kvh, head_dim, rope_theta,
+                          stream=None) -> None:
+    _check(load().spec_verify_kv_append(_ptr(k_rows), _ptr(v_rows), src_stride, _ptr(n_append), _ptr(k_pages),
+                                        _ptr(v_pages), _ptr(block_table), _ptr(prefix_lens), _ptr(status), dtype,
+                                        batch, page_size, max_pages, n_pages, n_kvh, head_dim, float(rope_theta),
+                                        _stream(stream)))

@@ -124,6 +124,91 @@ int spec_verify_attn_copies(const void *q, const void *k_new, const void *v_new,
                                       workspace, (hipStream_t)stream));
 }
 
+namespace {
+// the response layout of the paged call: n_copies == 0 is the paired layout
+int check_paged(int dtype, int batch, int block, int n_copies, int n_qh, int n_kvh, int head_dim, int max_prefix) {
+    if (dtype != SV_BF16) return SV_E_UNSUPPORTED;
+    if (n_copies < 0) return SV_E_SHAPE;
+    return n_copies == 0 ? check_heads(dtype, batch, block, n_qh, n_kvh, head_dim, max_prefix)
+                         : check_copies(dtype, batch, block, n_copies, n_qh, n_kvh, head_dim, max_prefix);
+}
+
+sv::AttnShape paged_shape(int dtype, int batch, int block, int n_copies, int max_prefix, int n_qh, int n_kvh,
+                          int head_dim) {
+    return sv::AttnShape{dtype, batch, block, max_prefix, n_qh, n_kvh, head_dim,
+                         n_copies == 0 ? 2 * block : n_copies * block, n_copies == 0 ? 0 : 1};
+}
+}  // namespace
+
+size_t spec_verify_attn_paged_workspace_size(int dtype, int batch, int block, int n_copies, int max_prefix,
+                                             int n_qh, int n_kvh, int head_dim) {
+    if (check_paged(dtype, batch, block, n_copies, n_qh, n_kvh, head_dim, max_prefix)) return 0;
+    return sv::attn_plan(paged_shape(dtype, batch, block, n_copies, max_prefix, n_qh, n_kvh, head_dim)).ws_total;
+}
+
+int spec_verify_attn_paged(const void *q, const void *k_new, const void *v_new, const void *k_pages,
+                           const void *v_pages, const int32_t *block_table, const int32_t *prefix_lens,
+                           const int32_t *tau, void *out, int dtype, int batch, int block, int n_copies,
+                           int max_prefix, int page_size, int max_pages, int n_pages, int n_qh, int n_kvh,
+                           int head_dim, double rope_theta, float softmax_scale, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    int rc = check_paged(dtype, batch, block, n_copies, n_qh, n_kvh, head_dim, max_prefix);
+    if (rc) return rc;
+    if (block_table) {
+        if (page_size < 64 || page_size % 64 != 0 || max_pages < 1 || n_pages < 1) return SV_E_SHAPE;
+        if ((long long)max_pages * page_size < max_prefix) return SV_E_SHAPE;
+        if ((long long)batch * max_pages > (1ll << 31) - 1) return SV_E_SHAPE;
+    } else {
+        if (page_size == 0) page_size = max_prefix;
+        if (page_size < max_prefix) return SV_E_SHAPE;
+    }
+    if (!q || !k_new || !v_new || !out || (n_copies == 0 && !tau)) return SV_E_NULL;
+    if (max_prefix > 0 && (!k_pages || !v_pages)) return SV_E_NULL;
+    if (!isfinite(rope_theta) || !isfinite(softmax_scale)) return SV_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return SV_E_ALIGN;
+    if (max_prefix > 0 && (!aligned16(k_pages) || !aligned16(v_pages))) return SV_E_ALIGN;
+    const sv::AttnShape s = paged_shape(dtype, batch, block, n_copies, max_prefix, n_qh, n_kvh, head_dim);
+    const sv::AttnPlan p = sv::attn_plan(s);
+    if (p.n_split > 1 && (!workspace || workspace_bytes < p.ws_total)) return SV_E_WORKSPACE;
+    if (p.n_split > 1 && !aligned16(workspace)) return SV_E_ALIGN;
+    sv::CacheView cv;
+    cv.prefix_lens = prefix_lens;
+    cv.block_table = block_table;
+    cv.page_size = page_size;
+    cv.max_pages = block_table ? max_pages : 0;
+    cv.n_pages = block_table ? n_pages : 0;
+    const float scale = softmax_scale > 0 ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+    return map_launch(sv::launch_attn(s, p, q, k_new, v_new, k_pages, v_pages, n_copies == 0 ? tau : nullptr, out,
+                                      rope_theta, scale, workspace, (hipStream_t)stream, cv));
+}
+
+int spec_verify_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,
+                       int32_t *remaining, int32_t *state, int32_t *n_append, void *stream) {
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block) return SV_E_SHAPE;
+    if ((long long)batch * block > (1ll << 31) - 1) return SV_E_SHAPE;
+    if (!out_tokens || !block_tokens || !remaining || !state || !n_append) return SV_E_NULL;
+    return map_launch(sv::launch_commit(out_tokens, block_tokens, batch, block, gamma, remaining, state, n_append,
+                                        (hipStream_t)stream));
+}
+
+int spec_verify_kv_append(const void *k_rows, const void *v_rows, int src_stride, const int32_t *n_append,
+                          void *k_pages, void *v_pages, const int32_t *block_table, int32_t *prefix_lens,
+                          int32_t *status, int dtype, int batch, int page_size, int max_pages, int n_pages,
+                          int n_kvh, int head_dim, double rope_theta, void *stream) {
+    if (dtype != SV_BF16) return SV_E_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return SV_E_UNSUPPORTED;
+    if (batch < 1 || src_stride < 1 || n_kvh < 1 || page_size < 1) return SV_E_SHAPE;
+    if ((long long)batch * n_kvh > (1ll << 31) - 1) return SV_E_SHAPE;
+    if (block_table && (max_pages < 1 || n_pages < 1)) return SV_E_SHAPE;
+    if (!isfinite(rope_theta)) return SV_E_SHAPE;
+    if (!k_rows || !v_rows || !n_append || !k_pages || !v_pages || !prefix_lens) return SV_E_NULL;
+    if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(k_pages) || !aligned16(v_pages)) return SV_E_ALIGN;
+    return map_launch(sv::launch_append(k_rows, v_rows, src_stride, n_append, k_pages, v_pages, block_table,
+                                        prefix_lens, status, batch, page_size, block_table ? max_pages : 1,
+                                        block_table ? n_pages : batch, n_kvh, head_dim, rope_theta,
+                                        (hipStream_t)stream));
+}
+
 size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))

@@ -124,18 +124,38 @@ struct BfArgs {
     float2 *ws_ml;  // [split][batch][2B][Hq] (running max in log2 units, sum)
     int batch, block, prefix, n_qh, n_kvh, n_rb, n_split, tiles_per_split, n_tiles;
     int n_resp;  // response rows (and keys) per sequence: 2B, or copies * block
+    // prompt cache: row j of (sequence b, kv head) lives in page
+    // block_table[b][j / page_size] at row j % page_size, pages laid out
+    // [page][kv head][page_size][D]; without a table the page is b and
+    // page_size is the row stride of a contiguous [batch][kv head][stride][D]
+    // cache.  prefix_lens (optional) gives each sequence its own prompt
+    // length; `prefix` is then the longest.
+    const int32_t *prefix_lens, *block_table;
+    int page_size, max_pages, n_pages;
     int use_rope;
     double log2_theta;
     float scale_log2;  // softmax scale * log2(e)
 };
 
+// A wave-uniform read of a table the kernel never writes, through the
+// constant address space, so that it is a scalar load (waited on by lgkmcnt):
+// a vector load here would make the compiler wait on vmcnt, which also counts
+// the direct tile loads in flight.
+__device__ __forceinline__ int32_t uniform_ld(const int32_t *p, size_t i) {
+    return *((const __attribute__((address_space(4))) int32_t *)(uintptr_t)p + i);
+}
+
+// Element offset of prompt row j of (b, kvh) in the cache.  Called with
+// wave-uniform arguments only.  Page ids outside [0, n_pages) are clamped (a
+// bad table gives wrong rows, never an access outside the pages).
 template <int D>
-__device__ __forceinline__ const uint16_t *key_row(const BfArgs &a, const uint16_t *cache,
-                                                   const uint16_t *fresh, int b, int kvh, int j) {
-    const int R = a.n_resp;
-    if (j >= a.prefix + R) j = a.prefix + R - 1;  // padding rows of the last tile: any valid row
-    if (j < a.prefix) return cache + (((size_t)b * a.n_kvh + kvh) * a.prefix + j) * D;
-    return fresh + (((size_t)b * R + (j - a.prefix)) * a.n_kvh + kvh) * D;
+__device__ __forceinline__ size_t cache_off(const BfArgs &a, int b, int kvh, int j) {
+    if (a.block_table) {
+        int pg = uniform_ld(a.block_table, (size_t)b * a.max_pages + j / a.page_size);
+        pg = min(max(pg, 0), a.n_pages - 1);
+        return (((size_t)pg * a.n_kvh + kvh) * a.page_size + j % a.page_size) * D;
+    }
+    return (((size_t)b * a.n_kvh + kvh) * a.page_size + j) * D;
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -220,25 +240,36 @@ __device__ __forceinline__ LoadOffs<D, NW> load_offsets(int w, int lane) {
     return o;
 }
 
-// Tiles that lie wholly inside the prompt take the fast path: the cache rows
-// of one (sequence, kv head) are contiguous, so the source is a uniform tile
-// base plus this lane's row/chunk offset.  Other tiles go through key_row;
-// there, keys at or past `jend` (the end of this workgroup's key range) read
-// the row jend - 1 instead: such rows are never used, and re-reading one row
-// keeps them in cache.
+// Tiles that lie wholly inside the prompt take the fast path: a tile's rows
+// are contiguous in one page (pages hold whole tiles; a contiguous cache is
+// one page), so the source is a uniform tile base plus this lane's
+// row/chunk offset.  Other tiles pick per row between the prompt (the same
+// page: all prompt rows a tile holds lie in the page of its first row) and
+// the response keys; keys at or past `jend` (the end of this workgroup's
+// key range) read the row jend - 1 instead: such rows are never used, and
+// re-reading one row keeps them in cache.
 template <int D, int NW, bool IS_V, bool NT>
 __device__ __forceinline__ void load_tile(const BfArgs &a, const uint16_t *cache, const uint16_t *fresh,
                                           int b, int kvh, int base, int jend, char *lds_tile, int w, int lane) {
     using T = Tile<D, IS_V>;
-    const bool fast = base + kTileKeys <= a.prefix;  // uniform
-    const uint16_t *tile = fast ? cache + (((size_t)b * a.n_kvh + kvh) * a.prefix + base) * D : nullptr;
+    const int P = a.prefix, R = a.n_resp;
+    const bool fast = base + kTileKeys <= P;  // uniform
+    // first row this tile reads (a tile past the end reads row jend - 1 only)
+    const int jref = min(base, jend - 1);
+    const uint16_t *tile = (jref < P) ? cache + cache_off<D>(a, b, kvh, jref) : cache;  // row jref
 #pragma unroll
     for (int i = 0; i < T::LOADS / NW; ++i) {
         const int r0 = (w + NW * i) * T::ROWS_PER_LOAD;
         const int row = r0 + lane / T::NCH, pc = lane % T::NCH;
         const int q = pc ^ T::swz(row);
-        const uint16_t *src = fast ? tile + row * D + q * 8
-                                   : key_row<D>(a, cache, fresh, b, kvh, min(base + row, jend - 1)) + q * 8;
+        const uint16_t *src;
+        if (fast) {
+            src = tile + row * D + q * 8;
+        } else {
+            const int j = min(base + row, jend - 1);
+            src = (j < P ? tile + (size_t)(j - jref) * D
+                         : fresh + (((size_t)b * R + (j - P)) * a.n_kvh + kvh) * D) + q * 8;
+        }
         direct_load16<NT>(src, lds_tile + r0 * T::ROW_BYTES);
     }
 }
@@ -364,8 +395,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
                                           char *__restrict__ kn, char *__restrict__ vn,
                                           const float2 *__restrict__ cs, const int *__restrict__ klab,
-                                          const char *v_stage0, const LoadOffs<D, NW> &ldo,
-                                          const uint16_t *k_unit, const uint16_t *v_unit) {
+                                          const char *v_stage0, const LoadOffs<D, NW> &ldo, size_t unit_off) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
@@ -402,7 +432,11 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     constexpr bool kNt = MASK == 0;         // see direct_load16
     const int nb = (t0 + it + 2) * kTileKeys;
     const bool prompt_refill = nb + kTileKeys <= P;  // uniform
-    const uint16_t *kb_src = k_unit + (size_t)nb * D, *vb_src = v_unit + (size_t)nb * D;
+    // element offset of the refill tile (contiguous cache: this unit's base
+    // plus the tile's rows, without the general page arithmetic)
+    size_t nb_off = 0;
+    if (prompt_refill) nb_off = a.block_table ? cache_off<D>(a, b, kvh, nb) : unit_off + (size_t)nb * D;
+    const uint16_t *kb_src = a.k_cache + nb_off, *vb_src = a.v_cache + nb_off;
     const uint32_t kn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)kn, vn_lds = (uint32_t)(uintptr_t)(SV_LDS char *)vn;
     auto refill = [&](int i) {  // load i of 2 * NL: K loads first, then V
         if (i < NL) direct_load16_s<kNt>(kb_src, ldo.k[i], kn_lds + ldo.lds[i]);
@@ -630,9 +664,25 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     rest /= a.n_rb;
     const int kvh = rest % a.n_kvh;
     const int b = rest / a.n_kvh;
+    // this sequence's prompt length, and its key tiles
+    if (a.prefix_lens) a.prefix = min(max(uniform_ld(a.prefix_lens, b), 0), a.prefix);
+    const int n_tiles = (a.prefix + R2 + kTileKeys - 1) / kTileKeys;
     const int t0 = split * a.tiles_per_split;
-    const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
+    const int t1 = min(n_tiles, t0 + a.tiles_per_split);
     const int nt = t1 - t0;
+    if (nt <= 0) {
+        // a split past this sequence's keys: an empty partial (the merge
+        // skips it without reading its output rows)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int rho = rb * ROWS_B + w * ROWS_W + qb * 32 + l32;
+            if (rho < R && h == 0) {
+                const size_t row = ((size_t)b * R2 + rho % R2) * a.n_qh + kvh * g + rho / R2;
+                a.ws_ml[(size_t)split * a.batch * R2 * a.n_qh + row] = make_float2(-INFINITY, 0.f);
+            }
+        }
+        return;
+    }
 
     // ---- tau (lane k of every wave holds tau[k]) and this lane's query rows:
     // their loads go out before the tiles' so that waiting for them does not
@@ -682,10 +732,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     }
     const LdsOffs<D> offs = lds_offsets<D>(lane, v_st0);
     const LoadOffs<D, NW> ldo = load_offsets<D, NW>(w, lane);
-    // K/V cache rows of this (sequence, kv head); only dereferenced for
-    // tiles that lie wholly inside the prompt
-    const size_t unit_off = ((size_t)b * a.n_kvh + kvh) * a.prefix * D;
-    const uint16_t *k_unit = a.k_cache + unit_off, *v_unit = a.v_cache + unit_off;
+    const size_t unit_off = ((size_t)b * a.n_kvh + kvh) * a.page_size * D;  // contiguous cache only
     const bool wave_active = (rb * ROWS_B + w * ROWS_W) < R;
 
     RowState<D, QB> st;
@@ -701,13 +748,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 
     for (int it = 0; it < nt; it += 3) {
         tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
-                             cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
+                             cs_lds, klab_lds, v_st0, ldo, unit_off);
         if (it + 1 < nt)
             tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
-                                 v_st0, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
+                                 v_st0, cs_lds, klab_lds, v_st0, ldo, unit_off);
         if (it + 2 < nt)
             tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
-                                 v_st1, cs_lds, klab_lds, v_st0, ldo, k_unit, v_unit);
+                                 v_st1, cs_lds, klab_lds, v_st0, ldo, unit_off);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 
@@ -768,8 +815,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
 #pragma unroll 8
     for (int s = 0; s < n_split; ++s) {
         const float2 ml = ws_ml[s * rows_total + row];
+        if (ml.x == -INFINITY) continue;  // no visible key in this split (or an empty split)
         const float4 o = *reinterpret_cast<const float4 *>(ws_o + (s * rows_total + row) * d + e);
-        const float f = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        const float f = __builtin_amdgcn_exp2f(ml.x - M);
         den += f * ml.y;
         num.x += f * o.x;
         num.y += f * o.y;
@@ -919,7 +967,7 @@ hipError_t launch_rope(const void *q_in, const void *k_in, void *q_out, void *k_
 hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, const void *k_new,
                        const void *v_new, const void *k_cache, const void *v_cache,
                        const int32_t *tau, void *out, double theta, float scale, void *ws,
-                       hipStream_t st) {
+                       hipStream_t st, const CacheView &cv) {
     const int R2 = s.n_resp;
     if (s.dtype == 1) {
         BfArgs a{};
@@ -942,6 +990,11 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.tiles_per_split = p.tiles_per_split;
         a.n_tiles = p.n_tiles;
         a.n_resp = s.n_resp;
+        a.prefix_lens = cv.prefix_lens;
+        a.block_table = cv.block_table;
+        a.page_size = cv.page_size > 0 ? cv.page_size : s.prefix;
+        a.max_pages = cv.max_pages;
+        a.n_pages = cv.n_pages;
         a.use_rope = theta > 0 ? 1 : 0;
         a.log2_theta = theta > 0 ? log2(theta) : 0.0;
         a.scale_log2 = scale * kLog2e;

@@ -40,10 +40,21 @@ hipError_t launch_rope(const void *q_in, const void *k_in, void *q_out, void *k_
                        int batch, int block, int n_qh, int n_kvh, int head_dim, int prefix,
                        double theta, hipStream_t st);
 
+// Addressing of the prompt K/V cache.  Default: contiguous
+// [batch][n_kvh][prefix][d], every sequence with `prefix` prompt keys.  With
+// a block table: pages [n_pages][n_kvh][page_size][d] (page_size a multiple
+// of 64), row j of sequence b in page block_table[b * max_pages + j /
+// page_size].  Without a table and page_size > 0: contiguous with row stride
+// page_size.  prefix_lens: per-sequence prompt lengths (<= prefix).
+struct CacheView {
+    const int32_t *prefix_lens = nullptr, *block_table = nullptr;
+    int page_size = 0, max_pages = 0, n_pages = 0;
+};
+
 hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, const void *k_new,
                        const void *v_new, const void *k_cache, const void *v_cache,
                        const int32_t *tau, void *out, double theta, float scale, void *ws,
-                       hipStream_t st);
+                       hipStream_t st, const CacheView &cv = CacheView());
 
 struct AcceptPlan {
     int rows;        // batch * block logits rows
@@ -85,5 +96,13 @@ RoutePlan route_plan(int batch, int block, int gamma, int64_t vocab);
 hipError_t launch_route(const RoutePlan &p, const float *probs, const int32_t *tau, int batch, int block,
                         int gamma, int64_t vocab, int estimator, double param, float *khat, float *alpha_hat,
                         void *ws, hipStream_t st);
+
+hipError_t launch_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,
+                         int32_t *remaining, int32_t *state, int32_t *n_append, hipStream_t st);
+
+hipError_t launch_append(const void *k_rows, const void *v_rows, int src_stride, const int32_t *n_append,
+                         void *k_pages, void *v_pages, const int32_t *block_table, int32_t *prefix_lens,
+                         int32_t *status, int batch, int page_size, int max_pages, int n_pages, int n_kvh,
+                         int head_dim, double theta, hipStream_t st);
 
 }  // namespace sv

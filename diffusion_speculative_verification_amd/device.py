@@ -67,6 +67,26 @@ class StepBuffers:
                                                           c.n_qh, c.n_kvh, c.head_dim)
             self.copies_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.copies_ws_bytes = n
+        if "paged" in parts:
+            self.k_pages = up(inputs["k_pages"], dt)
+            self.v_pages = up(inputs["v_pages"], dt)
+            self.block_table = up(inputs["block_table"])
+            self.prefix_lens = up(inputs["prefix_lens"])
+            self.prefix_lens0 = self.prefix_lens.clone()   # lengths before any append
+            self.block_tokens = up(inputs["block_tokens"])
+            self.block_tokens0 = self.block_tokens.clone()
+            self.max_pages = int(inputs["block_table"].shape[1])
+            self.n_pages = int(inputs["k_pages"].shape[0])
+            self.remaining = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.state = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.n_append = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.append_status = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.out_paged = torch.empty_like(self.q_c if "copies" in parts else self.q)
+            nc = c.n_copies if "copies" in parts else 0
+            n = sv.spec_verify_attn_paged_workspace_size(self.dtype_code, c.batch, c.block, nc, c.prefix_len,
+                                                         c.n_qh, c.n_kvh, c.head_dim)
+            self.paged_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.paged_ws_bytes = n
         if "route" in parts:
             if not hasattr(self, "draft_probs"):
                 self.draft_probs = up(inputs["draft_probs"])
@@ -117,6 +137,41 @@ class StepBuffers:
         sv.spec_verify_attn_copies(self.q_c, self.k_new_c, self.v_new_c, self.k_cache, self.v_cache, self.out_c,
                                    self.dtype_code, c.batch, c.block, c.n_copies, c.prefix_len, c.n_qh, c.n_kvh,
                                    c.head_dim, theta, 0.0, self.copies_ws, self.copies_ws_bytes, stream)
+
+    def attn_paged(self, n_copies: int = 0, rope_theta=None, max_prefix=None, stream=None):
+        """Verification attention over the paged prompt cache (paired layout, or
+        n_copies copies of the block), each sequence with its own length (at
+        most max_prefix, default the case's prompt length; the pages have room
+        for one appended block beyond it)."""
+        c = self.case
+        mp = c.prefix_len if max_prefix is None else max_prefix
+        theta = c.theta if rope_theta is None else rope_theta
+        q, kn, vn = (self.q_c, self.k_new_c, self.v_new_c) if n_copies else (self.q, self.k_new, self.v_new)
+        ws, ws_bytes = self.paged_ws, self.paged_ws_bytes
+        if mp != c.prefix_len:
+            ws_bytes = sv.spec_verify_attn_paged_workspace_size(self.dtype_code, c.batch, c.block, n_copies, mp,
+                                                                c.n_qh, c.n_kvh, c.head_dim)
+            if ws_bytes > self.paged_ws.numel():
+                ws = self.paged_ws = _torch().empty(ws_bytes, dtype=_torch().uint8, device=self.device)
+        sv.spec_verify_attn_paged(q, kn, vn, self.k_pages, self.v_pages, self.block_table, self.prefix_lens,
+                                  None if n_copies else self.tau, self.out_paged, self.dtype_code, c.batch, c.block,
+                                  n_copies, mp, c.page_size, self.max_pages, self.n_pages, c.n_qh,
+                                  c.n_kvh, c.head_dim, theta, 0.0, ws, ws_bytes, stream)
+
+    def commit(self, out_tokens, stream=None):
+        """Commit step: the verification's out_tokens into the block."""
+        c = self.case
+        sv.spec_verify_commit(out_tokens, self.block_tokens, c.batch, c.block, c.gamma, self.remaining, self.state,
+                              self.n_append, stream)
+
+    def kv_append(self, k_rows, v_rows, src_stride: int, rope_theta=None, stream=None):
+        """Append each finished block's rows (n_append, as commit left it) to the
+        paged prompt cache and advance the prompt lengths."""
+        c = self.case
+        theta = c.theta if rope_theta is None else rope_theta
+        sv.spec_verify_kv_append(k_rows, v_rows, src_stride, self.n_append, self.k_pages, self.v_pages,
+                                 self.block_table, self.prefix_lens, self.append_status, self.dtype_code, c.batch,
+                                 c.page_size, self.max_pages, self.n_pages, c.n_kvh, c.head_dim, theta, stream)
 
     def route(self, estimator: str, param: float, stream=None):
         """S2D2 verify-routing estimate K of every sequence (margin or entropy)."""

@@ -31,6 +31,11 @@ numpy default_rng(SeedSequence([s, t, b]))):
       positions ("SPOT", 前置知识 "Gumbel-Max 技巧与随机耦合")
   t=11 Q, t=12 K_new, t=13 V_new of the multi-copy layout: [C*B][heads][d]
       iid N(0,1), copy-major (the root and draft states of the block)
+  t=14 per-sequence prompt length (ragged cases): uniform integer in
+      [P/2, P]; otherwise P
+  t=15 (one stream for the batch) the page permutation of a paged cache: the
+      sequences' page tables take consecutive runs of a random permutation of
+      all pages, with one spare page per sequence that no table names
 bf16 cases round Q/K/V and the caches to bf16 (round-to-nearest-even) and keep
 them as float32 arrays holding exactly bf16-representable values.
 
@@ -74,6 +79,8 @@ class Case:
     seed: int = 0
     temperature: float = 1.0  # shared-noise verification (0: greedy)
     n_copies: int = 9          # multi-copy verification: root + 8 draft states
+    page_size: int = 64        # paged prompt cache: rows per page
+    ragged: bool = False       # paged inputs: per-sequence prompt lengths
 
     @property
     def rows(self) -> int:
@@ -260,4 +267,35 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
 
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill_cpl, range(n)))
+    if "paged" in parts:
+        _paged(case, out, seqs)
     return out
+
+
+_PAGE_FILL = 8192.0  # rows no prompt row maps to (bf16-exact; a read of one would show)
+
+
+def _paged(case: Case, out: dict, seqs) -> None:
+    """Paged copy of the prompt caches (made by the "attn" or "copies" part):
+    prefix_lens [n], block_table [n][max_pages] (room for the prompt plus one
+    appended block), k_pages / v_pages [n_pages][Hkv][page_size][d]."""
+    assert "k_cache" in out, "paged inputs page the prompt caches of the attn or copies part"
+    n, P, B, ps = len(seqs), case.prefix_len, case.block, case.page_size
+    assert ps >= 1
+    if case.ragged:
+        lens = np.array([_rng(case, 14, b).integers(P // 2, P + 1) for b in seqs], np.int32)
+    else:
+        lens = np.full(n, P, np.int32)
+    max_pages = max(1, -(-(P + B) // ps))
+    n_pages = n * max_pages + n
+    perm = np.random.default_rng(np.random.SeedSequence([case.seed, 15])).permutation(n_pages).astype(np.int32)
+    table = perm[:n * max_pages].reshape(n, max_pages)
+    shape = (n_pages, case.n_kvh, ps, case.head_dim)
+    kp, vp = np.full(shape, _PAGE_FILL, np.float32), np.full(shape, _PAGE_FILL, np.float32)
+    for i in range(n):
+        for k in range(-(-int(lens[i]) // ps)):
+            j0, j1 = k * ps, min((k + 1) * ps, int(lens[i]))
+            kp[table[i, k], :, :j1 - j0] = out["k_cache"][i][:, j0:j1]
+            vp[table[i, k], :, :j1 - j0] = out["v_cache"][i][:, j0:j1]
+    out["prefix_lens"], out["block_table"], out["k_pages"], out["v_pages"] = lens, table, kp, vp
+    out["block_tokens"] = np.full((n, B), -1, np.int32)  # a fresh block: every slot masked

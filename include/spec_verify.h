@@ -138,6 +138,82 @@ int spec_verify_attn_copies(const void *q, const void *k_new, const void *v_new,
                             int prefix_len, int n_qh, int n_kvh, int head_dim, double rope_theta,
                             float softmax_scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of workspace spec_verify_attn_paged needs for these sizes. */
+size_t spec_verify_attn_paged_workspace_size(int dtype, int batch, int block, int n_copies, int max_prefix,
+                                             int n_qh, int n_kvh, int head_dim);
+
+/*
+ * Verification attention over a paged prompt cache with per-sequence prompt
+ * lengths: spec_verify_attn (n_copies == 0, paired layout, tau required) or
+ * spec_verify_attn_copies (n_copies >= 1, tau ignored) with the prompt K/V
+ * read through a page table.  The pages say the prompt's K/V are cached
+ * ("SimSD: Simple Speculative Decoding in Diffusion Language Models",
+ * 损失函数 / 训练策略) and that finished blocks join that prefix (the
+ * block-diffusion prior, "SPOT", 前置知识); the paging is a storage layout.
+ *   k_pages, v_pages  with block_table: [n_pages][n_kvh][page_size][head_dim]
+ *          bf16 (page_size a multiple of 64); prompt row j of sequence b is
+ *          row j % page_size of page block_table[b * max_pages + j /
+ *          page_size].  Without a table (block_table NULL): contiguous
+ *          [batch][n_kvh][page_size][head_dim], page_size >= max_prefix the
+ *          row stride (0 means max_prefix); max_pages, n_pages ignored.
+ *   block_table [batch][max_pages] int32 page ids; ids outside [0, n_pages)
+ *          are clamped into range (wrong rows, never an access outside the
+ *          pages); max_pages * page_size >= max_prefix.
+ *   prefix_lens [batch] int32 per-sequence prompt lengths, clamped to
+ *          [0, max_prefix]; NULL: every sequence has max_prefix.  Each
+ *          sequence's response rows sit at positions prefix_lens[b] + ...
+ *   Other arguments, layouts and limits as spec_verify_attn /
+ *   spec_verify_attn_copies (q, k_new, v_new, out row-major as there).
+ * dtype SV_BF16 only.  SV_E_SHAPE for inconsistent page sizes.
+ */
+int spec_verify_attn_paged(const void *q, const void *k_new, const void *v_new, const void *k_pages,
+                           const void *v_pages, const int32_t *block_table, const int32_t *prefix_lens,
+                           const int32_t *tau, void *out, int dtype, int batch, int block, int n_copies,
+                           int max_prefix, int page_size, int max_pages, int n_pages, int n_qh, int n_kvh,
+                           int head_dim, double rope_theta, float softmax_scale, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * Commit step after a verification round ("SimSD", 关键设计 4: the accepted
+ * prefix is kept, the first rejected position is resampled in place; a block
+ * with fewer undecoded positions than the draft length is finished by
+ * ordinary target denoising).
+ *   out_tokens   [batch][block] int32: spec_verify_accept's (or
+ *                spec_verify_accept_coupled's) output, the committed token of
+ *                each slot or -1.
+ *   block_tokens [batch][block] int32, in/out: the block, -1 where masked;
+ *                each committed token is written into its slot.
+ *   remaining [batch]: masked slots left (R); state [batch]: 2 = the block is
+ *   finished, 1 = 0 < R < gamma (finish by target denoising), 0 = keep
+ *   speculating; n_append [batch]: block when finished, else 0 (the rows
+ *   spec_verify_kv_append should add).
+ * 1 <= gamma <= block <= 64.  Device pointers, caller-owned.
+ */
+int spec_verify_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,
+                       int32_t *remaining, int32_t *state, int32_t *n_append, void *stream);
+
+/*
+ * Append rows to each sequence's prompt cache (the finished block joins the
+ * cached prefix: "SPOT", 前置知识; "SimSD", 损失函数 / 训练策略).  Sequence b
+ * appends rows 0 .. n_append[b]-1 of k_rows / v_rows [batch][src_stride]
+ * [n_kvh][head_dim] bf16 at positions prefix_lens[b] + i, then
+ * prefix_lens[b] += n_append[b].  With rope_theta > 0 each key is rotated at
+ * its position first (the cache holds rotated keys; rotate-half pairs, as
+ * spec_verify_rope), stored as bf16 rounded to nearest even.  Cache layout,
+ * block_table and page_size as spec_verify_attn_paged (capacity max_pages *
+ * page_size, or the row stride page_size without a table).
+ *   status [batch] (optional): 0 appended (or nothing to append), 1 the rows
+ *   would pass the capacity (nothing written, length unchanged), 2 n_append[b]
+ *   outside [0, src_stride] (nothing written).
+ * n_append and prefix_lens live on the device (n_append as spec_verify_commit
+ * leaves it).  Pages shared by several sequences are the caller's to copy
+ * before an append.  dtype SV_BF16, head_dim 64 or 128.
+ */
+int spec_verify_kv_append(const void *k_rows, const void *v_rows, int src_stride, const int32_t *n_append,
+                          void *k_pages, void *v_pages, const int32_t *block_table, int32_t *prefix_lens,
+                          int32_t *status, int dtype, int batch, int page_size, int max_pages, int n_pages,
+                          int n_kvh, int head_dim, double rope_theta, void *stream);
+
 /* Bytes of workspace spec_verify_accept needs for these sizes. */
 size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab);
 

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -164,6 +164,55 @@ def test_copies_argument_checks(lib):
     assert call(C=33) == sv.SV_E_SHAPE
     assert call(L=65, C=2) == sv.SV_E_SHAPE
     assert call(o=A + 8) == sv.SV_E_ALIGN
+
+
+def test_paged_argument_checks(lib):
+    f = lib.spec_verify_attn_paged
+    ok = dict(q=A, k=A, v=A, kp=A, vp=A, tb=A, pl=A, tau=A, o=A, dt=1, b=2, L=32, C=0, P=2048, ps=64, mp=33, npg=66,
+              hq=32, hkv=8, d=128, th=1e6, sc=0.0, ws=A, wb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["kp"], a["vp"], a["tb"], a["pl"], a["tau"], a["o"], a["dt"], a["b"],
+                 a["L"], a["C"], a["P"], a["ps"], a["mp"], a["npg"], a["hq"], a["hkv"], a["d"], a["th"], a["sc"],
+                 a["ws"], a["wb"], None)
+    assert sv.spec_verify_attn_paged_workspace_size(1, 2, 32, 0, 2048, 32, 8, 128) > 0   # few units: splits
+    assert sv.spec_verify_attn_paged_workspace_size(0, 2, 32, 0, 2048, 32, 8, 128) == 0  # fp32: unsupported
+    assert call(dt=0) == sv.SV_E_UNSUPPORTED
+    assert call(ps=96) == sv.SV_E_SHAPE            # pages must hold whole 64-key tiles
+    assert call(mp=31) == sv.SV_E_SHAPE            # 31 * 64 < 2048
+    assert call(npg=0) == sv.SV_E_SHAPE
+    assert call(C=-1) == sv.SV_E_SHAPE
+    assert call(tb=None, ps=1000) == sv.SV_E_SHAPE   # contiguous stride below the longest prompt
+    assert call(tau=None) == sv.SV_E_NULL
+    assert call(tau=None, C=9, wb=0) == sv.SV_E_WORKSPACE   # copies need no tau (stops before any launch)
+    assert call(kp=None) == sv.SV_E_NULL
+    assert call(o=A + 4) == sv.SV_E_ALIGN
+    assert call(wb=0) == sv.SV_E_WORKSPACE
+
+
+def test_commit_and_append_argument_checks(lib):
+    c = lib.spec_verify_commit
+    assert c(A, A, 4, 32, 33, A, A, A, None) == sv.SV_E_SHAPE      # gamma > block
+    assert c(A, A, 4, 65, 8, A, A, A, None) == sv.SV_E_SHAPE       # block > 64
+    assert c(None, A, 4, 32, 8, A, A, A, None) == sv.SV_E_NULL
+    f = lib.spec_verify_kv_append
+    ok = dict(k=A, v=A, S=64, na=A, kp=A, vp=A, tb=A, pl=A, st=A, dt=1, b=4, ps=64, mp=33, npg=132, hkv=8, d=128,
+              th=1e6)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["k"], a["v"], a["S"], a["na"], a["kp"], a["vp"], a["tb"], a["pl"], a["st"], a["dt"], a["b"],
+                 a["ps"], a["mp"], a["npg"], a["hkv"], a["d"], a["th"], None)
+    assert call(dt=0) == sv.SV_E_UNSUPPORTED
+    assert call(d=96) == sv.SV_E_UNSUPPORTED
+    assert call(S=0) == sv.SV_E_SHAPE
+    assert call(mp=0) == sv.SV_E_SHAPE
+    assert call(th=float("nan")) == sv.SV_E_SHAPE
+    assert call(pl=None) == sv.SV_E_NULL
+    assert call(kp=A + 2) == sv.SV_E_ALIGN
 
 
 def test_rope_argument_checks(lib):

@@ -26,7 +26,12 @@ entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
 verification step instead: attention over C copies of the block (the root
 state and D = C - 1 draft states, spec_verify_attn_copies) followed by
 shared-noise (or, with --verify greedy, greedy) verification of the D draft
-steps; gamma = D.
+steps; gamma = D.  --paged PS keeps the prompt caches in pages of PS rows
+(spec_verify_attn_paged; --ragged gives each sequence its own prompt length)
+and ends each step with the commit step and the cache append of finished
+blocks (spec_verify_commit, spec_verify_kv_append); the prompt lengths and the
+block are restored at the start of every step so that each step does the same
+work.
 """
 from __future__ import annotations
 
@@ -45,24 +50,35 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-def attn_bytes(c, copies: int = 0) -> float:
+def attn_bytes(c, copies: int = 0, prompt_rows=None) -> float:
     """Algorithmic HBM bytes of one attention call: prompt K/V cache, Q,
     response K/V and the output, each read or written once (2B response rows,
-    or copies * B for the multi-copy layout)."""
+    or copies * B for the multi-copy layout).  prompt_rows: the prompt rows of
+    the whole batch (default batch * prefix)."""
     e = 2 if c.dtype == "bf16" else 4
     R = copies * c.block if copies else 2 * c.block
-    return e * (2 * c.batch * c.n_kvh * c.prefix_len * c.head_dim
+    pr = c.batch * c.prefix_len if prompt_rows is None else prompt_rows
+    return e * (2 * c.n_kvh * pr * c.head_dim
                 + c.batch * R * c.n_qh * c.head_dim * 2
                 + 2 * c.batch * R * c.n_kvh * c.head_dim)
 
 
-def attn_flops(c, copies: int = 0) -> float:
+def attn_flops(c, copies: int = 0, prompt_rows=None) -> float:
     """Algorithmic FLOPs: every response row attends to exactly P + B keys
     (QK^T and PV, 2 flops per multiply-add): the paired layout's D rows see
     P + (keys of earlier steps and their own), its mask rows as many, and
     every copy row sees the prompt and its own copy's B keys."""
     R = copies * c.block if copies else 2 * c.block
-    return 4.0 * c.batch * R * c.n_qh * c.head_dim * (c.prefix_len + c.block)
+    pr = c.batch * c.prefix_len if prompt_rows is None else prompt_rows
+    return 4.0 * R * c.n_qh * c.head_dim * (pr + c.batch * c.block)
+
+
+def commit_bytes(c, n_appended: int) -> float:
+    """Algorithmic HBM bytes of the commit step and the append: out_tokens and
+    the block read, the block written, four per-sequence outputs, plus the K
+    and V rows of each appended block read and written once."""
+    e = 2 if c.dtype == "bf16" else 4
+    return c.batch * (c.block * 4 * 3 + 4 * 6) + n_appended * 4 * c.block * c.n_kvh * c.head_dim * e
 
 
 def accept_bytes(c, n_rejecting: int) -> float:
@@ -112,7 +128,7 @@ def measured_traffic(call: str):
 
 
 def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
-                 attn_budget_s=20.0) -> dict:
+                 paged=False, attn_budget_s=20.0) -> dict:
     """The CPU oracle on this host over the same workload (one step).  The
     attention is timed over the first sequences of the batch until
     `attn_budget_s` has passed and scaled to the whole batch."""
@@ -126,7 +142,12 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     t = time.perf_counter()
     n_seq = 0
     for b in range(case.batch):
-        if copies:
+        if paged:
+            sl = slice(b, b + 1)
+            o.attention_paged(inp["q"][sl], inp["k_new"][sl], inp["v_new"][sl], inp["k_pages"], inp["v_pages"],
+                              inp["block_table"][sl], inp["prefix_lens"][sl], inp["tau"][sl], case.page_size,
+                              case.theta)
+        elif copies:
             o.attention_copies(inp["q_c"][b], inp["k_new_c"][b], inp["v_new_c"][b], inp["k_cache"][b],
                                inp["v_cache"][b], copies, case.theta)
         else:
@@ -138,19 +159,28 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     t_attn = (time.perf_counter() - t) * case.batch / n_seq
     t = time.perf_counter()
     if verify == "rejection":
-        o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"], inp["uniforms"],
-                 case.gamma)
+        out_tokens = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
+                              inp["uniforms"], case.gamma)[1]
     else:
-        o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None, inp["coupled_tokens"],
-                         inp["tau"], case.gamma, temperature)
+        out_tokens = o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None,
+                                      inp["coupled_tokens"], inp["tau"], case.gamma, temperature)[1]
     t_acc = time.perf_counter() - t
-    total = t_route + t_attn + t_acc
+    t_commit = 0.0
+    if paged:
+        t = time.perf_counter()
+        n_app = o.commit(out_tokens, inp["block_tokens"], case.gamma)[3]
+        o.kv_append(inp["k_new"], inp["v_new"], n_app, inp["k_pages"], inp["v_pages"], inp["block_table"],
+                    inp["prefix_lens"], case.page_size, case.theta)
+        t_commit = time.perf_counter() - t
+    total = t_route + t_attn + t_acc + t_commit
     attn_what = (f"attention {t_attn:.2f} s" if n_seq == case.batch else
                  f"attention {t_attn:.2f} s (timed on {n_seq} of {case.batch} sequences, scaled)")
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
             "sample": f"one step of the same workload ({case.batch} sequences): "
                       + (f"routing {t_route:.2f} s + " if route != "none" else "") +
-                      f"{attn_what} + accept {t_acc:.2f} s on {threads} OpenMP threads "
+                      f"{attn_what} + accept {t_acc:.2f} s"
+                      + (f" + commit and append {t_commit:.2f} s" if paged else "") +
+                      f" on {threads} OpenMP threads "
                       f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
 
 
@@ -164,6 +194,9 @@ def main():
     ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default=None,
                     help="epilogue: rejection sampling (headline), shared-noise or greedy verification "
                          "(default: rejection; coupled with --copies)")
+    ap.add_argument("--paged", type=int, default=0, metavar="PS",
+                    help="prompt caches in pages of PS rows, plus the commit step and the cache append")
+    ap.add_argument("--ragged", action="store_true", help="with --paged: per-sequence prompt lengths")
     ap.add_argument("--copies", type=int, default=0,
                     help="SPOT multi-copy verification over C copies of the block (root + C-1 draft states)")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
@@ -205,10 +238,18 @@ def main():
                   file=sys.stderr)
             sys.exit(2)
         case = case.with_(n_copies=copies, gamma=copies - 1)
+    paged = args.paged > 0
+    if paged:
+        if copies or args.route != "none" or args.paged % 64:
+            print("--paged takes a page size that is a multiple of 64, without --copies or --route", file=sys.stderr)
+            sys.exit(2)
+        case = case.with_(page_size=args.paged, ragged=args.ragged)
     T = 0.0 if verify == "greedy" else args.temperature
     parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
     if copies:
         parts = ("copies", "coupled")
+    if paged:
+        parts = parts + ("paged",)
     route = args.route
     rparam = args.route_param if args.route_param is not None else (0.05 if route == "margin" else 1.0)
     if verify != "rejection":
@@ -223,8 +264,18 @@ def main():
     def attend(s):
         if copies:
             s.attn_copies()
+        elif paged:
+            s.attn_paged()
         else:
             s.attn()
+
+    def commit(s):
+        s.commit(s.out_tokens if verify == "rejection" else s.cpl_out_tokens)
+        s.kv_append(s.k_new, s.v_new, 2 * case.block)   # a finished block's D rows, positions P_b ..
+        # the next step on this input set starts from the same prompt lengths
+        # and a fresh block (two small device copies, timed with the commit)
+        s.prefix_lens.copy_(s.prefix_lens0)
+        s.block_tokens.copy_(s.block_tokens0)
 
     def epilogue(s):
         if verify == "rejection":
@@ -237,10 +288,12 @@ def main():
             sets[i & 1].route(route, rparam)
         attend(sets[i & 1])
         epilogue(sets[i & 1])
+        if paged:
+            commit(sets[i & 1])
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
@@ -253,10 +306,14 @@ def main():
         ev[i][1].record(stream)
         epilogue(s)
         ev[i][2].record(stream)
+        if paged:
+            commit(s)
+        ev[i][4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    total_ms = ev[0][3].elapsed_time(ev[K - 1][2])
+    total_ms = ev[0][3].elapsed_time(ev[K - 1][4])
+    commit_ms = sum(ev[i][2].elapsed_time(ev[i][4]) for i in range(K)) / K if paged else 0.0
     route_ms = sum(ev[i][3].elapsed_time(ev[i][0]) for i in range(K)) / K if route != "none" else 0.0
     ms_step = total_ms / K
     attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
@@ -266,8 +323,9 @@ def main():
     slots = case.batch * case.gamma
     value = slots / (ms_step * 1e-3)
 
-    a_bytes, a_flops = attn_bytes(case, copies), attn_flops(case, copies)
-    attn_call = "spec_verify_attn_copies" if copies else "spec_verify_attn"
+    prompt_rows = int(inp["prefix_lens"].sum()) if paged else None
+    a_bytes, a_flops = attn_bytes(case, copies, prompt_rows), attn_flops(case, copies, prompt_rows)
+    attn_call = "spec_verify_attn_copies" if copies else "spec_verify_attn_paged" if paged else "spec_verify_attn"
     c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
     acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
     # the attention is bound by whichever of HBM bytes and bf16 MFMA flops
@@ -295,21 +353,31 @@ def main():
         rl_route["traffic"] = measured_traffic("spec_verify_route") if case.name == "headline" else None
         if route_ms > max(acc_ms, attn_ms):
             dom = ("spec_verify_route", rl_route)
+    rl_commit = None
+    if paged:
+        n_appended = int((sets[(K - 1) & 1].n_append > 0).sum())
+        m_bytes = commit_bytes(case, n_appended)
+        rl_commit = {"bound": "latency", "ms": commit_ms, "bytes": m_bytes, "appended_blocks": n_appended,
+                     "achieved": m_bytes / (commit_ms * 1e-3) / 1e9, "unit": "GB/s"}
     roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
-        c_bytes / (HBM_PEAK_GBS * 1e9) + (route_bytes(case) / (HBM_PEAK_GBS * 1e9) if route != "none" else 0.0)
+        c_bytes / (HBM_PEAK_GBS * 1e9) + (route_bytes(case) / (HBM_PEAK_GBS * 1e9) if route != "none" else 0.0) + \
+        (rl_commit["bytes"] / (HBM_PEAK_GBS * 1e9) if paged else 0.0)
     # traffic only applies to the headline workload the counters were taken on
     headline = case.name == "headline"
-    tag = f"_c{copies}" if copies else ""
-    rl_attn["traffic"] = measured_traffic(attn_call + tag) if headline else None
-    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") + tag) \
-        if headline else None
+    # counter lines are per workload: the copies step verifies gamma = D slots;
+    # the paged step's verification is the plain step's
+    acc_tag = f"_c{copies}" if copies else ""
+    attn_tag = acc_tag if copies else (f"_p{args.paged}{'r' if args.ragged else ''}" if paged else "")
+    rl_attn["traffic"] = measured_traffic(attn_call + attn_tag) if headline else None
+    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") +
+                                         acc_tag) if headline else None
     roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
                 "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
                 "traffic_unit": "bytes/launch", "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies)
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged)
 
     out = {
         "metric": METRIC,
@@ -332,10 +400,14 @@ def main():
                                f"vocab {case.vocab}, {case.dtype} attention, fp32 logits" +
                                ("" if verify == "rejection" else
                                 f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification") +
-                               ("" if route == "none" else f"; S2D2 routing estimate ({route}, {rparam:g}) first"),
+                               ("" if route == "none" else f"; S2D2 routing estimate ({route}, {rparam:g}) first") +
+                               ("" if not paged else f"; prompt cache in pages of {case.page_size} rows"
+                                + (", ragged prompt lengths (mean %.0f)" % inp["prefix_lens"].mean() if case.ragged
+                                   else "") + ", then commit and cache append"),
                    "route": None if route == "none" else {"estimator": route, "param": rparam},
                    "verify": verify, "temperature": None if verify == "rejection" else T,
                    "copies": copies or None,
+                   "page_size": case.page_size if paged else None, "ragged": bool(case.ragged) if paged else None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
                    "parallelism": "single GPU"},
@@ -344,6 +416,8 @@ def main():
         "detail": {
             "attn": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_attn.items()},
             "accept": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_acc.items()},
+            "commit": None if rl_commit is None else
+            {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_commit.items()},
             "route": None if rl_route is None else
             {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_route.items()},
             "step_roofline_us": round(roof_step_s * 1e6, 2),

@@ -14,9 +14,11 @@ float32 logits.  Two copies of the inputs live in HBM and steps alternate
 between them, so a step never finds the previous step's data in the 256 MB
 last-level cache.
 
-Prints ONE JSON line (rank 0, N = 1).  Also reports the roofline of the
-dominant call (timed live with HIP events on the launch stream) and the CPU
-oracle timed on this host over the same workload.
+Prints ONE JSON line (rank 0, N = 1).  After W untimed steps, K steps are
+timed with events only at their two ends (value, ms_per_step); the same K
+steps then run again with HIP events on the launch stream around every call,
+which gives the per-call durations for the roofline of the dominant call.
+Also reports the CPU oracle timed on this host over the same workload.
 
 --verify coupled | greedy replaces the epilogue by shared-noise verification
 (spec_verify_accept_coupled at --temperature, default 1) or its greedy form
@@ -188,7 +190,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the clocks need ~20 ms of load to settle)")
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verify", choices=("rejection", "coupled", "greedy"), default=None,
@@ -283,36 +286,50 @@ def main():
         else:
             s.accept_coupled(temperature=T)
 
-    for i in range(args.warmup):
-        if route != "none":
-            sets[i & 1].route(route, rparam)
-        attend(sets[i & 1])
-        epilogue(sets[i & 1])
-        if paged:
-            commit(sets[i & 1])
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(K):
-        s = sets[i & 1]
-        ev[i][3].record(stream)
+    def step(s, e=None):
+        """One step; with e (five events) each call is bracketed for its time."""
+        if e:
+            e[3].record(stream)
         if route != "none":
             s.route(route, rparam)
-        ev[i][0].record(stream)
+        if e:
+            e[0].record(stream)
         attend(s)
-        ev[i][1].record(stream)
+        if e:
+            e[1].record(stream)
         epilogue(s)
-        ev[i][2].record(stream)
+        if e:
+            e[2].record(stream)
         if paged:
             commit(s)
-        ev[i][4].record(stream)
+        if e:
+            e[4].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i & 1])
+    torch.cuda.synchronize()
+
+    # timed pass: K steps with events only at its two ends (an event between
+    # two calls costs a few microseconds of the step)
+    K = args.steps
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        step(sets[i & 1])
+    t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
 
-    total_ms = ev[0][3].elapsed_time(ev[K - 1][4])
+    # per-call pass: the same K steps again with every call bracketed by
+    # events on the launch stream; the per-call durations for the roofline
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for i in range(K):
+        step(sets[i & 1], ev[i])
+    torch.cuda.synchronize()
+
     commit_ms = sum(ev[i][2].elapsed_time(ev[i][4]) for i in range(K)) / K if paged else 0.0
     route_ms = sum(ev[i][3].elapsed_time(ev[i][0]) for i in range(K)) / K if route != "none" else 0.0
     ms_step = total_ms / K

@@ -3,7 +3,13 @@
 //
 // Method: "SimSD: Simple Speculative Decoding in Diffusion Language Models",
 // 关键设计 1 (paired layout [prompt | D | D~]), 关键设计 2 (mask A_ij from step
-// labels tau), 关键设计 3 (D~_k reuses D_k's RoPE position).
+// labels tau), 关键设计 3 (D~_k reuses D_k's RoPE position).  The same bf16
+// kernel, with a compile-time mask rule, runs the multi-copy layout of "SPOT:
+// Enhancing Speculative Decoding for Diffusion Language Models via
+// Commit-Order Prediction" (核心方法, third step: C copies of the block, each
+// bidirectional over its own keys, the prompt shared), and reads the prompt
+// cache either contiguously or through a page table with per-sequence
+// prompt lengths.
 //
 // bf16 kernel (attn_bf16_kernel): one workgroup = NW waves x 32 query rows
 // of one kv head (NW = 8 when the kv head has more than 128 rows, else 4;
@@ -120,9 +126,9 @@ struct BfArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
     const int32_t *tau;
     uint16_t *out;
-    float *ws_o;    // split partials [split][batch][2B][Hq][D]
-    float2 *ws_ml;  // [split][batch][2B][Hq] (running max in log2 units, sum)
-    int batch, block, prefix, n_qh, n_kvh, n_rb, n_split, tiles_per_split, n_tiles;
+    float *ws_o;    // split partials [split][batch][n_resp][Hq][D]
+    float2 *ws_ml;  // [split][batch][n_resp][Hq] (running max in log2 units, sum)
+    int batch, block, prefix, n_qh, n_kvh, n_rb, n_split, tiles_per_split;
     int n_resp;  // response rows (and keys) per sequence: 2B, or copies * block
     // prompt cache: row j of (sequence b, kv head) lives in page
     // block_table[b][j / page_size] at row j % page_size, pages laid out
@@ -334,6 +340,34 @@ constexpr int kCsStride = D / 2 + 1;
 // (1.0, 1.0) in bf16
 constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+// Key tiles a workgroup visits, in order: tile i of its list is tile
+// map(i) of [prompt | response keys].  The paired layout visits every tile;
+// in the multi-copy layout a workgroup visits the tiles holding prompt keys
+// and then only those holding its own copies' keys.
+template <int MASK>
+struct TileMap {
+    int n_prompt;  // tiles holding prompt keys (the list is the identity below it)
+    int shift;     // response tiles skipped after them
+    __device__ __forceinline__ int operator()(int i) const {
+        if constexpr (MASK == 0) return i;
+        else return i < n_prompt ? i : i + shift;
+    }
+};
+
+// Row rho of a kv head's rows -> (response row, query head within the GQA
+// group).  Paired layout: head-major, (head, row).  Multi-copy layout:
+// (copy, head, position), so that the rows of a workgroup, and of a wave,
+// belong to consecutive copies.
+template <int MASK>
+__device__ __forceinline__ int2 map_row(int rho, int R2, int B, int g) {
+    if constexpr (MASK == 0) {
+        return make_int2(rho % R2, rho / R2);
+    } else {
+        const int c = rho / (g * B), rem = rho % (g * B);
+        return make_int2(c * B + rem % B, rem / B);
+    }
+}
+
 template <int QB>
 struct RowInfo {
     int t_row[QB];     // step label of each row's slot (copies: the row's copy)
@@ -395,14 +429,14 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
                                           char *__restrict__ kn, char *__restrict__ vn,
                                           const float2 *__restrict__ cs, const int *__restrict__ klab,
-                                          const char *v_stage0, const LoadOffs<D, NW> &ldo, size_t unit_off) {
+                                          const char *v_stage0, const LoadOffs<D, NW> &ldo, size_t unit_off,
+                                          const TileMap<MASK> &tm, int jend) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16, NDB = D / 32, NTH = 64 * NW;
     constexpr int LPT = 2 * (T::LOADS / NW);  // direct loads per wave per tile (K and V)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix, Nk = P + a.n_resp;
-    const int base = (t0 + it) * kTileKeys;
-    const int jend = min(Nk, (t0 + nt) * kTileKeys);
+    const int base = tm(t0 + it) * kTileKeys;
     // the LPT most recent loads are the refill issued one step ago (tile
     // it + 1); everything older, tile it included, has landed
     wait_vmcnt<LPT>();
@@ -430,7 +464,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // behind the other waves' loads right after the barrier.
     constexpr int NL = LoadOffs<D, NW>::N;  // loads per tensor
     constexpr bool kNt = MASK == 0;         // see direct_load16
-    const int nb = (t0 + it + 2) * kTileKeys;
+    const int nb = tm(t0 + it + 2) * kTileKeys;
     const bool prompt_refill = nb + kTileKeys <= P;  // uniform
     // element offset of the refill tile (contiguous cache: this unit's base
     // plus the tile's rows, without the general page arithmetic)
@@ -586,7 +620,8 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 // keeps it out of the chip-wide burst that every workgroup waits on before
 // its first tile.  LDS regions are __restrict__ parameters (see tile_step).
 template <int D, int NW, int QB, int MASK>
-__device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, int jend, int tau_v,
+__device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, const TileMap<MASK> &tm, int jend,
+                                         int tau_v,
                                          uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
                                          bf16x8 (*qop)[D / 16], char *__restrict__ k0, char *__restrict__ v0,
                                          char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
@@ -596,8 +631,8 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)
     constexpr bool kNt = MASK == 0;
-    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, t0 * kTileKeys, jend, k0, w, lane);
-    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, t0 * kTileKeys, jend, v0, w, lane);
+    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, tm(t0) * kTileKeys, jend, k0, w, lane);
+    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, tm(t0) * kTileKeys, jend, v0, w, lane);
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
     if (a.use_rope) {
         if (tid < D / 2) invf[tid] = rope_inv_freq(tid, D, a.log2_theta);
@@ -629,8 +664,8 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     }
     // the second tile (a tile past the end reads clamped rows and is never
     // consumed)
-    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, (t0 + 1) * kTileKeys, jend, k1, w, lane);
-    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, (t0 + 1) * kTileKeys, jend, v1, w, lane);
+    load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, tm(t0 + 1) * kTileKeys, jend, k1, w, lane);
+    load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, tm(t0 + 1) * kTileKeys, jend, v1, w, lane);
 }
 
 // NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles
@@ -664,9 +699,22 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     rest /= a.n_rb;
     const int kvh = rest % a.n_kvh;
     const int b = rest / a.n_kvh;
-    // this sequence's prompt length, and its key tiles
+    // this sequence's prompt length, and the key tiles of this workgroup
     if (a.prefix_lens) a.prefix = min(max(uniform_ld(a.prefix_lens, b), 0), a.prefix);
-    const int n_tiles = (a.prefix + R2 + kTileKeys - 1) / kTileKeys;
+    int n_tiles;
+    TileMap<MASK> tm{0, 0};
+    if constexpr (MASK == 0) {
+        n_tiles = (a.prefix + R2 + kTileKeys - 1) / kTileKeys;
+    } else {
+        // copies cl .. ch hold this workgroup's rows; their keys lie in
+        // tiles ra .. rz
+        const int cl = (rb * ROWS_B) / (g * B), ch = (min(R, (rb + 1) * ROWS_B) - 1) / (g * B);
+        const int n_p = (a.prefix + kTileKeys - 1) / kTileKeys;
+        const int ra = max(n_p, (a.prefix + cl * B) / kTileKeys);
+        const int rz = (a.prefix + (ch + 1) * B - 1) / kTileKeys;
+        tm = TileMap<MASK>{n_p, ra - n_p};
+        n_tiles = n_p + max(0, rz - ra + 1);
+    }
     const int t0 = split * a.tiles_per_split;
     const int t1 = min(n_tiles, t0 + a.tiles_per_split);
     const int nt = t1 - t0;
@@ -677,7 +725,8 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
         for (int qb = 0; qb < QB; ++qb) {
             const int rho = rb * ROWS_B + w * ROWS_W + qb * 32 + l32;
             if (rho < R && h == 0) {
-                const size_t row = ((size_t)b * R2 + rho % R2) * a.n_qh + kvh * g + rho / R2;
+                const int2 rh = map_row<MASK>(rho, R2, B, g);
+                const size_t row = ((size_t)b * R2 + rh.x) * a.n_qh + kvh * g + rh.y;
                 a.ws_ml[(size_t)split * a.batch * R2 * a.n_qh + row] = make_float2(-INFINITY, 0.f);
             }
         }
@@ -695,17 +744,17 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const int rho = rb * ROWS_B + w * ROWS_W + qb * 32 + l32;
         rvalid[qb] = rho < R;
-        const int rr = rvalid[qb] ? rho : 0;
-        rrow[qb] = rr % R2;
-        qhead[qb] = kvh * g + rr / R2;
+        const int2 rh = map_row<MASK>(rvalid[qb] ? rho : 0, R2, B, g);
+        rrow[qb] = rh.x;
+        qhead[qb] = kvh * g + rh.y;
         pos_idx[qb] = rrow[qb] % B;
         const uint16_t *qp = a.q + (((size_t)b * R2 + rrow[qb]) * a.n_qh + qhead[qb]) * D + 8 * h;
 #pragma unroll
         for (int s = 0; s < NS; ++s) raw[qb][s] = *reinterpret_cast<const uint4 *>(qp + 16 * s);  // valid row
     }
-    const int jend = min(a.prefix + R2, t1 * kTileKeys);
+    const int jend = min(a.prefix + R2, (tm(t1 - 1) + 1) * kTileKeys);  // end of this workgroup's keys
     bf16x8 qop[QB][NS];
-    prologue<D, NW, QB, MASK>(a, b, kvh, t0, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
+    prologue<D, NW, QB, MASK>(a, b, kvh, t0, tm, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
                         invf_lds, klab_lds);
     RowInfo<QB> ri;
 #pragma unroll
@@ -721,13 +770,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     ri.c_lo = 0;
     ri.c_hi = R2 / B - 1;
     if constexpr (MASK == 1) {
-        // rows rho0 .. rho1 of this wave; one head's rows are contiguous in
-        // copy order, a wave that crosses into the next head keeps all copies
+        // rows rho0 .. rho1 of this wave belong to copies rho0 / (g B) ..
+        // rho1 / (g B) (rows are copy-major)
         const int rho0 = __builtin_amdgcn_readfirstlane(rb * ROWS_B + w * ROWS_W);
         const int rho1 = min(rho0 + ROWS_W, R) - 1;
-        if (rho0 < R && rho0 / R2 == rho1 / R2) {
-            ri.c_lo = (rho0 % R2) / B;
-            ri.c_hi = (rho1 % R2) / B;
+        if (rho0 < R) {
+            ri.c_lo = rho0 / (g * B);
+            ri.c_hi = rho1 / (g * B);
         }
     }
     const LdsOffs<D> offs = lds_offsets<D>(lane, v_st0);
@@ -748,13 +797,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 
     for (int it = 0; it < nt; it += 3) {
         tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
-                             cs_lds, klab_lds, v_st0, ldo, unit_off);
+                             cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 1 < nt)
             tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
-                                 v_st0, cs_lds, klab_lds, v_st0, ldo, unit_off);
+                                 v_st0, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 2 < nt)
             tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
-                                 v_st1, cs_lds, klab_lds, v_st0, ldo, unit_off);
+                                 v_st1, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 
@@ -988,7 +1037,6 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.n_rb = p.n_rb;
         a.n_split = p.n_split;
         a.tiles_per_split = p.tiles_per_split;
-        a.n_tiles = p.n_tiles;
         a.n_resp = s.n_resp;
         a.prefix_lens = cv.prefix_lens;
         a.block_table = cv.block_table;

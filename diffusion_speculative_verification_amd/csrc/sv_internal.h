@@ -21,11 +21,11 @@ struct AttnShape {
 };
 
 struct AttnPlan {
-    int rows;            // rows per kv head = (n_qh / n_kvh) * 2 * block
+    int rows;            // rows per kv head = (n_qh / n_kvh) * n_resp
     int nw;              // waves per workgroup
     int qb;              // 32-row query blocks per wave
     int n_rb;            // row blocks of 32 * qb * nw rows per kv head
-    int n_tiles;         // key tiles over prefix + 2 * block keys
+    int n_tiles;         // key tiles over prefix + n_resp keys (the longest prompt)
     int n_split;         // prefix splits (1 = no combine pass)
     int tiles_per_split;
     size_t ws_partial_o;   // bytes of split partial outputs (float32)

@@ -52,6 +52,8 @@ def check(o, case, rope_theta=None, check_seqs=None):
     dict(block=32, n_copies=32, prefix_len=100, n_qh=4, n_kvh=4),  # 1024 response rows (the limit)
     dict(head_dim=64, prefix_len=77),          # head_dim 64, ragged tail
     dict(batch=1, prefix_len=9000, n_qh=8, n_kvh=1, n_copies=3),   # prefix splits + combine
+    dict(batch=2, block=64, n_copies=16, prefix_len=1000, n_qh=64, n_kvh=8),   # B = 64, 1024 rows, g = 8
+    dict(block=24, n_copies=7, prefix_len=130),   # copies not aligned to 32-row waves or 64-key tiles
 ])
 def test_copies(o, kw):
     check(o, BASE.with_(**kw))

@@ -137,6 +137,12 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     import oracle
     o = oracle.Oracle()
     threads = o.max_threads()
+    cpu_model = "unknown"
+    if os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
     t = time.perf_counter()
     if route != "none":
         o.route(inp["draft_probs"], inp["tau"], case.gamma, route, rparam)
@@ -178,12 +184,49 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     attn_what = (f"attention {t_attn:.2f} s" if n_seq == case.batch else
                  f"attention {t_attn:.2f} s (timed on {n_seq} of {case.batch} sequences, scaled)")
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"one step of the same workload ({case.batch} sequences): "
                       + (f"routing {t_route:.2f} s + " if route != "none" else "") +
                       f"{attn_what} + accept {t_acc:.2f} s"
                       + (f" + commit and append {t_commit:.2f} s" if paged else "") +
                       f" on {threads} OpenMP threads "
                       f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
+
+
+def measured_peaks(torch) -> dict:
+    """Microbenchmarks on the same device in the same run, beside the
+    datasheet peaks: a 1 GiB device copy (bytes read + written), a 1 GiB
+    read-only pass (row sums of 4096 floats: the best read rate among
+    torch's reductions here), and a bf16 16384 x 16384 x 8192 GEMM through
+    torch (hipBLASLt)."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps * 1e-3
+
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: b.copy_(a), 10)
+    t_read = timed(lambda: a.view(-1, 4096).sum(1), 10)
+    del b
+    m, n, k = 16384, 16384, 8192
+    x = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.mm(x, y), 10)
+    del a, x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "hbm_read_gbs": round((1 << 30) / t_read / 1e9, 1),
+            "bf16_gemm_tflops": round(2 * m * n * k / t_mm / 1e12, 1),
+            "what": "1 GiB device copy (read + write bytes), 1 GiB of float32 row sums, bf16 16384x16384x8192 "
+                    "torch.mm"}
 
 
 def main():
@@ -261,7 +304,11 @@ def main():
     inp = synth.make_inputs(case, parts=gen_parts)
     if route != "none":
         parts = parts + ("route",)
-    sets = [StepBuffers(case, inp, parts=parts), StepBuffers(case, inp, parts=parts)]
+    # enough input sets in rotation that a step never finds the previous
+    # steps' data in the 256 MB last-level cache (at least 1 GiB in rotation)
+    set_bytes = sum(v.nbytes for v in inp.values() if hasattr(v, "nbytes"))
+    n_sets = int(min(8, max(2, -(-(1 << 30) // max(1, set_bytes)))))
+    sets = [StepBuffers(case, inp, parts=parts) for _ in range(n_sets)]
     stream = torch.cuda.current_stream()
 
     def attend(s):
@@ -306,7 +353,7 @@ def main():
             e[4].record(stream)
 
     for i in range(args.warmup):
-        step(sets[i & 1])
+        step(sets[i % n_sets])
     torch.cuda.synchronize()
 
     # timed pass: K steps with events only at its two ends (an event between
@@ -317,7 +364,7 @@ def main():
     wall0 = time.perf_counter()
     t_begin.record(stream)
     for i in range(K):
-        step(sets[i & 1])
+        step(sets[i % n_sets])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -327,7 +374,7 @@ def main():
     # events on the launch stream; the per-call durations for the roofline
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     for i in range(K):
-        step(sets[i & 1], ev[i])
+        step(sets[i % n_sets], ev[i])
     torch.cuda.synchronize()
 
     commit_ms = sum(ev[i][2].elapsed_time(ev[i][4]) for i in range(K)) / K if paged else 0.0
@@ -372,26 +419,38 @@ def main():
             dom = ("spec_verify_route", rl_route)
     rl_commit = None
     if paged:
-        n_appended = int((sets[(K - 1) & 1].n_append > 0).sum())
+        n_appended = int((sets[(K - 1) % n_sets].n_append > 0).sum())
         m_bytes = commit_bytes(case, n_appended)
         rl_commit = {"bound": "latency", "ms": commit_ms, "bytes": m_bytes, "appended_blocks": n_appended,
                      "achieved": m_bytes / (commit_ms * 1e-3) / 1e9, "unit": "GB/s"}
     roof_step_s = max(a_bytes / (HBM_PEAK_GBS * 1e9), a_flops / (BF16_PEAK_TFLOPS * 1e12)) + \
         c_bytes / (HBM_PEAK_GBS * 1e9) + (route_bytes(case) / (HBM_PEAK_GBS * 1e9) if route != "none" else 0.0) + \
         (rl_commit["bytes"] / (HBM_PEAK_GBS * 1e9) if paged else 0.0)
-    # traffic only applies to the headline workload the counters were taken on
+    # counter lines exist for the headline workload's variants and for the
+    # plain step of the long-prefix and wide workloads
     headline = case.name == "headline"
     # counter lines are per workload: the copies step verifies gamma = D slots;
     # the paged step's verification is the plain step's
     acc_tag = f"_c{copies}" if copies else ""
     attn_tag = acc_tag if copies else (f"_p{args.paged}{'r' if args.ragged else ''}" if paged else "")
-    rl_attn["traffic"] = measured_traffic(attn_call + attn_tag) if headline else None
-    rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") +
-                                         acc_tag) if headline else None
+    if headline:
+        rl_attn["traffic"] = measured_traffic(attn_call + attn_tag)
+        rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") +
+                                             acc_tag)
+    elif not (copies or paged or route != "none" or verify != "rejection"):
+        # the plain step of another workload has its own counter lines
+        rl_attn["traffic"] = measured_traffic(f"{attn_call}_{case.name}")
+        rl_acc["traffic"] = measured_traffic(f"{acc_call}_{case.name}")
+    else:
+        rl_attn["traffic"] = rl_acc["traffic"] = None
     roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
                 "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
                 "traffic_unit": "bytes/launch", "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
 
+    peaks = measured_peaks(torch)
+    roofline["frac_of_measured_peak"] = round(dom[1]["achieved"] / (peaks["bf16_gemm_tflops"] if
+                                                                    dom[1]["unit"] == "TFLOP/s" else
+                                                                    peaks["hbm_read_gbs"]), 4)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged)
@@ -431,6 +490,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": {
+            "input_sets": n_sets,
+            "measured_peaks": peaks,
             "attn": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_attn.items()},
             "accept": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in rl_acc.items()},
             "commit": None if rl_commit is None else

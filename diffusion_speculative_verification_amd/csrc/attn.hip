@@ -178,11 +178,11 @@ __device__ __forceinline__ uint16_t u4_elem(const uint4 &v, int e) {
 // ROWS_PER_LOAD; lane l writes physical chunk l % NCH of its row and
 // therefore fetches the logical chunk that the swizzle places there.
 // One wave-wide direct global->LDS load: lane l's 16 bytes at `src` land at
-// LDS address lds_dst + 16 * l, with the non-temporal hint when NT.  The
-// paired layout reads each K/V tile once per workgroup and streams it (NT);
-// in the multi-copy layout several row blocks of one kv head read the same
-// prompt tiles at about the same time on one XCD, and plain loads let the
-// later ones hit in L2.  Issued as inline assembly so that the
+// LDS address lds_dst + 16 * l, with the non-temporal hint when NT.  With one
+// row block per kv head each K/V tile is read once and streamed (NT); with
+// several (the multi-copy layout, wide GQA groups) the row blocks of a kv
+// head read the same prompt tiles at about the same time on one XCD, and
+// plain loads let the later ones hit in L2.  Issued as inline assembly so that the
 // compiler's wait insertion does not treat later LDS reads of other ring
 // stages as dependent on it: every wait on these loads is explicit
 // (wait_vmcnt), and no compiler-visible global load is issued while tile
@@ -423,7 +423,7 @@ __device__ __forceinline__ LdsOffs<D> lds_offsets(int lane, const char *v_stage0
 // prove that the refill in flight never aliases this step's reads.  Each
 // lane owns QB query rows (one per 32-row MFMA block); every K and V operand
 // read from LDS feeds QB MFMAs.
-template <int D, int NW, int QB, int MASK>
+template <int D, int NW, int QB, int MASK, bool NT>
 __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t0, int nt, int it, bool wave_active,
                                           const RowInfo<QB> &ri, const LdsOffs<D> &lo_, const bf16x8 (*qop)[D / 16],
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
@@ -463,7 +463,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // k-steps, so that their issue overlaps matrix work instead of queueing
     // behind the other waves' loads right after the barrier.
     constexpr int NL = LoadOffs<D, NW>::N;  // loads per tensor
-    constexpr bool kNt = MASK == 0;         // see direct_load16
+    constexpr bool kNt = NT;                // see direct_load16
     const int nb = tm(t0 + it + 2) * kTileKeys;
     const bool prompt_refill = nb + kTileKeys <= P;  // uniform
     // element offset of the refill tile (contiguous cache: this unit's base
@@ -619,7 +619,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 // registers is a full vmcnt(0): issuing the second tile after that wait
 // keeps it out of the chip-wide burst that every workgroup waits on before
 // its first tile.  LDS regions are __restrict__ parameters (see tile_step).
-template <int D, int NW, int QB, int MASK>
+template <int D, int NW, int QB, int MASK, bool NT>
 __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0, const TileMap<MASK> &tm, int jend,
                                          int tau_v,
                                          uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
@@ -630,7 +630,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)
-    constexpr bool kNt = MASK == 0;
+    constexpr bool kNt = NT;
     load_tile<D, NW, false, kNt>(a, a.k_cache, a.k_new, b, kvh, tm(t0) * kTileKeys, jend, k0, w, lane);
     load_tile<D, NW, true, kNt>(a, a.v_cache, a.v_new, b, kvh, tm(t0) * kTileKeys, jend, v0, w, lane);
     // RoPE cos/sin table for positions P + 0..B-1 (float64 angles)
@@ -670,7 +670,7 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
 
 // NW waves x QB x 32 query rows per workgroup; 3-deep LDS ring of K/V tiles
 // fed by direct global->LDS loads.
-template <int D, int NW, int QB, int MASK>
+template <int D, int NW, int QB, int MASK, bool NT>
 __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     using T = Tile<D, false>;
     constexpr int NS = D / 16;
@@ -754,7 +754,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     }
     const int jend = min(a.prefix + R2, (tm(t1 - 1) + 1) * kTileKeys);  // end of this workgroup's keys
     bf16x8 qop[QB][NS];
-    prologue<D, NW, QB, MASK>(a, b, kvh, t0, tm, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
+    prologue<D, NW, QB, MASK, NT>(a, b, kvh, t0, tm, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
                         invf_lds, klab_lds);
     RowInfo<QB> ri;
 #pragma unroll
@@ -796,13 +796,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     }
 
     for (int it = 0; it < nt; it += 3) {
-        tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
+        tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
                              cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 1 < nt)
-            tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
+            tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
                                  v_st0, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 2 < nt)
-            tile_step<D, NW, QB, MASK>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
+            tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
                                  v_st1, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
@@ -1013,6 +1013,14 @@ hipError_t launch_rope(const void *q_in, const void *k_in, void *q_out, void *k_
     return hipGetLastError();
 }
 
+template <int MASK, bool NT>
+void launch_bf16(int head_dim, int nw, unsigned grid, dim3 blk, hipStream_t st, const BfArgs &a) {
+    if (head_dim == 128 && nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, MASK, NT>), dim3(grid), blk, 0, st, a);
+    else if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1, MASK, NT>), dim3(grid), blk, 0, st, a);
+    else if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, MASK, NT>), dim3(grid), blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1, MASK, NT>), dim3(grid), blk, 0, st, a);
+}
+
 hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, const void *k_new,
                        const void *v_new, const void *k_cache, const void *v_cache,
                        const int32_t *tau, void *out, double theta, float scale, void *ws,
@@ -1048,16 +1056,16 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.scale_log2 = scale * kLog2e;
         const unsigned grid = (unsigned)((size_t)s.batch * s.n_kvh * p.n_rb * p.n_split);
         const dim3 blk(64 * p.nw);
+        // non-temporal tile loads when each kv head's K/V is read by one
+        // row block only; with several row blocks the later ones find the
+        // prompt tiles in L2
+        const bool nt = p.n_rb == 1;
         if (s.mask == 0) {
-            if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 0>), dim3(grid), blk, 0, st, a);
-            else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1, 0>), dim3(grid), blk, 0, st, a);
-            else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 0>), dim3(grid), blk, 0, st, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1, 0>), dim3(grid), blk, 0, st, a);
+            if (nt) launch_bf16<0, true>(s.head_dim, p.nw, grid, blk, st, a);
+            else launch_bf16<0, false>(s.head_dim, p.nw, grid, blk, st, a);
         } else {
-            if (s.head_dim == 128 && p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8, 1, 1>), dim3(grid), blk, 0, st, a);
-            else if (s.head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 4, 1, 1>), dim3(grid), blk, 0, st, a);
-            else if (p.nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8, 1, 1>), dim3(grid), blk, 0, st, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<64, 4, 1, 1>), dim3(grid), blk, 0, st, a);
+            if (nt) launch_bf16<1, true>(s.head_dim, p.nw, grid, blk, st, a);
+            else launch_bf16<1, false>(s.head_dim, p.nw, grid, blk, st, a);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.n_split == 1) return e;

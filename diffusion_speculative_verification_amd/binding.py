@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_E_NULL, SV_E_SHAPE, SV_E_UNSUPPORTED, SV_E_ALIGN, SV_E_WORKSPACE, SV_E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+SV_E_INVALID_TAU = -7
 SV_F32, SV_BF16 = 0, 1
 
 _lib = None
@@ -66,6 +67,8 @@ def load(path: str | None = None):
     lib.spec_verify_attn_paged.restype = I
     lib.spec_verify_attn_paged.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, I, I, I, D, F, V,
                                            SZ, V]
+    lib.spec_verify_check_tau.restype = I
+    lib.spec_verify_check_tau.argtypes = [V, I, I, V, V]
     lib.spec_verify_commit.restype = I
     lib.spec_verify_commit.argtypes = [V, V, I, I, I, V, V, V, V]
     lib.spec_verify_kv_append.restype = I
@@ -207,3 +210,7 @@ def spec_verify_kv_append(k_rows, v_rows, src_stride, n_append, k_pages, v_pages
                                         _ptr(v_pages), _ptr(block_table), _ptr(prefix_lens), _ptr(status), dtype,
                                         batch, page_size, max_pages, n_pages, n_kvh, head_dim, float(rope_theta),
                                         _stream(stream)))
+
+
+def spec_verify_check_tau(tau, batch, block, bad, stream=None) -> None:
+    _check(load().spec_verify_check_tau(_ptr(tau), batch, block, _ptr(bad), _stream(stream)))

@@ -40,6 +40,7 @@ const char *spec_verify_status_string(int status) {
         case SV_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case SV_E_WORKSPACE: return "workspace missing or too small";
         case SV_E_LAUNCH: return "kernel launch failed";
+        case SV_E_INVALID_TAU: return "tau is not a permutation of 1..block";
         default: return "unknown status";
     }
 }
@@ -180,6 +181,12 @@ int spec_verify_attn_paged(const void *q, const void *k_new, const void *v_new, 
     const float scale = softmax_scale > 0 ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
     return map_launch(sv::launch_attn(s, p, q, k_new, v_new, k_pages, v_pages, n_copies == 0 ? tau : nullptr, out,
                                       rope_theta, scale, workspace, (hipStream_t)stream, cv));
+}
+
+int spec_verify_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, void *stream) {
+    if (batch < 1 || block < 1 || block > 64) return SV_E_SHAPE;
+    if (!tau || !bad) return SV_E_NULL;
+    return map_launch(sv::launch_check_tau(tau, batch, block, bad, (hipStream_t)stream));
 }
 
 int spec_verify_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,

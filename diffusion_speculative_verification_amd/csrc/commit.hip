@@ -124,6 +124,27 @@ __global__ void __launch_bounds__(256) append_lens_kernel(const int32_t *__restr
     if (status) status[b] = s;
 }
 
+// One wave per sequence: bad[b] = 0 when tau[b] is a permutation of
+// 1..block, else 1 (each label in range, and together they cover every
+// label: the OR of one bit per lane is full).
+__global__ void __launch_bounds__(64) check_tau_kernel(const int32_t *__restrict__ tau, int block, int32_t *bad) {
+    const int lane = threadIdx.x, b = blockIdx.x;
+    const bool in = lane < block;
+    const int t = in ? tau[(size_t)b * block + lane] : 1;
+    const bool ok = t >= 1 && t <= block;
+    unsigned long long bits = (in && ok) ? (1ull << (t - 1)) : 0ull;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bits |= __shfl_xor(bits, o);
+    const unsigned long long full = block == 64 ? ~0ull : ((1ull << block) - 1);
+    const bool all_ok = __ballot(in && !ok) == 0ull;
+    if (lane == 0) bad[b] = (all_ok && bits == full) ? 0 : 1;
+}
+
+hipError_t launch_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, hipStream_t st) {
+    hipLaunchKernelGGL(check_tau_kernel, dim3(batch), dim3(64), 0, st, tau, block, bad);
+    return hipGetLastError();
+}
+
 hipError_t launch_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,
                          int32_t *remaining, int32_t *state, int32_t *n_append, hipStream_t st) {
     hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(64), 0, st, out_tokens, block_tokens, block, gamma,

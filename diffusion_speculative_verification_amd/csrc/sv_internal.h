@@ -97,6 +97,8 @@ hipError_t launch_route(const RoutePlan &p, const float *probs, const int32_t *t
                         int gamma, int64_t vocab, int estimator, double param, float *khat, float *alpha_hat,
                         void *ws, hipStream_t st);
 
+hipError_t launch_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, hipStream_t st);
+
 hipError_t launch_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,
                          int32_t *remaining, int32_t *state, int32_t *n_append, hipStream_t st);
 

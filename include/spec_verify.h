@@ -35,7 +35,7 @@
  *     non-zero status nothing is enqueued and no output is touched.
  *     SV_E_LAUNCH reports a launch the runtime refused.
  *   - tau being a permutation of 1..block is a precondition (not checked on
- *     the device).
+ *     the device by the compute calls; spec_verify_check_tau validates it).
  *   - dtype SV_BF16: bfloat16 tensors, bf16 MFMA with fp32 accumulation.
  *     dtype SV_F32: float32 tensors and float32 arithmetic throughout.
  *   - Shape limits: 1 <= block <= 64, n_qh % n_kvh == 0, head_dim in
@@ -61,7 +61,8 @@ enum {
     SV_E_UNSUPPORTED = -3, /* dtype / head_dim not provided by the library */
     SV_E_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned     */
     SV_E_WORKSPACE = -5,   /* workspace missing or smaller than required  */
-    SV_E_LAUNCH = -6       /* the HIP runtime refused a kernel launch     */
+    SV_E_LAUNCH = -6,      /* the HIP runtime refused a kernel launch     */
+    SV_E_INVALID_TAU = -7  /* validation only: tau not a permutation      */
 };
 
 enum { SV_F32 = 0, SV_BF16 = 1 };
@@ -177,6 +178,19 @@ int spec_verify_attn_paged(const void *q, const void *k_new, const void *v_new, 
                            int max_prefix, int page_size, int max_pages, int n_pages, int n_qh, int n_kvh,
                            int head_dim, double rope_theta, float softmax_scale, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Validation of the step labels ("SimSD: Simple Speculative Decoding in
+ * Diffusion Language Models", 关键设计 2: tau assigns each slot of the block
+ * its draft step, a permutation of 1..block).  The other calls take this as
+ * a precondition and do not check it on the device (an invalid tau gives
+ * wrong results but no access outside the buffers).
+ *   tau [batch][block] int32; bad [batch] int32 out: 0 when row b is a
+ *   permutation of 1..block, else 1.  1 <= block <= 64.  The caller reads
+ *   bad after the stream reaches this point (SV_E_INVALID_TAU names the
+ *   condition for its own error handling).
+ */
+int spec_verify_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, void *stream);
 
 /*
  * Commit step after a verification round ("SimSD", 关键设计 4: the accepted

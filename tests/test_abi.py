@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
 
@@ -194,6 +194,9 @@ def test_paged_argument_checks(lib):
 
 
 def test_commit_and_append_argument_checks(lib):
+    assert lib.spec_verify_check_tau(A, 4, 65, A, None) == sv.SV_E_SHAPE
+    assert lib.spec_verify_check_tau(None, 4, 32, A, None) == sv.SV_E_NULL
+    assert "tau" in sv.spec_verify_status_string(sv.SV_E_INVALID_TAU)
     c = lib.spec_verify_commit
     assert c(A, A, 4, 32, 33, A, A, A, None) == sv.SV_E_SHAPE      # gamma > block
     assert c(A, A, 4, 65, 8, A, A, A, None) == sv.SV_E_SHAPE       # block > 64

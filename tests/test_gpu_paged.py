@@ -248,3 +248,33 @@ def test_step_chain(o):
     for b in range(case.batch):
         parity.check_attn(got[b], ref[b], "bf16", f"chain seq {b}")
     print(f"[result] chain: accept_len {L.tolist()} n_append {na_o.tolist()} lengths {lens_o.tolist()}", flush=True)
+
+
+# ------------------------------------------------------------------ tau validation
+@pytest.mark.parametrize("B", [1, 7, 32, 64])
+def test_check_tau(B):
+    """Rows that are permutations of 1..B pass; rows with a label out of
+    range (0, B + 1, negative) or a repeated label are flagged."""
+    print(f"[case] check_tau B={B}", flush=True)
+    _cuda()
+    r = np.random.default_rng(2000 + B)
+    n = 200
+    tau = np.stack([r.permutation(B) + 1 for _ in range(n)]).astype(np.int32)
+    for i in range(0, n, 2):
+        k = int(r.integers(0, B))
+        kind = (i // 2) % 4
+        if kind == 0:
+            tau[i, k] = 0
+        elif kind == 1:
+            tau[i, k] = B + 1
+        elif kind == 2:
+            tau[i, k] = -5
+        elif B > 1:
+            tau[i, k] = tau[i, (k + 1) % B]          # a repeated label
+    want = np.array([0 if sorted(row.tolist()) == list(range(1, B + 1)) else 1 for row in tau], np.int32)
+    t = torch.from_numpy(tau).cuda()
+    bad = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    sv.spec_verify_check_tau(t, n, B, bad)
+    torch.cuda.synchronize()
+    assert np.array_equal(bad.cpu().numpy(), want)
+    print(f"[result] check_tau B={B}: {int(want.sum())} bad rows found", flush=True)

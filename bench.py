@@ -255,7 +255,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the verification step is sharded across GPUs only by design, see DESIGN.md)", file=sys.stderr)
+              "(the verification step shards across GPUs without communication, but only one GPU is used here)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -39,7 +39,7 @@
  *     "SPOT", 前置知识 (finished blocks join the cached prefix): the commit
  *     step, the cache append and the paged prompt cache at the end of this
  *     file.
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   prompt carries step label 0 and counts as data; D~_k shares tau(k) with
  *   D_k; positions are 0..P-1 for the prompt and P+k for both D_k and D~_k;
  *   rotate-half RoPE with inv_freq_i = theta^(-2i/d); scale 1/sqrt(d) by

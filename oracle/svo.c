@@ -548,9 +548,10 @@ int svo_route(const float *probs, const int32_t *tau, int batch, int B, int gamm
  * prompt K (or V) in pages.  The pages say only that the prompt's K/V are
  * cached ("SimSD", 损失函数 / 训练策略: a KV cache makes the prefix cost
  * linear; the block-diffusion prior in "SPOT", 前置知识: finished blocks are
- * cached and later blocks attend to them).  Paging is this build's storage
- * reading of that cache: row j of the sequence is row j % page_size of page
- * table_row[j / page_size], pages laid out [n_pages][Hkv][page_size][d].
+ * cached and later blocks attend to them).  Paging is a storage layout for
+ * that cache, not something the pages prescribe: row j of the sequence is
+ * row j % page_size of page table_row[j / page_size], pages laid out
+ * [n_pages][Hkv][page_size][d].
  * out [Hkv][P][d].  Returns SVO_BAD_ARG for a page id outside [0, n_pages).
  */
 int svo_gather_prefix(const float *pages, const int32_t *table_row, int P, int page_size, int n_pages,

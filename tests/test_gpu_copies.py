@@ -63,6 +63,13 @@ def test_copies_pre_rotated(o):
     check(o, BASE.with_(prefix_len=40), rope_theta=0.0)
 
 
+def test_copies_headline_d20_sampled(o):
+    """The headline shape with the root and 20 draft states (672 response
+    rows per sequence), batch 32; sampled sequences checked."""
+    case = synth.config_by_name("headline").with_(n_copies=21)
+    check(o, case, check_seqs=[5, 30])
+
+
 def test_copies_headline_budget_sampled(o):
     """The headline shape with the root and 8 draft states, batch 32, in the
     launch configuration a benchmark would time; sampled sequences checked."""

@@ -65,6 +65,8 @@ def run_paged(o, case, n_copies=0, lens=None, check_seqs=None):
     (dict(), 5),                                      # the multi-copy layout over pages
     (dict(batch=2, prefix_len=9000, n_qh=8, n_kvh=1), 0),   # prefix splits: empty splits for the shorter
     (dict(batch=2, prefix_len=9000, n_qh=8, n_kvh=1), 3),
+    (dict(head_dim=64, prefix_len=600, page_size=256), 6),   # copies, head_dim 64, pages of 256
+    (dict(block=64, gamma=64, n_qh=16, n_kvh=2, prefix_len=1500, page_size=512), 0),   # B = 64, pages of 512
 ])
 def test_paged(o, kw, n_copies):
     run_paged(o, BASE.with_(**kw), n_copies)
@@ -157,12 +159,12 @@ def _bf16_close(got, want):
     return bool((np.abs(got - want) <= ulp).all())
 
 
-@pytest.mark.parametrize("paged,theta,head_dim", [(True, 1e6, 128), (True, 0.0, 128), (False, 1e4, 64),
-                                                  (True, 1e4, 64)])
-def test_kv_append(o, paged, theta, head_dim):
-    print(f"[case] append paged={paged} theta={theta} d={head_dim}", flush=True)
+@pytest.mark.parametrize("paged,theta,head_dim,ps", [(True, 1e6, 128, 64), (True, 0.0, 128, 64), (False, 1e4, 64, 64),
+                                                     (True, 1e4, 64, 64), (True, 1e6, 128, 128)])
+def test_kv_append(o, paged, theta, head_dim, ps):
+    print(f"[case] append paged={paged} theta={theta} d={head_dim} page_size={ps}", flush=True)
     _cuda()
-    case = BASE.with_(batch=6, head_dim=head_dim, ragged=True, prefix_len=200, page_size=64)
+    case = BASE.with_(batch=6, head_dim=head_dim, ragged=True, prefix_len=200, page_size=ps)
     inp = synth.make_inputs(case, parts=("attn", "paged"))
     B, S = case.block, 2 * case.block
     n_app = np.array([B, 0, 5, B, B, S + 1], np.int32)   # seq 5: more rows than the source holds

@@ -93,6 +93,7 @@ class Oracle:
         lib.svo_route.argtypes = [P, P, i32, i32, i32, i64, i32, dbl, P, P]
         lib.svo_attn_copies.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, dbl, P]
         lib.svo_gather_prefix.argtypes = [P, P, i32, i32, i32, i32, i32, P]
+        lib.svo_tree_verify.argtypes = [P, P, P, P, P, P, i32, i32, i64, ctypes.c_float, P, P, P, P, P]
         lib.svo_commit.argtypes = [P, P, i32, i32, i32, P, P, P]
         lib.svo_kv_append.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, dbl, P, P, P]
         lib.svo_set_threads.argtypes = [i32]
@@ -244,6 +245,22 @@ class Oracle:
                     kp[pg, :, j % page_size], vp[pg, :, j % page_size] = ks[b, i], vo[b, i]
         return kp, vp, pl, st
 
+    def tree_verify(self, logits, gumbel, parent, node_pos, node_tok, target_pos, temperature: float):
+        """Verification of a draft tree ("SPOT"): logits/gumbel [batch][N][V] (row n:
+        the target at node n's own next commit position), parent/node_pos/node_tok/
+        target_pos [batch][N] -> (path_len [batch], path [batch][N], commit_pos
+        [batch], commit_tok [batch], target_tok [batch][N])."""
+        logits = _c(logits, np.float32)
+        n, N, V = logits.shape
+        g = None if gumbel is None or temperature == 0 else _c(gumbel, np.float32)
+        parent, node_pos = _c(parent, np.int32), _c(node_pos, np.int32)
+        node_tok, target_pos = _c(node_tok, np.int32), _c(target_pos, np.int32)
+        pl, cp, ct = (np.empty(n, np.int32) for _ in range(3))
+        path, tt = np.empty((n, N), np.int32), np.empty((n, N), np.int32)
+        _check(self.lib.svo_tree_verify(_p(logits), _p(g), _p(parent), _p(node_pos), _p(node_tok), _p(target_pos),
+                                        n, N, V, float(temperature), _p(pl), _p(path), _p(cp), _p(ct), _p(tt)))
+        return pl, path, cp, ct, tt
+
     def softmax(self, l):
         """Float64 softmax of one logits row -> (p, m, s)."""
         l = _c(l, np.float32)
@@ -343,6 +360,7 @@ def attention_paged(*a, **k): return default().attention_paged(*a, **k)
 def gather_prefix(*a, **k): return default().gather_prefix(*a, **k)
 def commit(*a, **k): return default().commit(*a, **k)
 def kv_append(*a, **k): return default().kv_append(*a, **k)
+def tree_verify(*a, **k): return default().tree_verify(*a, **k)
 def softmax(l): return default().softmax(l)
 def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)

@@ -640,3 +640,62 @@ int svo_kv_append(const float *k_rows, const float *v_rows, int src_stride, cons
     }
     return SVO_OK;
 }
+
+/*
+ * Verification of a draft tree ("SPOT", 核心方法, second step: a tree of
+ * draft states, each child its parent plus one commit (position, token);
+ * 方法步骤详情, 验证: one forward gives the target's own next commit at the
+ * root and at every draft state, edges equal to it are accepted, otherwise
+ * the target's own commit is made).  Per sequence, nodes 0..N-1 with node 0
+ * the root state:
+ *   parent[n] (node 0's is ignored), node_pos[n], node_tok[n]: node n is its
+ *     parent plus the commit of node_tok[n] at position node_pos[n];
+ *   target_pos[n]: the position the target's own policy commits next at
+ *     state n (an input: the policy belongs to the model);
+ *   logits[n][V], gumbel[n][V]: the target's logits at that position in
+ *     node n's copy and the noise row of its absolute position (gumbel may
+ *     be NULL when temperature == 0).
+ * The target's own token at n is svo_coupled_choice of its row.  From the
+ * root, the walk moves to the child (smallest index if several) whose
+ * commit equals the target's own commit at the current node, and stops when
+ * none does.
+ * Outputs: path_len[b] = accepted edges L; path[b][0..L] = the nodes of the
+ * walk (root first), -1 after; commit_pos[b], commit_tok[b] = the target's
+ * own commit at the last node; target_tok[b][n] = the target's own token at
+ * every node.  Returns SVO_BAD_ARG for a parent index outside [0, n).
+ */
+int svo_tree_verify(const float *logits, const float *gumbel, const int32_t *parent, const int32_t *node_pos,
+                    const int32_t *node_tok, const int32_t *target_pos, int batch, int N, int64_t V,
+                    float temperature, int32_t *path_len, int32_t *path, int32_t *commit_pos,
+                    int32_t *commit_tok, int32_t *target_tok) {
+    if (batch < 0 || N < 1 || V < 1 || !(temperature >= 0.f)) return SVO_BAD_ARG;
+    const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.0f;  /* 0: greedy */
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *pb = parent + (size_t)b * N;
+        for (int n = 1; n < N; ++n)
+            if (pb[n] < 0 || pb[n] >= n) return SVO_BAD_ARG;
+        int32_t *tt = target_tok + (size_t)b * N;
+        for (int n = 0; n < N; ++n) {
+            const size_t row = (size_t)b * N + n;
+            tt[n] = (int32_t)svo_coupled_choice(logits + row * V, gumbel ? gumbel + row * V : NULL, V, inv_t);
+        }
+        const int32_t *tp = target_pos + (size_t)b * N;
+        const int32_t *np = node_pos + (size_t)b * N, *nt = node_tok + (size_t)b * N;
+        int32_t *pa = path + (size_t)b * N;
+        for (int n = 0; n < N; ++n) pa[n] = -1;
+        int cur = 0, L = 0;
+        pa[0] = 0;
+        while (L < N - 1) {  /* a walk down a tree has at most N - 1 edges */
+            int next = -1;
+            for (int c = 1; c < N; ++c)
+                if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }
+            if (next < 0) break;
+            cur = next;
+            pa[++L] = cur;
+        }
+        path_len[b] = L;
+        commit_pos[b] = tp[cur];
+        commit_tok[b] = tt[cur];
+    }
+    return SVO_OK;
+}

@@ -805,6 +805,7 @@ def all_pins(o):
     all_route_pins(o)
     all_copies_pins(o)
     all_cache_pins(o)
+    all_tree_pins(o)
 
 
 # ---------------------------------------------------------------- paged cache, commit, append
@@ -957,3 +958,116 @@ def all_cache_pins(o):
     pin_commit_invariants(o)
     pin_append_roundtrip(o)
     pin_append_rotation(o)
+
+
+# ---------------------------------------------------------------- draft-tree verification
+def pin_tree_golden(o):
+    g = json.load(open(os.path.join(GOLDEN, "tree_tiny.json")))
+    pl, path, cp, ct, tt = o.tree_verify(np.array([g["logits"]], np.float32), None, np.array([g["parent"]]),
+                                         np.array([g["node_pos"]]), np.array([g["node_tok"]]),
+                                         np.array([g["target_pos"]]), g["temperature"])
+    assert int(pl[0]) == g["path_len"] and path[0].tolist() == g["path"]
+    assert int(cp[0]) == g["commit_pos"] and int(ct[0]) == g["commit_tok"]
+    assert tt[0].tolist() == g["target_tok"]
+
+
+def _chain_from_coupled(lt, gum, tok, tau, gamma):
+    """A draft chain of gamma commits in draft order as a tree: node r (1..gamma)
+    commits slot o_r; node r's target row is slot o_{r+1}'s."""
+    n, B, V = lt.shape
+    N = gamma + 1
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (n, 1))
+    node_pos, node_tok = np.full((n, N), -1, np.int32), np.full((n, N), -1, np.int32)
+    tpos = np.zeros((n, N), np.int32)
+    L_rows = np.zeros((n, N, V), np.float32)
+    G_rows = np.zeros((n, N, V), np.float32)
+    for b in range(n):
+        o = np.argsort(tau[b])                 # o[r - 1] = slot with tau = r
+        for r in range(1, N):
+            node_pos[b, r], node_tok[b, r] = o[r - 1], tok[b, o[r - 1]]
+        for r in range(N):
+            s = o[min(r, gamma - 1)] if r < gamma else o[gamma - 1]
+            tpos[b, r] = s
+            L_rows[b, r], G_rows[b, r] = lt[b, s], gum[b, s]
+    return L_rows, G_rows, parent, node_pos, node_tok, tpos
+
+
+def pin_tree_chain_is_coupled(o):
+    """A chain of draft commits in draft order is verified exactly as the
+    shared-noise verification of the same steps: the same number of accepted
+    edges, and the same committed target token after a rejection."""
+    r = np.random.default_rng(120)
+    n, B, V, gamma = 40, 6, 7, 5
+    for T in (1.0, 0.0):
+        lt = r.normal(0, 1, (n, B, V)).astype(np.float32)
+        gum = (-np.log(-np.log(r.random((n, B, V))))).astype(np.float32)
+        tau = np.stack([r.permutation(B) + 1 for _ in range(n)]).astype(np.int32)
+        choice = np.stack([[o.coupled_choice(lt[b, k], gum[b, k], T) for k in range(B)] for b in range(n)])
+        tok = np.where(r.random((n, B)) < 0.7, choice, (choice + 1) % V).astype(np.int32)
+        L_c, ot_c, _ = o.accept_coupled(lt, gum if T > 0 else None, tok, tau, gamma, T)
+        rows = _chain_from_coupled(lt, gum, tok, tau, gamma)
+        pl, path, cp, ct, tt = o.tree_verify(rows[0], rows[1] if T > 0 else None, *rows[2:], T)
+        assert np.array_equal(pl, L_c), (pl, L_c)
+        for b in range(n):
+            if L_c[b] < gamma:
+                o_next = int(np.argsort(tau[b])[L_c[b]])
+                assert ct[b] == ot_c[b, o_next] and cp[b] == o_next
+            assert path[b, :pl[b] + 1].tolist() == list(range(pl[b] + 1))
+
+
+def pin_tree_bruteforce(o):
+    """Random trees (siblings commit distinct (position, token) pairs): the
+    walk visits exactly the nodes whose every edge from the root equals the
+    target's own commit at the edge's parent, in depth order, and commits the
+    target's own at the deepest of them."""
+    r = np.random.default_rng(121)
+    for trial in range(300):
+        N, V, P = int(r.integers(1, 10)), int(r.integers(2, 4)), 3
+        parent = [-1] + [int(r.integers(0, n)) for n in range(1, N)]
+        used = {}
+        pos, tok = [-1] * N, [-1] * N
+        for n in range(1, N):
+            while True:
+                pv = (int(r.integers(0, P)), int(r.integers(0, V)))
+                if pv not in used.setdefault(parent[n], set()):
+                    used[parent[n]].add(pv)
+                    break
+            pos[n], tok[n] = pv
+        tpos = [int(r.integers(0, P)) for _ in range(N)]
+        T = float(r.choice([0.0, 0.7]))
+        lt = r.normal(0, 1, (1, N, V)).astype(np.float32)
+        gum = (-np.log(-np.log(r.random((1, N, V))))).astype(np.float32)
+        pl, path, cp, ct, tt = o.tree_verify(lt, gum, np.array([parent]), np.array([pos]), np.array([tok]),
+                                             np.array([tpos]), T)
+        own = [o.coupled_choice(lt[0, n], gum[0, n], T) for n in range(N)]
+        ok = [False] * N
+        ok[0] = True
+        for n in range(1, N):                  # parents come first
+            p = parent[n]
+            ok[n] = ok[p] and pos[n] == tpos[p] and tok[n] == own[p]
+        chain = [n for n in range(N) if ok[n]]
+        assert path[0, :pl[0] + 1].tolist() == chain, (trial, chain, path[0])
+        last = chain[-1]
+        assert cp[0] == tpos[last] and ct[0] == own[last] and tt[0].tolist() == own
+
+
+def pin_tree_rejects_bad_parent(o):
+    bad = np.array([[-1, 0, 3, 1]], np.int32)   # node 2's parent comes after it
+    z = np.zeros((1, 4), np.int32)
+    try:
+        o.tree_verify(np.zeros((1, 4, 3), np.float32), None, bad, z, z, z, 0.0)
+    except oracle_error():
+        return
+    raise AssertionError("a parent after its child was accepted")
+
+
+def oracle_error():
+    import oracle
+    return oracle.OracleError
+
+
+def all_tree_pins(o):
+    pin_tree_golden(o)
+    pin_tree_chain_is_coupled(o)
+    pin_tree_bruteforce(o)
+    pin_tree_rejects_bad_parent(o)

@@ -61,6 +61,13 @@ MUTANTS = [
     ("append rotates at the row index", "const double pos = (double)P + (double)i;", "const double pos = (double)i;"),
     ("append leaves the length", "prefix_lens[b] = P + n;", "prefix_lens[b] = P;"),
     ("append refuses an exact fit", "if ((long long)P + n > capacity) { status[b] = 1; continue; }", "if ((long long)P + n >= capacity) { status[b] = 1; continue; }"),
+    ("tree follows any earlier node", "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }",
+     "if (pb[c] <= cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }"),
+    ("tree ignores the commit position", "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }",
+     "if (pb[c] == cur && nt[c] == tt[cur]) { next = c; break; }"),
+    ("tree compares the child's own choice", "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }",
+     "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[c]) { next = c; break; }"),
+    ("tree commits at the root", "commit_pos[b] = tp[cur];", "commit_pos[b] = tp[0];"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

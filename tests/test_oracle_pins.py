@@ -165,3 +165,19 @@ def test_append_roundtrip(o):
 
 def test_append_rotation(o):
     pins.pin_append_rotation(o)
+
+
+def test_tree_golden(o):
+    pins.pin_tree_golden(o)
+
+
+def test_tree_chain_is_coupled(o):
+    pins.pin_tree_chain_is_coupled(o)
+
+
+def test_tree_bruteforce(o):
+    pins.pin_tree_bruteforce(o)
+
+
+def test_tree_rejects_bad_parent(o):
+    pins.pin_tree_rejects_bad_parent(o)

@@ -67,6 +67,10 @@ def load(path: str | None = None):
     lib.spec_verify_attn_paged.restype = I
     lib.spec_verify_attn_paged.argtypes = [V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, I, I, I, I, D, F, V,
                                            SZ, V]
+    lib.spec_verify_tree_workspace_size.restype = SZ
+    lib.spec_verify_tree_workspace_size.argtypes = [I, I, I64]
+    lib.spec_verify_tree.restype = I
+    lib.spec_verify_tree.argtypes = [V, V, V, V, V, V, I, I, I64, F, V, V, V, V, V, V, SZ, V]
     lib.spec_verify_check_tau.restype = I
     lib.spec_verify_check_tau.argtypes = [V, I, I, V, V]
     lib.spec_verify_commit.restype = I
@@ -214,3 +218,16 @@ def spec_verify_kv_append(k_rows, v_rows, src_stride, n_append, k_pages, v_pages
 
 def spec_verify_check_tau(tau, batch, block, bad, stream=None) -> None:
     _check(load().spec_verify_check_tau(_ptr(tau), batch, block, _ptr(bad), _stream(stream)))
+
+
+def spec_verify_tree_workspace_size(batch, n_nodes, vocab) -> int:
+    return int(load().spec_verify_tree_workspace_size(batch, n_nodes, vocab))
+
+
+def spec_verify_tree(target_logits, gumbel, parent, node_pos, node_tok, target_pos, batch, n_nodes, vocab,
+                     temperature, path_len, path, commit_pos, commit_tok, target_tok, workspace, workspace_bytes,
+                     stream=None) -> None:
+    _check(load().spec_verify_tree(_ptr(target_logits), _ptr(gumbel), _ptr(parent), _ptr(node_pos), _ptr(node_tok),
+                                   _ptr(target_pos), batch, n_nodes, int(vocab), float(temperature), _ptr(path_len),
+                                   _ptr(path), _ptr(commit_pos), _ptr(commit_tok), _ptr(target_tok),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))

@@ -278,6 +278,32 @@ int spec_verify_accept_coupled(const float *target_logits, const float *gumbel, 
                                          target_tokens, workspace, (hipStream_t)stream));
 }
 
+size_t spec_verify_tree_workspace_size(int batch, int n_nodes, int64_t vocab) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1 || vocab > (1ll << 21)) return 0;
+    return sv::coupled_plan(batch, n_nodes, n_nodes, vocab).ws_total;
+}
+
+int spec_verify_tree(const float *target_logits, const float *gumbel, const int32_t *parent, const int32_t *node_pos,
+                     const int32_t *node_tok, const int32_t *target_pos, int batch, int n_nodes, int64_t vocab,
+                     float temperature, int32_t *path_len, int32_t *path, int32_t *commit_pos, int32_t *commit_tok,
+                     int32_t *target_tok, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1 || vocab > (1ll << 21)) return SV_E_SHAPE;
+    if ((long long)batch * n_nodes * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!(temperature >= 0.f) || !isfinite(temperature)) return SV_E_SHAPE;
+    if (!target_logits || !parent || !node_pos || !node_tok || !target_pos || !path_len || !path || !commit_pos ||
+        !commit_tok)
+        return SV_E_NULL;
+    if (temperature > 0.f && !gumbel) return SV_E_NULL;
+    if (!aligned16(target_logits) || (gumbel && !aligned16(gumbel))) return SV_E_ALIGN;
+    const sv::CoupledPlan p = sv::coupled_plan(batch, n_nodes, n_nodes, vocab);
+    if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
+    if (!aligned16(workspace)) return SV_E_ALIGN;
+    const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.f;
+    return map_launch(sv::launch_tree(p, target_logits, temperature > 0.f ? gumbel : nullptr, parent, node_pos,
+                                      node_tok, target_pos, batch, n_nodes, vocab, inv_t, path_len, path, commit_pos,
+                                      commit_tok, target_tok, workspace, (hipStream_t)stream));
+}
+
 size_t spec_verify_route_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))

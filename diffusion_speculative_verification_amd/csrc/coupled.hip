@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(256) coupled_partial_kernel(const float *__res
     __shared__ float red_s[4];
     __shared__ int32_t red_i[4];
     const int row = blockIdx.x / n_vsplit, sp = blockIdx.x % n_vsplit;
-    if (tau[row] > gamma) return;  // slot not verified in this call
+    if (tau && tau[row] > gamma) return;  // slot not verified in this call (no tau: every row)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float bs = -INFINITY;
     int32_t bi = INT32_MAX;
@@ -146,6 +146,79 @@ __global__ void __launch_bounds__(64) coupled_scan_kernel(const int32_t *__restr
         if (target_tokens) target_tokens[row] = choice;
     }
     if (lane == 0) accept_len[b] = L;
+}
+
+// Draft-tree verification ("SPOT", 核心方法 second step and 方法步骤详情 验证),
+// one wave per sequence: lane n merges node n's partials into the target's
+// own token at its next commit position; then, from the root, each step is
+// one ballot over the nodes for the child whose (position, token) equals
+// the target's own commit at the current node (the smallest such index).
+// A walk has at most n_nodes - 1 edges, so the loop ends whatever the
+// parent array holds; node 0 is the root and is never taken as a child.
+__global__ void __launch_bounds__(64) tree_scan_kernel(const Best *__restrict__ parts, const int32_t *__restrict__ parent,
+                                                       const int32_t *__restrict__ node_pos,
+                                                       const int32_t *__restrict__ node_tok,
+                                                       const int32_t *__restrict__ target_pos, int n_nodes,
+                                                       int n_vsplit, int32_t *path_len, int32_t *path,
+                                                       int32_t *commit_pos, int32_t *commit_tok, int32_t *target_tok) {
+    const int lane = threadIdx.x, b = blockIdx.x;
+    const bool in = lane < n_nodes;
+    const size_t row = (size_t)b * n_nodes + (in ? lane : 0);
+    const int par = in ? parent[row] : -2, pos = in ? node_pos[row] : -1, tok = in ? node_tok[row] : -1;
+    const int tpos = in ? target_pos[row] : -1;
+    float bs = -INFINITY;
+    int32_t bi = INT32_MAX;
+    if (in) {
+#pragma unroll 4
+        for (int i = 0; i < n_vsplit; ++i) {
+            const Best p = parts[row * n_vsplit + i];
+            if (better(p.s, p.i, bs, bi)) { bs = p.s; bi = p.i; }
+        }
+    }
+    const int own = in ? bi : -1;  // the target's own token at this node's next commit
+    if (in && target_tok) target_tok[row] = own;
+    int cur = 0, L = 0;
+    for (; L < n_nodes - 1; ++L) {
+        const int cpos = __shfl(tpos, cur), ctok = __shfl(own, cur);
+        const unsigned long long m = __ballot(in && lane > 0 && par == cur && pos == cpos && tok == ctok);
+        if (!m) break;
+        cur = __ffsll((long long)m) - 1;
+        if (lane == 0) path[(size_t)b * n_nodes + L + 1] = cur;
+    }
+    if (in && lane > L) path[row] = -1;
+    if (lane == 0) {
+        path[(size_t)b * n_nodes] = 0;
+        path_len[b] = L;
+    }
+    const int fpos = __shfl(tpos, cur), ftok = __shfl(own, cur);
+    if (lane == 0) { commit_pos[b] = fpos; commit_tok[b] = ftok; }
+}
+
+hipError_t launch_tree(const CoupledPlan &p, const float *logits, const float *noise, const int32_t *parent,
+                       const int32_t *node_pos, const int32_t *node_tok, const int32_t *target_pos, int batch,
+                       int n_nodes, int64_t vocab, float inv_t, int32_t *path_len, int32_t *path, int32_t *commit_pos,
+                       int32_t *commit_tok, int32_t *target_tok, void *ws, hipStream_t st) {
+    Best *parts = (Best *)ws;
+    const dim3 g1((unsigned)((size_t)p.rows * p.n_vsplit));
+    const bool vec = (vocab & 3) == 0, greedy = !(inv_t > 0.f);
+    const int32_t *no_tau = nullptr;
+    if (vec && greedy)
+        hipLaunchKernelGGL((coupled_partial_kernel<true, true>), g1, dim3(256), 0, st, logits, noise, no_tau, parts,
+                           n_nodes, vocab, p.n_vsplit, inv_t);
+    else if (vec)
+        hipLaunchKernelGGL((coupled_partial_kernel<true, false>), g1, dim3(256), 0, st, logits, noise, no_tau, parts,
+                           n_nodes, vocab, p.n_vsplit, inv_t);
+    else if (greedy)
+        hipLaunchKernelGGL((coupled_partial_kernel<false, true>), g1, dim3(256), 0, st, logits, noise, no_tau, parts,
+                           n_nodes, vocab, p.n_vsplit, inv_t);
+    else
+        hipLaunchKernelGGL((coupled_partial_kernel<false, false>), g1, dim3(256), 0, st, logits, noise, no_tau, parts,
+                           n_nodes, vocab, p.n_vsplit, inv_t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tree_scan_kernel, dim3(batch), dim3(64), 0, st, parts, parent, node_pos, node_tok, target_pos,
+                       n_nodes, p.n_vsplit, path_len, path, commit_pos, commit_tok, target_tok);
+    return hipGetLastError();
 }
 
 CoupledPlan coupled_plan(int batch, int block, int gamma, int64_t vocab) {

@@ -97,6 +97,11 @@ hipError_t launch_route(const RoutePlan &p, const float *probs, const int32_t *t
                         int gamma, int64_t vocab, int estimator, double param, float *khat, float *alpha_hat,
                         void *ws, hipStream_t st);
 
+hipError_t launch_tree(const CoupledPlan &p, const float *logits, const float *noise, const int32_t *parent,
+                       const int32_t *node_pos, const int32_t *node_tok, const int32_t *target_pos, int batch,
+                       int n_nodes, int64_t vocab, float inv_t, int32_t *path_len, int32_t *path, int32_t *commit_pos,
+                       int32_t *commit_tok, int32_t *target_tok, void *ws, hipStream_t st);
+
 hipError_t launch_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, hipStream_t st);
 
 hipError_t launch_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,

@@ -87,6 +87,20 @@ class StepBuffers:
                                                          c.n_qh, c.n_kvh, c.head_dim)
             self.paged_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.paged_ws_bytes = n
+        if "tree" in parts:
+            N = c.n_copies
+            self.tree_logits = up(inputs["tree_logits"])
+            self.tree_gumbel = up(inputs["tree_gumbel"])
+            self.parent, self.node_pos = up(inputs["parent"]), up(inputs["node_pos"])
+            self.node_tok, self.target_pos = up(inputs["node_tok"]), up(inputs["target_pos"])
+            self.path_len = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.path = torch.empty((c.batch, N), dtype=torch.int32, device=device)
+            self.commit_pos = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.commit_tok = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.tree_target_tok = torch.empty((c.batch, N), dtype=torch.int32, device=device)
+            n = sv.spec_verify_tree_workspace_size(c.batch, N, c.vocab)
+            self.tree_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.tree_ws_bytes = n
         if "route" in parts:
             if not hasattr(self, "draft_probs"):
                 self.draft_probs = up(inputs["draft_probs"])
@@ -172,6 +186,15 @@ class StepBuffers:
         sv.spec_verify_kv_append(k_rows, v_rows, src_stride, self.n_append, self.k_pages, self.v_pages,
                                  self.block_table, self.prefix_lens, self.append_status, self.dtype_code, c.batch,
                                  c.page_size, self.max_pages, self.n_pages, c.n_kvh, c.head_dim, theta, stream)
+
+    def tree(self, temperature=None, stream=None):
+        """Draft-tree verification ("SPOT") of the case's n_copies nodes."""
+        c = self.case
+        T = c.temperature if temperature is None else temperature
+        sv.spec_verify_tree(self.tree_logits, self.tree_gumbel if T > 0 else None, self.parent, self.node_pos,
+                            self.node_tok, self.target_pos, c.batch, c.n_copies, c.vocab, T, self.path_len,
+                            self.path, self.commit_pos, self.commit_tok, self.tree_target_tok, self.tree_ws,
+                            self.tree_ws_bytes, stream)
 
     def route(self, estimator: str, param: float, stream=None):
         """S2D2 verify-routing estimate K of every sequence (margin or entropy)."""

@@ -33,6 +33,13 @@ numpy default_rng(SeedSequence([s, t, b]))):
       iid N(0,1), copy-major (the root and draft states of the block)
   t=14 per-sequence prompt length (ragged cases): uniform integer in
       [P/2, P]; otherwise P
+  t=16 draft tree of case.n_copies nodes (root = node 0): each node's parent
+      among the three nodes before it, the target's next commit position at
+      each node (a position its path has not committed), target logits and
+      Gumbel rows per node (as t=6 and t=10, at that position), and a
+      synthetic drafter: a child commits at its parent's target position the
+      draft's own Gumbel-max token (draft logits = target + N(0,1)) with
+      probability 3/4, otherwise another (position, token); siblings differ
   t=15 (one stream for the batch) the page permutation of a paged cache: the
       sequences' page tables take consecutive runs of a random permutation of
       all pages, with one spare page per sequence that no table names
@@ -269,7 +276,54 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
             list(ex.map(fill_cpl, range(n)))
     if "paged" in parts:
         _paged(case, out, seqs)
+    if "tree" in parts:
+        _tree(case, out, seqs, threads)
     return out
+
+
+def _tree(case: Case, out: dict, seqs, threads: int) -> None:
+    """Draft-tree inputs (tensor id 16): parent, node_pos, node_tok, target_pos
+    [n][N], tree_logits and tree_gumbel [n][N][V], N = case.n_copies."""
+    n, N, V, B = len(seqs), case.n_copies, case.vocab, case.block
+    shape = (n, N)
+    out["parent"], out["node_pos"] = np.full(shape, -1, np.int32), np.full(shape, -1, np.int32)
+    out["node_tok"], out["target_pos"] = np.full(shape, -1, np.int32), np.zeros(shape, np.int32)
+    out["tree_logits"] = np.empty((n, N, V), np.float32)
+    out["tree_gumbel"] = np.empty((n, N, V), np.float32)
+
+    def fill(i):
+        r = _rng(case, 16, seqs[i])
+        tgt = r.standard_normal((N, V)) * np.sqrt(case.target_var)
+        u = np.maximum(r.random((N, V)), np.finfo(np.float64).tiny)
+        g = -np.log(-np.log(u))
+        drf = tgt + r.standard_normal((N, V)) * np.sqrt(case.draft_var)
+        out["tree_logits"][i], out["tree_gumbel"][i] = tgt.astype(np.float32), g.astype(np.float32)
+        used = [set() for _ in range(N)]       # positions committed on each node's path
+        kids = [set() for _ in range(N)]       # (position, token) of each node's children
+        for k in range(N):
+            if k > 0:
+                p = int(r.integers(max(0, k - 3), k))
+                while True:
+                    if r.random() < 0.75:
+                        pos = int(out["target_pos"][i, p])
+                        if case.temperature > 0:
+                            sc = drf[p].astype(np.float32) * (np.float32(1) / np.float32(case.temperature)) + \
+                                out["tree_gumbel"][i, p]
+                        else:
+                            sc = drf[p]
+                        tok = int(np.argmax(sc))
+                    else:
+                        pos, tok = int(r.integers(0, B)), int(r.integers(0, V))
+                    if (pos, tok) not in kids[p] and pos not in used[p]:
+                        break
+                kids[p].add((pos, tok))
+                out["parent"][i, k], out["node_pos"][i, k], out["node_tok"][i, k] = p, pos, tok
+                used[k] = used[p] | {pos}
+            free = [q for q in range(B) if q not in used[k]] or [0]
+            out["target_pos"][i, k] = free[int(r.integers(0, len(free)))]
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(n)))
 
 
 _PAGE_FILL = 8192.0  # rows no prompt row maps to (bf16-exact; a read of one would show)

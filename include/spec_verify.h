@@ -18,9 +18,9 @@
  *     the longest accepted prefix, and a resample at the first rejection from
  *     the residual (P_target - P_draft)^+ (page "S2D2: Fast Decoding for
  *     Diffusion LLMs via Training-Free Self-Speculation", 方法步骤 (5)).
- * Around it: shared-noise and greedy verification and the multi-copy
- * attention of "SPOT: Enhancing Speculative Decoding for Diffusion Language
- * Models via Commit-Order Prediction"; S2D2's verify-routing estimate; a
+ * Around it: shared-noise and greedy verification, the multi-copy
+ * attention and draft-tree verification of "SPOT: Enhancing Speculative
+ * Decoding for Diffusion Language Models via Commit-Order Prediction"; S2D2's verify-routing estimate; a
  * paged prompt cache with per-sequence lengths, the commit step and the
  * cache append (each call below cites its passage).
  *
@@ -178,6 +178,44 @@ int spec_verify_attn_paged(const void *q, const void *k_new, const void *v_new, 
                            int max_prefix, int page_size, int max_pages, int n_pages, int n_qh, int n_kvh,
                            int head_dim, double rope_theta, float softmax_scale, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace spec_verify_tree needs for these sizes. */
+size_t spec_verify_tree_workspace_size(int batch, int n_nodes, int64_t vocab);
+
+/*
+ * Verification of a draft tree ("SPOT: Enhancing Speculative Decoding for
+ * Diffusion Language Models via Commit-Order Prediction", 核心方法, second
+ * step: a tree of draft states, each child its parent plus one commit
+ * (position, token); 方法步骤详情, 验证: one forward gives the target's own next
+ * commit at the root and at every draft state, edges equal to it are
+ * accepted, otherwise the target's own commit is made).  Per sequence,
+ * nodes 0..n_nodes-1, node 0 the root state (its copy the root copy of
+ * spec_verify_attn_copies):
+ *   parent [batch][n_nodes]: node n's parent (node 0's is ignored);
+ *   node_pos, node_tok [batch][n_nodes]: node n is its parent plus the
+ *     commit of node_tok at position node_pos;
+ *   target_pos [batch][n_nodes]: the position the target's own policy
+ *     commits next at state n (the policy belongs to the model);
+ *   target_logits, gumbel [batch][n_nodes][vocab] float32: the target's
+ *     logits at that position in node n's copy, and the noise-table row of
+ *     that position's absolute index (gumbel may be NULL when temperature
+ *     == 0).
+ * The target's own token at node n is argmax_v fmaf(l_v, 1/T, g_v) in
+ * float32 (T == 0: argmax_v l_v), the smallest v among equal scores.  From
+ * the root the walk moves to the child (smallest index if several) whose
+ * commit equals the target's own commit at the current node.
+ * Outputs: path_len [batch] = accepted edges L; path [batch][n_nodes] = the
+ * nodes of the walk (root first), -1 after; commit_pos, commit_tok [batch] =
+ * the target's own commit at the last node; target_tok [batch][n_nodes]
+ * (optional) = the target's own token at every node.
+ * 1 <= n_nodes <= 64, 1 <= vocab <= 2^21, temperature >= 0 finite.  A walk
+ * has at most n_nodes - 1 edges, so a malformed parent array gives a wrong
+ * path but the call still ends.
+ */
+int spec_verify_tree(const float *target_logits, const float *gumbel, const int32_t *parent, const int32_t *node_pos,
+                     const int32_t *node_tok, const int32_t *target_pos, int batch, int n_nodes, int64_t vocab,
+                     float temperature, int32_t *path_len, int32_t *path, int32_t *commit_pos, int32_t *commit_tok,
+                     int32_t *target_tok, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Validation of the step labels ("SimSD: Simple Speculative Decoding in

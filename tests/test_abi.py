@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
 
@@ -190,6 +190,28 @@ def test_paged_argument_checks(lib):
     assert call(tau=None, C=9, wb=0) == sv.SV_E_WORKSPACE   # copies need no tau (stops before any launch)
     assert call(kp=None) == sv.SV_E_NULL
     assert call(o=A + 4) == sv.SV_E_ALIGN
+    assert call(wb=0) == sv.SV_E_WORKSPACE
+
+
+def test_tree_argument_checks(lib):
+    f = lib.spec_verify_tree
+    ok = dict(l=A, g=A, par=A, pos=A, tok=A, tp=A, b=4, n=9, V=151936, T=1.0, pl=A, path=A, cp=A, ct=A, tt=A,
+              ws=A, wb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["l"], a["g"], a["par"], a["pos"], a["tok"], a["tp"], a["b"], a["n"], a["V"], a["T"], a["pl"],
+                 a["path"], a["cp"], a["ct"], a["tt"], a["ws"], a["wb"], None)
+    assert sv.spec_verify_tree_workspace_size(4, 9, 151936) > 0
+    assert sv.spec_verify_tree_workspace_size(4, 65, 151936) == 0
+    assert call(n=65) == sv.SV_E_SHAPE
+    assert call(n=0) == sv.SV_E_SHAPE
+    assert call(T=-1.0) == sv.SV_E_SHAPE
+    assert call(T=float("inf")) == sv.SV_E_SHAPE
+    assert call(g=None) == sv.SV_E_NULL            # T > 0 needs the noise rows
+    assert call(par=None) == sv.SV_E_NULL
+    assert call(l=A + 4) == sv.SV_E_ALIGN
     assert call(wb=0) == sv.SV_E_WORKSPACE
 
 

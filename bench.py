@@ -28,7 +28,8 @@ entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
 verification step instead: attention over C copies of the block (the root
 state and D = C - 1 draft states, spec_verify_attn_copies) followed by
 shared-noise (or, with --verify greedy, greedy) verification of the D draft
-steps; gamma = D.  --paged PS keeps the prompt caches in pages of PS rows
+steps; gamma = D.  --copies C --tree verifies a draft tree of the C states
+instead of a chain (spec_verify_tree).  --paged PS keeps the prompt caches in pages of PS rows
 (spec_verify_attn_paged; --ragged gives each sequence its own prompt length)
 and ends each step with the commit step and the cache append of finished
 blocks (spec_verify_commit, spec_verify_kv_append); the prompt lengths and the
@@ -104,6 +105,14 @@ def coupled_bytes(c, greedy: bool) -> float:
     return rows * (1 if greedy else 2) + small
 
 
+def tree_bytes(c, greedy: bool) -> float:
+    """Algorithmic HBM bytes of one draft-tree verification call: the float32
+    target row of every node once, its noise row once (not read when greedy),
+    plus the tree arrays and the outputs."""
+    rows = 4.0 * c.batch * c.n_copies * c.vocab
+    return rows * (1 if greedy else 2) + c.batch * (c.n_copies * 4 * 6 + 12)
+
+
 def route_bytes(c) -> float:
     """Algorithmic HBM bytes of one routing call: the float32 draft
     distribution of every verified slot once, plus tau and the outputs."""
@@ -130,7 +139,7 @@ def measured_traffic(call: str):
 
 
 def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
-                 paged=False, attn_budget_s=20.0) -> dict:
+                 paged=False, tree=False, attn_budget_s=20.0) -> dict:
     """The CPU oracle on this host over the same workload (one step).  The
     attention is timed over the first sequences of the batch until
     `attn_budget_s` has passed and scaled to the whole batch."""
@@ -166,7 +175,11 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
             break
     t_attn = (time.perf_counter() - t) * case.batch / n_seq
     t = time.perf_counter()
-    if verify == "rejection":
+    if tree:
+        o.tree_verify(inp["tree_logits"], inp["tree_gumbel"] if temperature > 0 else None, inp["parent"],
+                      inp["node_pos"], inp["node_tok"], inp["target_pos"], temperature)
+        out_tokens = None
+    elif verify == "rejection":
         out_tokens = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
                               inp["uniforms"], case.gamma)[1]
     else:
@@ -243,6 +256,8 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="PS",
                     help="prompt caches in pages of PS rows, plus the commit step and the cache append")
     ap.add_argument("--ragged", action="store_true", help="with --paged: per-sequence prompt lengths")
+    ap.add_argument("--tree", action="store_true",
+                    help="with --copies: verify a draft tree of the C states instead of a chain")
     ap.add_argument("--copies", type=int, default=0,
                     help="SPOT multi-copy verification over C copies of the block (root + C-1 draft states)")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
@@ -284,6 +299,10 @@ def main():
                   file=sys.stderr)
             sys.exit(2)
         case = case.with_(n_copies=copies, gamma=copies - 1)
+    tree = bool(args.tree)
+    if tree and not copies:
+        print("--tree verifies the draft states of --copies C", file=sys.stderr)
+        sys.exit(2)
     paged = args.paged > 0
     if paged:
         if copies or args.route != "none" or args.paged % 64:
@@ -293,7 +312,7 @@ def main():
     T = 0.0 if verify == "greedy" else args.temperature
     parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
     if copies:
-        parts = ("copies", "coupled")
+        parts = ("copies", "tree") if tree else ("copies", "coupled")
     if paged:
         parts = parts + ("paged",)
     route = args.route
@@ -328,7 +347,9 @@ def main():
         s.block_tokens.copy_(s.block_tokens0)
 
     def epilogue(s):
-        if verify == "rejection":
+        if tree:
+            s.tree(temperature=T)
+        elif verify == "rejection":
             s.accept()
         else:
             s.accept_coupled(temperature=T)
@@ -382,7 +403,7 @@ def main():
     ms_step = total_ms / K
     attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
     acc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
-    L = (sets[0].accept_len if verify == "rejection" else sets[0].cpl_accept_len).cpu()
+    L = (sets[0].path_len if tree else sets[0].accept_len if verify == "rejection" else sets[0].cpl_accept_len).cpu()
     n_rej = int((L < case.gamma).sum())
     slots = case.batch * case.gamma
     value = slots / (ms_step * 1e-3)
@@ -390,8 +411,11 @@ def main():
     prompt_rows = int(inp["prefix_lens"].sum()) if paged else None
     a_bytes, a_flops = attn_bytes(case, copies, prompt_rows), attn_flops(case, copies, prompt_rows)
     attn_call = "spec_verify_attn_copies" if copies else "spec_verify_attn_paged" if paged else "spec_verify_attn"
-    c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
-    acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
+    if tree:
+        c_bytes, acc_call = tree_bytes(case, T == 0), "spec_verify_tree"
+    else:
+        c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
+        acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
     # the attention is bound by whichever of HBM bytes and bf16 MFMA flops
     # takes longer at peak (the multi-copy layout does B-fold more flops per
     # prompt byte and crosses into the MFMA-bound side)
@@ -453,7 +477,7 @@ def main():
                                                                     peaks["hbm_read_gbs"]), 4)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged)
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree)
 
     out = {
         "metric": METRIC,
@@ -469,7 +493,8 @@ def main():
         "dtype": case.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{case.name} SPOT multi-copy verify step: {copies} copies (root + D={copies - 1} "
-                                f"draft states), gamma=D" if copies else f"{case.name} verify step") +
+                                f"draft states" + (" in a draft tree" if tree else "") + "), gamma=D"
+                                if copies else f"{case.name} verify step") +
                                f": batch {case.batch}, prefix {case.prefix_len}, "
                                f"B={case.block}, gamma={case.gamma}, {case.n_qh}/{case.n_kvh} heads, "
                                f"head_dim {case.head_dim}, "
@@ -482,7 +507,7 @@ def main():
                                    else "") + ", then commit and cache append"),
                    "route": None if route == "none" else {"estimator": route, "param": rparam},
                    "verify": verify, "temperature": None if verify == "rejection" else T,
-                   "copies": copies or None,
+                   "copies": copies or None, "tree": tree if copies else None,
                    "page_size": case.page_size if paged else None, "ragged": bool(case.ragged) if paged else None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,

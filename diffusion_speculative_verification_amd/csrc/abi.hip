@@ -25,6 +25,13 @@ int check_heads(int dtype, int batch, int block, int n_qh, int n_kvh, int head_d
 
 int map_launch(hipError_t e) { return e == hipSuccess ? SV_OK : SV_E_LAUNCH; }
 
+// the vocabulary-streaming calls: batch x rows (slots or nodes) x vocab
+// within the kernels' index ranges (grids of rows x vocab splits stay below
+// 2^31 workgroups)
+bool rows_ok(int batch, int rows, int64_t vocab) {
+    return (long long)batch * rows <= (1ll << 26) && (long long)batch * rows * vocab <= (1ll << 40);
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,7 +225,7 @@ int spec_verify_kv_append(const void *k_rows, const void *v_rows, int src_stride
 
 size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
-        vocab > (1ll << 21))
+        vocab > (1ll << 21) || !rows_ok(batch, block, vocab))
         return 0;
     return sv::accept_plan(batch, block, gamma, vocab).ws_total;
 }
@@ -230,7 +237,7 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs, con
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))
         return SV_E_SHAPE;
-    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!rows_ok(batch, block, vocab)) return SV_E_SHAPE;
     if (!target_logits || !draft_probs || !draft_tokens || !tau || !uniforms || !accept_len || !out_tokens)
         return SV_E_NULL;
     if (!aligned16(target_logits) || !aligned16(draft_probs) || !aligned16(draft_tokens) || !aligned16(tau) ||
@@ -246,7 +253,7 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs, con
 
 size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
-        vocab > (1ll << 21))
+        vocab > (1ll << 21) || !rows_ok(batch, block, vocab))
         return 0;
     return sv::coupled_plan(batch, block, gamma, vocab).ws_total;
 }
@@ -258,7 +265,7 @@ int spec_verify_accept_coupled(const float *target_logits, const float *gumbel, 
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))
         return SV_E_SHAPE;
-    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!rows_ok(batch, block, vocab)) return SV_E_SHAPE;
     if (!(temperature >= 0.f) || !isfinite(temperature)) return SV_E_SHAPE;
     if (!target_logits || !draft_tokens || !tau || !accept_len || !out_tokens) return SV_E_NULL;
     if (temperature > 0.f && !gumbel) return SV_E_NULL;
@@ -279,7 +286,9 @@ int spec_verify_accept_coupled(const float *target_logits, const float *gumbel, 
 }
 
 size_t spec_verify_tree_workspace_size(int batch, int n_nodes, int64_t vocab) {
-    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1 || vocab > (1ll << 21)) return 0;
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1 || vocab > (1ll << 21) ||
+        !rows_ok(batch, n_nodes, vocab))
+        return 0;
     return sv::coupled_plan(batch, n_nodes, n_nodes, vocab).ws_total;
 }
 
@@ -288,7 +297,7 @@ int spec_verify_tree(const float *target_logits, const float *gumbel, const int3
                      float temperature, int32_t *path_len, int32_t *path, int32_t *commit_pos, int32_t *commit_tok,
                      int32_t *target_tok, void *workspace, size_t workspace_bytes, void *stream) {
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1 || vocab > (1ll << 21)) return SV_E_SHAPE;
-    if ((long long)batch * n_nodes * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!rows_ok(batch, n_nodes, vocab)) return SV_E_SHAPE;
     if (!(temperature >= 0.f) || !isfinite(temperature)) return SV_E_SHAPE;
     if (!target_logits || !parent || !node_pos || !node_tok || !target_pos || !path_len || !path || !commit_pos ||
         !commit_tok)
@@ -299,6 +308,7 @@ int spec_verify_tree(const float *target_logits, const float *gumbel, const int3
     if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
     if (!aligned16(workspace)) return SV_E_ALIGN;
     const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.f;
+    if (temperature > 0.f && !isfinite(inv_t)) return SV_E_SHAPE;
     return map_launch(sv::launch_tree(p, target_logits, temperature > 0.f ? gumbel : nullptr, parent, node_pos,
                                       node_tok, target_pos, batch, n_nodes, vocab, inv_t, path_len, path, commit_pos,
                                       commit_tok, target_tok, workspace, (hipStream_t)stream));
@@ -306,7 +316,7 @@ int spec_verify_tree(const float *target_logits, const float *gumbel, const int3
 
 size_t spec_verify_route_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
-        vocab > (1ll << 21))
+        vocab > (1ll << 21) || !rows_ok(batch, block, vocab))
         return 0;
     return sv::route_plan(batch, block, gamma, vocab).ws_total;
 }
@@ -317,7 +327,7 @@ int spec_verify_route(const float *draft_probs, const int32_t *tau, int batch, i
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))
         return SV_E_SHAPE;
-    if ((long long)batch * block * vocab > (1ll << 40)) return SV_E_SHAPE;
+    if (!rows_ok(batch, block, vocab)) return SV_E_SHAPE;
     if (estimator != SV_ROUTE_MARGIN && estimator != SV_ROUTE_ENTROPY) return SV_E_UNSUPPORTED;
     if (!isfinite(param)) return SV_E_SHAPE;
     if (!draft_probs || !tau || !khat) return SV_E_NULL;

@@ -39,8 +39,11 @@
  *   - dtype SV_BF16: bfloat16 tensors, bf16 MFMA with fp32 accumulation.
  *     dtype SV_F32: float32 tensors and float32 arithmetic throughout.
  *   - Shape limits: 1 <= block <= 64, n_qh % n_kvh == 0, head_dim in
- *     {64, 128}, prefix_len >= 0, batch >= 1; accept: 1 <= gamma <= block,
- *     1 <= vocab <= 2^21.
+ *     {64, 128}, prefix_len >= 0, batch >= 1; the calls that stream a
+ *     vocabulary (accept, accept_coupled, route, tree): 1 <= gamma <= block,
+ *     1 <= vocab <= 2^21, batch * rows <= 2^26 and batch * rows * vocab <=
+ *     2^40 (rows = block, or n_nodes for the tree); the workspace-size calls
+ *     return 0 outside these limits.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

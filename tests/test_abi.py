@@ -96,6 +96,11 @@ def test_accept_argument_checks(lib):
     assert accept(lib, u=A + 4) == sv.SV_E_ALIGN
     assert accept(lib, ws=None) == sv.SV_E_WORKSPACE
     assert accept(lib, ws_bytes=8) == sv.SV_E_WORKSPACE
+    # batch * block beyond 2^26 rows, or batch * block * vocab beyond 2^40
+    assert accept(lib, batch=1 << 21, block=64, gamma=8, vocab=4) == sv.SV_E_SHAPE
+    assert accept(lib, batch=1 << 14, block=64, gamma=8, vocab=1 << 21) == sv.SV_E_SHAPE
+    assert sv.spec_verify_accept_workspace_size(1 << 21, 64, 8, 4) == 0
+    assert sv.spec_verify_route_workspace_size(1 << 21, 64, 8, 4) == 0
 
 
 def coupled(lib, **kw):
@@ -121,6 +126,7 @@ def test_coupled_argument_checks(lib):
     assert coupled(lib, g=A + 4) == sv.SV_E_ALIGN
     assert coupled(lib, tt=A + 4) == sv.SV_E_ALIGN
     assert coupled(lib, ws_bytes=4) == sv.SV_E_WORKSPACE
+    assert coupled(lib, batch=1 << 21, block=64, gamma=8, vocab=4) == sv.SV_E_SHAPE
 
 
 def route(lib, **kw):
@@ -209,6 +215,9 @@ def test_tree_argument_checks(lib):
     assert call(n=0) == sv.SV_E_SHAPE
     assert call(T=-1.0) == sv.SV_E_SHAPE
     assert call(T=float("inf")) == sv.SV_E_SHAPE
+    assert call(T=1e-45) == sv.SV_E_SHAPE          # 1/T overflows float32
+    assert call(b=1 << 21, n=64, V=4) == sv.SV_E_SHAPE  # more than 2^26 nodes
+    assert sv.spec_verify_tree_workspace_size(1 << 21, 64, 4) == 0
     assert call(g=None) == sv.SV_E_NULL            # T > 0 needs the noise rows
     assert call(par=None) == sv.SV_E_NULL
     assert call(l=A + 4) == sv.SV_E_ALIGN

@@ -1,6 +1,6 @@
 """Comparison rules between the HIP path and the CPU oracle.
 
-Tolerances (spec bar of the verification step):
+Tolerances of the verification step's parity bar:
   attention, float32 inputs: max |gpu - oracle| <= 1e-5
   attention, bf16 inputs:    max |gpu - oracle| <= 2e-2 and
                              ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2

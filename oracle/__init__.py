@@ -86,7 +86,7 @@ class Oracle:
         lib.svo_softmax.argtypes = [P, i64, P, P, P]
         lib.svo_residual.argtypes = [P, P, i64, dbl, P, P, P]
         lib.svo_residual.restype = i64
-        lib.svo_accept.argtypes = [P, P, P, P, P, i32, i32, i32, i64, P, P, P, P]
+        lib.svo_accept.argtypes = [P, P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P, P]
         lib.svo_coupled_choice.argtypes = [P, P, i64, ctypes.c_float]
         lib.svo_coupled_choice.restype = i64
         lib.svo_accept_coupled.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, P, P, P]
@@ -280,10 +280,12 @@ class Oracle:
         tok = self.lib.svo_residual(_p(l), _p(pphi), V, float(u), _p(cdf), _p(Z), _p(ut))
         return int(tok), cdf, float(Z[0]), bool(ut[0])
 
-    def accept(self, logits, probs, tokens, tau, u, gamma: int):
+    def accept(self, logits, probs, tokens, tau, u, gamma: int, temperature: float = 1.0):
         """Acceptance + resample for a batch (SimSD 关键设计 4).
 
-        logits/probs [n][B][V], tokens/tau [n][B], u [n][gamma+1].
+        logits/probs [n][B][V], tokens/tau [n][B], u [n][gamma+1].  At
+        temperature T the target distribution of a slot is the softmax of its
+        logits times 1/T (both rounded to float32); probs are the draft's.
         Returns (accept_len[n], out_tokens[n][B], alpha[n][gamma] float64,
         resample_slot[n]).
         """
@@ -296,8 +298,9 @@ class Oracle:
         ot = np.empty((n, B), np.int32)
         al = np.empty((n, gamma), np.float64)
         rs = np.empty(n, np.int32)
+        inv_t = np.float32(1.0) / np.float32(temperature)
         _check(self.lib.svo_accept(_p(logits), _p(probs), _p(tokens), _p(tau), _p(u), n, B, gamma,
-                                   V, _p(L), _p(ot), _p(al), _p(rs)))
+                                   V, float(inv_t), _p(L), _p(ot), _p(al), _p(rs)))
         return L, ot, al, rs
 
 

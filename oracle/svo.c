@@ -326,9 +326,20 @@ int64_t svo_residual(const float *l, const float *pphi, int64_t V, double u,
     return pick;
 }
 
+/* Tempered logits row (sampling at temperature T: the target distribution
+ * is softmax(l / T)).  z[v] = l[v] * inv_t, the product rounded to float32,
+ * with inv_t = 1/T rounded to float32 by the caller; T = 1 (inv_t = 1)
+ * leaves the row unchanged. */
+static void temper_row(const float *l, int64_t V, float inv_t, float *z) {
+    for (int64_t v = 0; v < V; ++v) z[v] = l[v] * inv_t;
+}
+
 /*
  * Acceptance for `batch` sequences (SimSD 关键设计 4).
  *   logits, probs [batch][B][V] indexed by slot (the slot's D~ row);
+ *   inv_t: 1/T in float32; the target distribution of a slot is the softmax
+ *   of its tempered logits row (temper_row); the draft probabilities are the
+ *   caller's, already at the drafter's temperature;
  *   tokens [batch][B] draft token per slot; tau [batch][B];
  *   u [batch][gamma+1]: u[r-1] tests draft step r, u[gamma] drives the resample.
  * Draft step r (1..gamma) verifies slot o_r with tau(o_r) = r:
@@ -342,9 +353,10 @@ int64_t svo_residual(const float *l, const float *pphi, int64_t V, double u,
  */
 int svo_accept(const float *logits, const float *probs, const int32_t *tokens,
                const int32_t *tau, const float *u, int batch, int B, int gamma,
-               int64_t V, int32_t *accept_len, int32_t *out_tokens, double *alpha,
+               int64_t V, float inv_t, int32_t *accept_len, int32_t *out_tokens, double *alpha,
                int32_t *resample_slot) {
     if (batch < 0 || B < 1 || gamma < 1 || gamma > B || V < 1) return SVO_BAD_ARG;
+    if (!(inv_t > 0.f) || !isfinite(inv_t)) return SVO_BAD_ARG;
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < batch; ++b) {
@@ -366,16 +378,17 @@ int svo_accept(const float *logits, const float *probs, const int32_t *tokens,
         }
         int order[64 + 1];
         int *o = (B <= 64) ? order : (int *)malloc(sizeof(int) * ((size_t)B + 1));
+        float *z = (float *)malloc(sizeof(float) * (size_t)V);  /* tempered row */
         for (int k = 0; k < B; ++k) o[tb[k]] = k;   /* o[r] = slot decoded at step r */
         int L = -1;
         for (int r = 1; r <= gamma; ++r) {
             const int k = o[r];
-            const float *lk = logits + ((size_t)b * B + k) * V;
+            temper_row(logits + ((size_t)b * B + k) * V, V, inv_t, z);
             const float *pk = probs + ((size_t)b * B + k) * V;
             double m, s;
-            svo_softmax(lk, V, NULL, &m, &s);
+            svo_softmax(z, V, NULL, &m, &s);
             const int x = xb[k];
-            const double pt = exp((double)lk[x] - m) / s;
+            const double pt = exp((double)z[x] - m) / s;
             const double pd = (double)pk[x];
             double a = (pd > 0.0) ? pt / pd : 1.0;
             if (a > 1.0) a = 1.0;
@@ -388,11 +401,12 @@ int svo_accept(const float *logits, const float *probs, const int32_t *tokens,
         int rs = -1;
         if (L < gamma) {
             rs = o[L + 1];
-            const float *lk = logits + ((size_t)b * B + rs) * V;
+            temper_row(logits + ((size_t)b * B + rs) * V, V, inv_t, z);
             const float *pk = probs + ((size_t)b * B + rs) * V;
-            ob[rs] = (int32_t)svo_residual(lk, pk, V, (double)ub[gamma], NULL, NULL, NULL);
+            ob[rs] = (int32_t)svo_residual(z, pk, V, (double)ub[gamma], NULL, NULL, NULL);
         }
         if (resample_slot) resample_slot[b] = rs;
+        free(z);
         if (o != order) free(o);
     }
     return err;

@@ -373,9 +373,9 @@ def pin_softmax(o):
     assert abs(p1.sum() - 1) < 1e-13 and np.abs(p1 - p2).max() < 1e-12
 
 
-def _one_slot(o, lt, pd, x, u0, u1):
+def _one_slot(o, lt, pd, x, u0, u1, temperature=1.0):
     L, ot, al, _ = o.accept(lt[None, None], pd[None, None], np.array([[x]], np.int32),
-                            np.array([[1]], np.int32), np.array([[u0, u1]], np.float32), 1)
+                            np.array([[1]], np.int32), np.array([[u0, u1]], np.float32), 1, temperature)
     return int(L[0]), int(ot[0, 0]), float(al[0, 0])
 
 
@@ -500,6 +500,37 @@ def pin_accept_energy(o, seed=35):
         assert abs(a - min(1.0, np.exp(-E))) < 1e-12
 
 
+def pin_accept_tempered(o, V=4, seed=37, N=1000):
+    """Sampling at temperature T: draft token x ~ p_phi, acceptance with
+    alpha and the resample emit tokens distributed as the tempered target
+    softmax(l / T) -- scipy's softmax of the float64 quotient (the float32
+    rounding of l * (1/T) moves the law by ~1e-7) -- and the acceptance rate
+    is sum_v min(softmax(l / T), p_phi).  At T = 0.5 and T = 2, where
+    untempered logits, or logits multiplied by T, give other laws."""
+    from scipy.special import softmax
+    r = rng(seed)
+    lt = (r.standard_normal(V) * 1.2).astype(np.float32)
+    pd = r.dirichlet(np.ones(V))
+    pd32 = (pd / pd.sum()).astype(np.float32)
+    grid = (np.arange(N) + 0.5) / N
+    for T in (0.5, 2.0):
+        pt = softmax(lt.astype(np.float64) / T)
+        law, rate = np.zeros(V), 0.0
+        for x in range(V):
+            a = _one_slot(o, lt, pd32, x, 0.0, 0.5, T)[2]
+            rate += float(pd32[x]) * a
+            law[x] += float(pd32[x]) * a
+            counts = np.zeros(V)
+            for u1 in grid:
+                L, t, _ = _one_slot(o, lt, pd32, x, 0.999999, float(u1), T)
+                if L == 0:
+                    counts[t] += 1
+            if counts.sum():
+                law += float(pd32[x]) * (1 - a) * counts / N
+        assert np.abs(law - pt).max() < 2.0 / N + 1e-6, (T, law, pt)
+        assert abs(rate - np.minimum(pt, pd32.astype(np.float64)).sum()) < 1e-6, (T, rate)
+
+
 def all_accept_pins(o, exact=True):
     pin_accept_golden(o)
     pin_softmax(o)
@@ -507,6 +538,7 @@ def all_accept_pins(o, exact=True):
     pin_accept_special_cases(o)
     pin_accept_assembly(o)
     pin_accept_energy(o)
+    pin_accept_tempered(o)
     if exact:
         pin_accept_exact_distribution(o, N=1000)
 

@@ -92,3 +92,15 @@ def test_graph_paged_commit_append():
 
     _graph_check(buf, step, [buf.out_paged, buf.accept_len, buf.out_tokens, buf.block_tokens, buf.prefix_lens,
                              buf.remaining, buf.state, buf.n_append], restore=restore)
+
+
+def test_graph_copies_and_tree():
+    print("[case] graph: multi-copy attention + draft-tree verification", flush=True)
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_speculative_verification_amd.device import StepBuffers
+    case = synth.config_by_name("small").with_(n_copies=9, gamma=8, temperature=1.0)
+    inp = synth.make_inputs(case, parts=("copies", "tree"))
+    buf = StepBuffers(case, inp, parts=("copies", "tree"))
+    _graph_check(buf, lambda: (buf.attn_copies(), buf.tree(temperature=1.0)),
+                 [buf.out_c, buf.path_len, buf.path, buf.commit_pos, buf.commit_tok, buf.tree_target_tok])

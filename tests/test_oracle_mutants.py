@@ -27,8 +27,8 @@ MUTANTS = [
     ("softmax scale", "scale = 1.0 / sqrt((double)d);", "scale = 1.0 / (double)d;"),
     ("unnormalised weights", "const double w = sc[j] / den;", "const double w = sc[j];"),
     ("ratio inverted", "double a = (pd > 0.0) ? pt / pd : 1.0;", "double a = (pd > 0.0) ? pd / pt : 1.0;"),
-    ("target prob unnormalised", "const double pt = exp((double)lk[x] - m) / s;", "const double pt = exp((double)lk[x] - m);"),
-    ("slot order instead of draft order", "const int k = o[r];\n            const float *lk", "const int k = r - 1;\n            const float *lk"),
+    ("target prob unnormalised", "const double pt = exp((double)z[x] - m) / s;", "const double pt = exp((double)z[x] - m);"),
+    ("slot order instead of draft order", "const int k = o[r];\n            temper_row", "const int k = r - 1;\n            temper_row"),
     ("prefix off by one", "< a)) L = r - 1;", "< a)) L = r;"),
     ("assembly off by one", "ob[k] = (tb[k] <= L) ? xb[k] : -1;\n        int rs = -1;",
      "ob[k] = (tb[k] < L) ? xb[k] : -1;\n        int rs = -1;"),
@@ -68,6 +68,10 @@ MUTANTS = [
     ("tree compares the child's own choice", "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[cur]) { next = c; break; }",
      "if (pb[c] == cur && np[c] == tp[cur] && nt[c] == tt[c]) { next = c; break; }"),
     ("tree commits at the root", "commit_pos[b] = tp[cur];", "commit_pos[b] = tp[0];"),
+    ("temperature multiplies", "z[v] = l[v] * inv_t;", "z[v] = l[v] / inv_t;"),
+    ("temperature ignored", "z[v] = l[v] * inv_t;", "z[v] = l[v];"),
+    ("resample row untempered", "ob[rs] = (int32_t)svo_residual(z, pk,",
+     "ob[rs] = (int32_t)svo_residual(logits + ((size_t)b * B + rs) * V, pk,"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
 ]
 

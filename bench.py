@@ -22,7 +22,8 @@ Also reports the CPU oracle timed on this host over the same workload.
 
 --verify coupled | greedy replaces the epilogue by shared-noise verification
 (spec_verify_accept_coupled at --temperature, default 1) or its greedy form
-(T = 0); the default, rejection, is the headline step.  --route margin |
+(T = 0); the default, rejection, is the headline step (at --temperature T
+other than 1 through spec_verify_accept_temperature).  --route margin |
 entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
 --route-param) in front of each step.  --copies C runs SPOT's multi-copy
 verification step instead: attention over C copies of the block (the root
@@ -181,7 +182,7 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
         out_tokens = None
     elif verify == "rejection":
         out_tokens = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
-                              inp["uniforms"], case.gamma)[1]
+                              inp["uniforms"], case.gamma, temperature)[1]
     else:
         out_tokens = o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None,
                                       inp["coupled_tokens"], inp["tau"], case.gamma, temperature)[1]
@@ -260,7 +261,8 @@ def main():
                     help="with --copies: verify a draft tree of the C states instead of a chain")
     ap.add_argument("--copies", type=int, default=0,
                     help="SPOT multi-copy verification over C copies of the block (root + C-1 draft states)")
-    ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --verify coupled")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="sampling temperature (rejection: spec_verify_accept_temperature when not 1)")
     ap.add_argument("--route", choices=("none", "margin", "entropy"), default="none",
                     help="add the S2D2 verify-routing estimate in front of each step")
     ap.add_argument("--route-param", type=float, default=None,
@@ -350,7 +352,7 @@ def main():
         if tree:
             s.tree(temperature=T)
         elif verify == "rejection":
-            s.accept()
+            s.accept(temperature=None if T == 1.0 else T)
         else:
             s.accept_coupled(temperature=T)
 
@@ -501,12 +503,13 @@ def main():
                                f"vocab {case.vocab}, {case.dtype} attention, fp32 logits" +
                                ("" if verify == "rejection" else
                                 f"; {'greedy' if T == 0 else f'shared-noise (T={T:g})'} verification") +
+                               (f"; rejection sampling at T={T:g}" if verify == "rejection" and T != 1.0 else "") +
                                ("" if route == "none" else f"; S2D2 routing estimate ({route}, {rparam:g}) first") +
                                ("" if not paged else f"; prompt cache in pages of {case.page_size} rows"
                                 + (", ragged prompt lengths (mean %.0f)" % inp["prefix_lens"].mean() if case.ragged
                                    else "") + ", then commit and cache append"),
                    "route": None if route == "none" else {"estimator": route, "param": rparam},
-                   "verify": verify, "temperature": None if verify == "rejection" else T,
+                   "verify": verify, "temperature": None if verify == "rejection" and T == 1.0 else T,
                    "copies": copies or None, "tree": tree if copies else None,
                    "page_size": case.page_size if paged else None, "ragged": bool(case.ragged) if paged else None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,

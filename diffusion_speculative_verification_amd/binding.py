@@ -54,6 +54,8 @@ def load(path: str | None = None):
     lib.spec_verify_accept_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept.restype = I
     lib.spec_verify_accept.argtypes = [V, V, V, V, V, I, I, I, I64, V, V, V, V, SZ, V]
+    lib.spec_verify_accept_temperature.restype = I
+    lib.spec_verify_accept_temperature.argtypes = [V, V, V, V, V, I, I, I, I64, F, V, V, V, V, SZ, V]
     lib.spec_verify_accept_coupled_workspace_size.restype = SZ
     lib.spec_verify_accept_coupled_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept_coupled.restype = I
@@ -143,6 +145,16 @@ def spec_verify_accept(target_logits, draft_probs, draft_tokens, tau, uniforms, 
                                      _ptr(uniforms), batch, block, gamma, vocab, _ptr(accept_len),
                                      _ptr(out_tokens), _ptr(alpha), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream)))
+
+
+def spec_verify_accept_temperature(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma,
+                                   vocab, temperature, accept_len, out_tokens, alpha, workspace, workspace_bytes,
+                                   stream=None) -> None:
+    _check(load().spec_verify_accept_temperature(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                                 _ptr(tau), _ptr(uniforms), batch, block, gamma, vocab,
+                                                 float(temperature), _ptr(accept_len), _ptr(out_tokens),
+                                                 _ptr(alpha), _ptr(workspace), int(workspace_bytes),
+                                                 _stream(stream)))
 
 
 def spec_verify_accept_coupled_workspace_size(batch, block, gamma, vocab) -> int:

@@ -230,10 +230,11 @@ size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_
     return sv::accept_plan(batch, block, gamma, vocab).ws_total;
 }
 
-int spec_verify_accept(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
-                       const int32_t *tau, const float *uniforms, int batch, int block, int gamma,
-                       int64_t vocab, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+namespace {
+int accept_impl(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                const int32_t *tau, const float *uniforms, int batch, int block, int gamma, int64_t vocab,
+                float inv_t, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
+                size_t workspace_bytes, void *stream) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21))
         return SV_E_SHAPE;
@@ -247,8 +248,31 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs, con
     if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
     if (!aligned16(workspace)) return SV_E_ALIGN;
     return map_launch(sv::launch_accept(p, target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block,
-                                        gamma, vocab, accept_len, out_tokens, alpha, workspace,
+                                        gamma, vocab, inv_t, accept_len, out_tokens, alpha, workspace,
                                         (hipStream_t)stream));
+}
+}  // namespace
+
+int spec_verify_accept(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                       const int32_t *tau, const float *uniforms, int batch, int block, int gamma,
+                       int64_t vocab, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return accept_impl(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma, vocab, 1.0f,
+                       accept_len, out_tokens, alpha, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_accept_temperature(const float *target_logits, const float *draft_probs,
+                                   const int32_t *draft_tokens, const int32_t *tau, const float *uniforms, int batch,
+                                   int block, int gamma, int64_t vocab, float temperature, int32_t *accept_len,
+                                   int32_t *out_tokens, float *alpha, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_E_SHAPE;
+    // 1/T rounded to float32 once, here: the kernels and the definition use
+    // the same reciprocal
+    const float inv_t = 1.0f / temperature;
+    if (!isfinite(inv_t)) return SV_E_SHAPE;
+    return accept_impl(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma, vocab, inv_t,
+                       accept_len, out_tokens, alpha, workspace, workspace_bytes, stream);
 }
 
 size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab) {

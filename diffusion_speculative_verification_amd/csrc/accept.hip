@@ -31,6 +31,9 @@
 //   residual_pick_kernel one workgroup per sequence: block scans over the
 //                        chunk sums find the chunk holding u * Z, a second
 //                        scan inside it finds the token.
+// At temperature T every target logit is tempered as it is loaded: l * (1/T),
+// the product rounded to float32 (1/T rounded to float32 once, on the host);
+// T = 1 multiplies by 1.0f and leaves every value unchanged.
 // The kernel boundaries order the hand-offs: a last-workgroup hand-off
 // inside one kernel would need a device-scope release per workgroup, which on
 // this GPU writes back the L2.
@@ -70,12 +73,20 @@ constexpr int kPickChunk = kResChunk / 2;   // vocab entries per published chunk
 constexpr int kPickRun = kPickChunk / 256;  // contiguous entries per thread in the pick scan
 constexpr int kMaxChunks = 1024;            // vocab <= kPickChunk * kMaxChunks = 2^21
 
-template <bool VEC>
+// temper(x): x * inv_t rounded to float32 in the tempered instantiation,
+// x itself at T = 1 (where the product is the identity).
+template <bool TEMP>
+__device__ __forceinline__ float temper(float x, float inv_t) {
+    return TEMP ? __fmul_rn(x, inv_t) : x;
+}
+
+template <bool VEC, bool TEMP>
 __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restrict__ logits,
                                                           const float *__restrict__ probs,
                                                           const int32_t *__restrict__ tokens,
                                                           const int32_t *__restrict__ tau, Part *parts, Gath *gath,
-                                                          int block, int gamma, int64_t vocab, int n_vsplit) {
+                                                          int block, int gamma, int64_t vocab, int n_vsplit,
+                                                          float inv_t) {
     __shared__ float red_m[4];
     __shared__ double red_s[4];
     const int row = blockIdx.x / n_vsplit, sp = blockIdx.x % n_vsplit;
@@ -86,7 +97,7 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
     // the draft-token gather; its loads travel with the first stream loads
     Gath g{0.f, 0.f, 0, 0};
     if (gatherer && x >= 0 && x < vocab) {
-        g.l = logits[(size_t)row * vocab + x];
+        g.l = temper<TEMP>(logits[(size_t)row * vocab + x], inv_t);
         g.p = probs[(size_t)row * vocab + x];
         g.ok = 1;
     }
@@ -105,7 +116,8 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
                 ok[u] = i + 256 * u < c1;
                 if (ok[u]) {
                     const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(src + i + 256 * u));
-                    x[u] = make_float4(v[0], v[1], v[2], v[3]);
+                    x[u] = make_float4(temper<TEMP>(v[0], inv_t), temper<TEMP>(v[1], inv_t),
+                                       temper<TEMP>(v[2], inv_t), temper<TEMP>(v[3], inv_t));
                 } else {
                     x[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
                 }
@@ -132,7 +144,7 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
         const int64_t c0 = vocab * sp / n_vsplit, c1 = vocab * (sp + 1) / n_vsplit;
         const float *src = logits + (size_t)row * vocab;
         for (int64_t i = c0 + tid; i < c1; i += 256) {
-            const float x = src[i];
+            const float x = temper<TEMP>(src[i], inv_t);
             if (x > m) {
                 if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - x) * kLog2e);
                 m = x;
@@ -161,11 +173,12 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
 }
 
 // Mass of one vocab entry at the rejected slot: p_theta(v) (float32 exp of
-// the logit against the merged max, scaled by the float64 reciprocal of the
-// merged normaliser) and the residual max(0, p_theta(v) - p_phi(v)) formed in
-// float64.
-__device__ __forceinline__ void masses(float l, float pd, float m, double inv_s, double &r, double &pt) {
-    pt = (double)__builtin_amdgcn_exp2f((l - m) * kLog2e) * inv_s;
+// the tempered logit against the merged max, scaled by the float64
+// reciprocal of the merged normaliser) and the residual max(0, p_theta(v) -
+// p_phi(v)) formed in float64.
+__device__ __forceinline__ void masses(float l, float pd, float m, double inv_s, float inv_t, double &r,
+                                       double &pt) {
+    pt = (double)__builtin_amdgcn_exp2f((__fmul_rn(l, inv_t) - m) * kLog2e) * inv_s;
     const double d = pt - (double)pd;
     r = d > 0.0 ? d : 0.0;
 }
@@ -259,7 +272,7 @@ __global__ void __launch_bounds__(256) accept_resid_kernel(
     const float *__restrict__ logits, const float *__restrict__ probs, const int32_t *__restrict__ tokens,
     const int32_t *__restrict__ tau, const float *__restrict__ u, const Part *__restrict__ parts,
     const Gath *__restrict__ gath, int block, int gamma, int64_t vocab, int n_vsplit, int n_chunk, int n_pick,
-    int32_t *accept_len, int32_t *out_tokens, float *alpha_out, ResInfo *res, double2 *chunk_sums) {
+    float inv_t, int32_t *accept_len, int32_t *out_tokens, float *alpha_out, ResInfo *res, double2 *chunk_sums) {
     __shared__ int slot_s;
     __shared__ float m_s;
     __shared__ double s_s;
@@ -319,10 +332,10 @@ __global__ void __launch_bounds__(256) accept_resid_kernel(
             if (tid + 256 * k >= n4) continue;
             const int h = k / (U / 2);
             double r, pt;
-            masses(xl[k].x, xp[k].x, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
-            masses(xl[k].y, xp[k].y, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
-            masses(xl[k].z, xp[k].z, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
-            masses(xl[k].w, xp[k].w, M, inv_sum, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].x, xp[k].x, M, inv_sum, inv_t, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].y, xp[k].y, M, inv_sum, inv_t, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].z, xp[k].z, M, inv_sum, inv_t, r, pt); ra[h] += r; pa[h] += pt;
+            masses(xl[k].w, xp[k].w, M, inv_sum, inv_t, r, pt); ra[h] += r; pa[h] += pt;
         }
     } else {
 #pragma unroll
@@ -330,7 +343,7 @@ __global__ void __launch_bounds__(256) accept_resid_kernel(
 #pragma unroll 4
             for (int i = h * kPickChunk + tid; i < min(n, (h + 1) * kPickChunk); i += 256) {
                 double r, pt;
-                masses(lr[v0 + i], pr[v0 + i], M, inv_sum, r, pt);
+                masses(lr[v0 + i], pr[v0 + i], M, inv_sum, inv_t, r, pt);
                 ra[h] += r;
                 pa[h] += pt;
             }
@@ -359,7 +372,7 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
                                                             const ResInfo *__restrict__ res,
                                                             const double2 *__restrict__ chunk_sums,
                                                             int32_t *out_tokens, int block, int gamma, int64_t vocab,
-                                                            int n_chunk) {
+                                                            int n_chunk, float inv_t) {
     constexpr int CPT = kMaxChunks / 256;  // chunks per thread
     __shared__ double wave_tot[4];
     __shared__ double tot_s[2];
@@ -440,7 +453,7 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
     for (int k = 0; k < kPickRun; ++k) {
         const int i = tid * kPickRun + k;
         double r = 0.0, pt = 0.0;
-        if (i < n) masses(xl[k], xp[k], ri.m, inv_sum, r, pt);
+        if (i < n) masses(xl[k], xp[k], ri.m, inv_sum, inv_t, r, pt);
         mass[k] = use_t ? pt : r;
         mine += mass[k];
         if (mass[k] > 0.0) lastpos = i;
@@ -484,7 +497,7 @@ AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab) {
 
 hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *probs,
                          const int32_t *tokens, const int32_t *tau, const float *u, int batch,
-                         int block, int gamma, int64_t vocab, int32_t *accept_len,
+                         int block, int gamma, int64_t vocab, float inv_t, int32_t *accept_len,
                          int32_t *out_tokens, float *alpha, void *ws, hipStream_t st) {
     char *base = (char *)ws;
     Part *parts = (Part *)(base + p.off_part);
@@ -492,27 +505,34 @@ hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *
     ResInfo *res = (ResInfo *)(base + p.off_res);
     double2 *chunks = (double2 *)(base + p.off_chunk);
     const unsigned g1 = (unsigned)((size_t)p.rows * p.n_vsplit);
-    if ((vocab & 3) == 0)
-        hipLaunchKernelGGL(lse_partial_kernel<true>, dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau, parts,
-                           gath, block, gamma, vocab, p.n_vsplit);
+    const bool vec = (vocab & 3) == 0, temp = inv_t != 1.0f;
+    if (vec && !temp)
+        hipLaunchKernelGGL((lse_partial_kernel<true, false>), dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau,
+                           parts, gath, block, gamma, vocab, p.n_vsplit, inv_t);
+    else if (vec)
+        hipLaunchKernelGGL((lse_partial_kernel<true, true>), dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau,
+                           parts, gath, block, gamma, vocab, p.n_vsplit, inv_t);
+    else if (!temp)
+        hipLaunchKernelGGL((lse_partial_kernel<false, false>), dim3(g1), dim3(256), 0, st, logits, probs, tokens,
+                           tau, parts, gath, block, gamma, vocab, p.n_vsplit, inv_t);
     else
-        hipLaunchKernelGGL(lse_partial_kernel<false>, dim3(g1), dim3(256), 0, st, logits, probs, tokens, tau,
-                           parts, gath, block, gamma, vocab, p.n_vsplit);
+        hipLaunchKernelGGL((lse_partial_kernel<false, true>), dim3(g1), dim3(256), 0, st, logits, probs, tokens,
+                           tau, parts, gath, block, gamma, vocab, p.n_vsplit, inv_t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)((size_t)batch * p.n_chunk));
     if ((vocab & 3) == 0)
         hipLaunchKernelGGL(accept_resid_kernel<true>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts, gath,
-                           block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, accept_len, out_tokens, alpha, res,
-                           chunks);
+                           block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, inv_t, accept_len, out_tokens, alpha,
+                           res, chunks);
     else
         hipLaunchKernelGGL(accept_resid_kernel<false>, g2, dim3(256), 0, st, logits, probs, tokens, tau, u, parts,
-                           gath, block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, accept_len, out_tokens, alpha,
-                           res, chunks);
+                           gath, block, gamma, vocab, p.n_vsplit, p.n_chunk, p.n_pick, inv_t, accept_len, out_tokens,
+                           alpha, res, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(residual_pick_kernel, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks, out_tokens,
-                       block, gamma, vocab, p.n_pick);
+                       block, gamma, vocab, p.n_pick, inv_t);
     return hipGetLastError();
 }
 

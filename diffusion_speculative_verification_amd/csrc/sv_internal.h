@@ -69,7 +69,7 @@ AcceptPlan accept_plan(int batch, int block, int gamma, int64_t vocab);
 
 hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *probs,
                          const int32_t *tokens, const int32_t *tau, const float *u, int batch,
-                         int block, int gamma, int64_t vocab, int32_t *accept_len,
+                         int block, int gamma, int64_t vocab, float inv_t, int32_t *accept_len,
                          int32_t *out_tokens, float *alpha, void *ws, hipStream_t st);
 
 struct CoupledPlan {

@@ -129,11 +129,19 @@ class StepBuffers:
                             c.prefix_len, c.n_qh, c.n_kvh, c.head_dim, theta, 0.0, self.attn_ws,
                             self.attn_ws_bytes, stream)
 
-    def accept(self, stream=None):
+    def accept(self, stream=None, temperature=None):
+        """Rejection-sampling verification of the batch; with a temperature,
+        the tempered call (the target distribution softmax(logits / T))."""
         c = self.case
-        sv.spec_verify_accept(self.target_logits, self.draft_probs, self.draft_tokens, self.tau, self.uniforms,
-                              c.batch, c.block, c.gamma, c.vocab, self.accept_len, self.out_tokens, self.alpha,
-                              self.acc_ws, self.acc_ws_bytes, stream)
+        if temperature is None:
+            sv.spec_verify_accept(self.target_logits, self.draft_probs, self.draft_tokens, self.tau, self.uniforms,
+                                  c.batch, c.block, c.gamma, c.vocab, self.accept_len, self.out_tokens, self.alpha,
+                                  self.acc_ws, self.acc_ws_bytes, stream)
+        else:
+            sv.spec_verify_accept_temperature(self.target_logits, self.draft_probs, self.draft_tokens, self.tau,
+                                              self.uniforms, c.batch, c.block, c.gamma, c.vocab, temperature,
+                                              self.accept_len, self.out_tokens, self.alpha, self.acc_ws,
+                                              self.acc_ws_bytes, stream)
 
     def accept_coupled(self, stream=None, temperature=None):
         """Shared-noise (T > 0) or greedy (T = 0) verification of the batch."""

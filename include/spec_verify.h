@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 2
+#define SPEC_VERIFY_ABI_VERSION 3
 
 enum {
     SV_OK = 0,
@@ -306,6 +306,26 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs,
                        int batch, int block, int gamma, int64_t vocab, int32_t *accept_len,
                        int32_t *out_tokens, float *alpha, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * The same verification epilogue when target and draft sample at temperature
+ * T > 0 (speculative sampling with the min(1, q/p) acceptance: "S2D2",
+ * 前置知识; the classic rejection-sampling verifier that "SPOT" (核心创新,
+ * 新颖性) sets beside shared-noise verification at any temperature).  The
+ * target distribution of a slot is p_theta = softmax(target_logits[k] * 1/T):
+ * 1/T is rounded to float32 once and every product l * (1/T) is rounded to
+ * float32 before use.  draft_probs is the drafter's distribution, already at
+ * its own temperature.  Arguments, outputs, workspace
+ * (spec_verify_accept_workspace_size) and errors as spec_verify_accept; a
+ * temperature that is not finite and positive, or whose reciprocal overflows
+ * float32, gives SV_E_SHAPE.  T = 1 gives exactly spec_verify_accept's
+ * results.  (T = 0, greedy verification, is spec_verify_accept_coupled.)
+ */
+int spec_verify_accept_temperature(const float *target_logits, const float *draft_probs,
+                                   const int32_t *draft_tokens, const int32_t *tau, const float *uniforms,
+                                   int batch, int block, int gamma, int64_t vocab, float temperature,
+                                   int32_t *accept_len, int32_t *out_tokens, float *alpha, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace spec_verify_accept_coupled needs for these sizes. */
 size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab);

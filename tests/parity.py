@@ -31,9 +31,10 @@ def check_attn(gpu, ref, dtype: str, what=""):
     return mx, rel
 
 
-def check_accept(o, inp, gamma, L_g, tok_g, alpha_g, seqs=None):
+def check_accept(o, inp, gamma, L_g, tok_g, alpha_g, seqs=None, temperature=1.0):
     """Compare GPU acceptance outputs with the oracle on sequences `seqs`
-    (indices into the batch).  Returns the number of counted ties."""
+    (indices into the batch), at `temperature`.  Returns the number of
+    counted ties."""
     n = inp["tau"].shape[0]
     seqs = range(n) if seqs is None else seqs
     seqs = list(seqs)
@@ -42,7 +43,9 @@ def check_accept(o, inp, gamma, L_g, tok_g, alpha_g, seqs=None):
     toks = inp["draft_tokens"][seqs]
     tau = inp["tau"][seqs]
     u = inp["uniforms"][seqs]
-    L_o, tok_o, al_o, rs_o = o.accept(lt, pd, toks, tau, u, gamma)
+    L_o, tok_o, al_o, rs_o = o.accept(lt, pd, toks, tau, u, gamma, temperature)
+    if temperature != 1.0:   # the tempered rows the oracle's resample used
+        lt = lt * (np.float32(1.0) / np.float32(temperature))
     ties = 0
     for i, b in enumerate(seqs):
         # alpha of every step: float32 output of a float64 value

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
 
@@ -101,6 +101,22 @@ def test_accept_argument_checks(lib):
     assert accept(lib, batch=1 << 14, block=64, gamma=8, vocab=1 << 21) == sv.SV_E_SHAPE
     assert sv.spec_verify_accept_workspace_size(1 << 21, 64, 8, 4) == 0
     assert sv.spec_verify_route_workspace_size(1 << 21, 64, 8, 4) == 0
+
+
+def test_accept_temperature_argument_checks(lib):
+    f = lib.spec_verify_accept_temperature
+
+    def call(T, **kw):
+        a = dict(tl=A, dp=A, dt=A, tau=A, u=A, batch=2, block=8, gamma=8, vocab=512, L=A, ot=A, al=A, ws=None,
+                 ws_bytes=0)
+        a.update(kw)
+        return f(a["tl"], a["dp"], a["dt"], a["tau"], a["u"], a["batch"], a["block"], a["gamma"], a["vocab"], T,
+                 a["L"], a["ot"], a["al"], a["ws"], a["ws_bytes"], None)
+    for T in (0.0, -1.0, float("inf"), float("nan"), 1e-45):   # 1e-45: 1/T overflows float32
+        assert call(T) == sv.SV_E_SHAPE, T
+    assert call(0.7) == sv.SV_E_WORKSPACE      # checks pass up to the missing workspace: nothing launched
+    assert call(0.7, tl=None) == sv.SV_E_NULL
+    assert call(0.7, gamma=9) == sv.SV_E_SHAPE
 
 
 def coupled(lib, **kw):

@@ -18,11 +18,12 @@
  *     the longest accepted prefix, and a resample at the first rejection from
  *     the residual (P_target - P_draft)^+ (page "S2D2: Fast Decoding for
  *     Diffusion LLMs via Training-Free Self-Speculation", 方法步骤 (5)).
- * Around it: shared-noise and greedy verification, the multi-copy
- * attention and draft-tree verification of "SPOT: Enhancing Speculative
- * Decoding for Diffusion Language Models via Commit-Order Prediction"; S2D2's verify-routing estimate; a
- * paged prompt cache with per-sequence lengths, the commit step and the
- * cache append (each call below cites its passage).
+ * Around it: the same epilogue at a sampling temperature T; shared-noise and
+ * greedy verification, the multi-copy attention and draft-tree verification
+ * of "SPOT: Enhancing Speculative Decoding for Diffusion Language Models via
+ * Commit-Order Prediction"; S2D2's verify-routing estimate; a paged prompt
+ * cache with per-sequence lengths, the commit step and the cache append
+ * (each call below cites its passage).
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller,

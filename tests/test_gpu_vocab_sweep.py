@@ -44,7 +44,14 @@ def o():
     return oracle.Oracle()
 
 
-@pytest.mark.parametrize("sh", _shapes(22, 11), ids=lambda sh: f"b{sh['batch']}-B{sh['block']}-g{sh['gamma']}-V{sh['vocab']}-T{sh['T']}")
+# the largest vocabulary the calls accept (2^21: 1024 published half-chunk
+# sums in the resample), and one below it on the scalar-load path
+MAX_VOCAB = [dict(batch=2, block=3, gamma=3, vocab=1 << 21, T=0.8, nodes=3, seed=590),
+             dict(batch=1, block=4, gamma=2, vocab=(1 << 21) - 1, T=0.0, nodes=4, seed=591)]
+
+
+@pytest.mark.parametrize("sh", _shapes(22, 11) + MAX_VOCAB,
+                         ids=lambda sh: f"b{sh['batch']}-B{sh['block']}-g{sh['gamma']}-V{sh['vocab']}-T{sh['T']}")
 def test_vocab_sweep(o, sh):
     print(f"[case] {sh}", flush=True)
     if not torch.cuda.is_available():

@@ -461,9 +461,11 @@ def main():
     attn_tag = acc_tag if copies else (f"_p{args.paged}{'r' if args.ragged else ''}" if paged else "")
     if headline:
         rl_attn["traffic"] = measured_traffic(attn_call + attn_tag)
+        # the tempered rejection path runs its own instantiation of the
+        # normaliser pass, which has no counter line of its own
         rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") +
-                                             acc_tag)
-    elif not (copies or paged or route != "none" or verify != "rejection"):
+                                             ("_tempered" if verify == "rejection" and T != 1.0 else "") + acc_tag)
+    elif not (copies or paged or route != "none" or verify != "rejection" or T != 1.0):
         # the plain step of another workload has its own counter lines
         rl_attn["traffic"] = measured_traffic(f"{attn_call}_{case.name}")
         rl_acc["traffic"] = measured_traffic(f"{acc_call}_{case.name}")

@@ -462,7 +462,7 @@ def main():
     if headline:
         rl_attn["traffic"] = measured_traffic(attn_call + attn_tag)
         # the tempered rejection path runs its own instantiation of the
-        # normaliser pass, which has no counter line of its own
+        # normaliser pass, with a counter line of its own
         rl_acc["traffic"] = measured_traffic(acc_call + ("_greedy" if T == 0 and verify != "rejection" else "") +
                                              ("_tempered" if verify == "rejection" and T != 1.0 else "") + acc_tag)
     elif not (copies or paged or route != "none" or verify != "rejection" or T != 1.0):

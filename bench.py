@@ -17,8 +17,13 @@ last-level cache.
 Prints ONE JSON line (rank 0, N = 1).  After W untimed steps, K steps are
 timed with events only at their two ends (value, ms_per_step); the same K
 steps then run again with HIP events on the launch stream around every call,
-which gives the per-call durations for the roofline of the dominant call.
-Also reports the CPU oracle timed on this host over the same workload.
+which gives the per-call durations.  `roofline` is the step's: every call at
+its bound (HBM bytes at 8 TB/s, or bf16 MFMA flops at 2.5 PFLOP/s when they
+take longer) against the timed step; `roofline.dominant_kernel` gives the
+dominant call's own rate against its bound.  Same-run peak microbenchmarks
+run before the warmup steps (their load lets the clocks settle).  Also
+reports the CPU oracle timed on this host over the same workload, and how
+the GPU's acceptance outputs agree with the oracle's (ties counted).
 
 --verify coupled | greedy replaces the epilogue by shared-noise verification
 (spec_verify_accept_coupled at --temperature, default 1) or its greedy form
@@ -139,11 +144,50 @@ def measured_traffic(call: str):
     return None
 
 
+def oracle_agreement(o, inp, gamma, temperature, L_o, tok_o, al_o, rs_o, gpu) -> dict:
+    """Agreement of the GPU's rejection-sampling outputs `gpu` = (accept_len,
+    out_tokens) with the oracle's on the same inputs: sequences equal, and
+    sequences that differ only where the decision is a tie (|u - alpha| <
+    1e-6 for the first differing acceptance test; u * Z within 1e-6 * Z of a
+    running-sum boundary for the resampled token).  Anything else is counted
+    as a mismatch."""
+    import numpy as np
+    L_g, tok_g = gpu
+    u = inp["uniforms"]
+    lt = inp["target_logits"]
+    if temperature != 1.0:
+        lt = lt * (np.float32(1.0) / np.float32(temperature))
+    equal = ties = mismatch = 0
+    for b in range(len(L_o)):
+        if int(L_g[b]) == int(L_o[b]) and np.array_equal(tok_g[b], tok_o[b]):
+            equal += 1
+            continue
+        if int(L_g[b]) != int(L_o[b]):
+            r = min(int(L_g[b]), int(L_o[b]))
+            ok = abs(float(u[b, r]) - float(al_o[b, r])) < 1e-6
+        else:
+            diff = np.nonzero(tok_g[b] != tok_o[b])[0].tolist()
+            slot = int(rs_o[b])
+            ok = diff == [slot]
+            if ok:
+                v = int(tok_g[b, slot])
+                _, cdf, Z, _ = o.residual(lt[b, slot], inp["draft_probs"][b, slot], float(u[b, gamma]))
+                thr = float(u[b, gamma]) * Z
+                lo_b = cdf[v - 1] if v > 0 else 0.0
+                ok = 0 <= v < len(cdf) and lo_b - 1e-6 * Z <= thr <= cdf[v] + 1e-6 * Z
+        ties += int(ok)
+        mismatch += int(not ok)
+    return {"sequences": len(L_o), "equal": equal, "ties": ties, "mismatches": mismatch}
+
+
 def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
-                 paged=False, tree=False, attn_budget_s=20.0) -> dict:
+                 paged=False, tree=False, attn_budget_s=20.0, gpu_accept=None) -> dict:
     """The CPU oracle on this host over the same workload (one step).  The
     attention is timed over the first sequences of the batch until
-    `attn_budget_s` has passed and scaled to the whole batch."""
+    `attn_budget_s` has passed and scaled to the whole batch.  With
+    `gpu_accept` (the GPU's accept_len and out_tokens of the same inputs) the
+    oracle's acceptance outputs are also compared with the GPU's
+    (oracle_agreement), outside the timed part."""
     import oracle
     o = oracle.Oracle()
     threads = o.max_threads()
@@ -181,8 +225,9 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
                       inp["node_pos"], inp["node_tok"], inp["target_pos"], temperature)
         out_tokens = None
     elif verify == "rejection":
-        out_tokens = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
-                              inp["uniforms"], case.gamma, temperature)[1]
+        acc_o = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
+                         inp["uniforms"], case.gamma, temperature)
+        out_tokens = acc_o[1]
     else:
         out_tokens = o.accept_coupled(inp["target_logits"], inp["gumbel"] if temperature > 0 else None,
                                       inp["coupled_tokens"], inp["tau"], case.gamma, temperature)[1]
@@ -195,6 +240,9 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
                     inp["prefix_lens"], case.page_size, case.theta)
         t_commit = time.perf_counter() - t
     total = t_route + t_attn + t_acc + t_commit
+    agreement = None
+    if gpu_accept is not None and verify == "rejection" and not tree:
+        agreement = oracle_agreement(o, inp, case.gamma, temperature, *acc_o, gpu_accept)
     attn_what = (f"attention {t_attn:.2f} s" if n_seq == case.batch else
                  f"attention {t_attn:.2f} s (timed on {n_seq} of {case.batch} sequences, scaled)")
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
@@ -204,7 +252,8 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
                       f"{attn_what} + accept {t_acc:.2f} s"
                       + (f" + commit and append {t_commit:.2f} s" if paged else "") +
                       f" on {threads} OpenMP threads "
-                      f"(host reports {os.cpu_count()} CPUs); input generation excluded"}
+                      f"(host reports {os.cpu_count()} CPUs); input generation excluded",
+            "agreement": agreement}
 
 
 def measured_peaks(torch) -> dict:
@@ -375,6 +424,10 @@ def main():
         if e:
             e[4].record(stream)
 
+    # the same-run peak microbenchmarks go first: after the idle time of the
+    # input generation they put the GPU under load long enough (~0.1 s) for
+    # its clocks to settle, so that even a short warmup ends in steady state
+    peaks = measured_peaks(torch)
     for i in range(args.warmup):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
@@ -471,17 +524,42 @@ def main():
         rl_acc["traffic"] = measured_traffic(f"{acc_call}_{case.name}")
     else:
         rl_attn["traffic"] = rl_acc["traffic"] = None
-    roofline = {"bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1), "peak": dom[1]["peak"],
-                "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4), "traffic": dom[1]["traffic"],
-                "traffic_unit": "bytes/launch", "call": dom[0], "ms_per_launch": round(dom[1]["ms"], 5)}
-
-    peaks = measured_peaks(torch)
-    roofline["frac_of_measured_peak"] = round(dom[1]["achieved"] / (peaks["bf16_gemm_tflops"] if
-                                                                    dom[1]["unit"] == "TFLOP/s" else
-                                                                    peaks["hbm_read_gbs"]), 4)
+    # the dominant call: algorithmic work per launch over its event-timed
+    # average launch
+    dom_rl = {"call": dom[0], "bound": dom[1]["bound"], "achieved": round(dom[1]["achieved"], 1),
+              "peak": dom[1]["peak"], "unit": dom[1]["unit"], "frac": round(dom[1]["frac"], 4),
+              "traffic": dom[1]["traffic"], "traffic_unit": "bytes/launch", "ms_per_launch": round(dom[1]["ms"], 5)}
+    dom_rl["frac_of_measured_peak"] = round(dom[1]["achieved"] / (peaks["bf16_gemm_tflops"] if
+                                                                  dom[1]["unit"] == "TFLOP/s" else
+                                                                  peaks["hbm_read_gbs"]), 4)
+    # the metric's roofline is the step's: its calls back to back at their
+    # bounds (roof_step_s) against the timed step.  When every call is bound
+    # by HBM the step is too, and its rate is the step's algorithmic bytes
+    # per timed step; a step whose attention is bound by the MFMA reports the
+    # two times instead.
+    step_bytes = a_bytes + c_bytes + (route_bytes(case) if route != "none" else 0.0) + \
+        (rl_commit["bytes"] if paged else 0.0)
+    hbm_step = rl_attn["bound"] == "hbm"
+    parts_traffic = [rl_attn["traffic"], rl_acc["traffic"]] + ([rl_route["traffic"]] if rl_route else [])
+    if hbm_step:
+        roofline = {"bound": "hbm", "achieved": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(roof_step_s / (ms_step * 1e-3), 4),
+                    "traffic": (sum(parts_traffic) if all(t is not None for t in parts_traffic) and not paged
+                                else None),
+                    "traffic_unit": "bytes/step", "algorithmic_bytes": round(step_bytes)}
+    else:
+        roofline = {"bound": "mfma+hbm", "achieved": round(roof_step_s * 1e6, 2), "peak": round(ms_step * 1e3, 2),
+                    "unit": "us (step at its bounds / timed step)", "frac": round(roof_step_s / (ms_step * 1e-3), 4),
+                    "traffic": None, "traffic_unit": "bytes/step"}
+    roofline["what"] = "whole step (every call at its roofline) vs the timed step"
+    roofline["dominant_kernel"] = dom_rl
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree)
+        gpu_acc = None
+        if verify == "rejection" and not tree and not paged:
+            # the GPU's outputs of the inputs in `inp` (every input set holds them)
+            gpu_acc = (sets[0].accept_len.cpu().numpy(), sets[0].out_tokens.cpu().numpy())
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree, gpu_accept=gpu_acc)
 
     out = {
         "metric": METRIC,
@@ -533,6 +611,9 @@ def main():
             "wall_s": round(wall, 4),
             "mean_accept_len": float(L.float().mean()),
             "rejecting_sequences": n_rej,
+            # acceptance outputs of the GPU against the oracle on the same inputs
+            # (counted ties are decisions within 1e-6 of their threshold)
+            "oracle_agreement": cpu["agreement"] if cpu else None,
         },
     }
     print(json.dumps(out))

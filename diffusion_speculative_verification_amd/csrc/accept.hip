@@ -130,13 +130,17 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
                 if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - gm) * kLog2e);
                 m = gm;
             }
+            // while every entry so far is -inf (masked logits), m is -inf
+            // and so are the entries of this round: subtracting 0 instead
+            // keeps exp(-inf - m) at 0 rather than NaN
+            const float mu = (m == -INFINITY) ? 0.f : m;
             float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                ps += __builtin_amdgcn_exp2f((x[u].x - m) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].y - m) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].z - m) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].w - m) * kLog2e);
+                ps += __builtin_amdgcn_exp2f((x[u].x - mu) * kLog2e);
+                ps += __builtin_amdgcn_exp2f((x[u].y - mu) * kLog2e);
+                ps += __builtin_amdgcn_exp2f((x[u].z - mu) * kLog2e);
+                ps += __builtin_amdgcn_exp2f((x[u].w - mu) * kLog2e);
             }
             s += (double)ps;
         }
@@ -149,7 +153,7 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
                 if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - x) * kLog2e);
                 m = x;
             }
-            s += (double)__builtin_amdgcn_exp2f((x - m) * kLog2e);
+            s += (double)__builtin_amdgcn_exp2f((x - ((m == -INFINITY) ? 0.f : m)) * kLog2e);
         }
     }
     // workgroup merge
@@ -244,7 +248,11 @@ __device__ __forceinline__ int acceptance_scan(const int32_t *__restrict__ token
     if (ver && g.ok) {  // an out-of-range draft token is rejected (alpha = 0)
         const double pt = exp((double)g.l - (double)M) / S;
         const double pd = (double)g.p;
-        a = (pd > 0.0) ? fmin(1.0, pt / pd) : 1.0;
+        // a row without a finite logit has no target distribution: its
+        // NaN ratio survives the clamp (fmin would turn it into 1) and the
+        // test u < alpha below rejects the step
+        a = (pd > 0.0) ? pt / pd : 1.0;
+        if (a > 1.0) a = 1.0;
     }
     const float ur = __shfl(ul, ver ? t - 1 : 0);  // uniform of draft step t
     const bool rejected = ver && !((double)ur < a);

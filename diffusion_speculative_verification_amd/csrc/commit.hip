@@ -57,10 +57,22 @@ __global__ void __launch_bounds__(64) commit_kernel(const int32_t *__restrict__ 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 // append status of a sequence: 0 appended (or nothing to append), 1 would
-// pass the capacity (nothing written), 2 n_append outside [0, src_stride]
-__device__ __forceinline__ int append_status(int n, int P, int src_stride, long long capacity) {
+// pass the capacity (nothing written), 2 n_append outside [0, src_stride],
+// 3 a page the rows would land in has an id outside [0, n_pages) (nothing
+// written: writing there could overwrite another sequence's page).  table is
+// the sequence's block-table row (NULL: contiguous cache); every workgroup
+// of the sequence and the length update read the same entries, so they agree.
+__device__ __forceinline__ int append_status(int n, int P, int src_stride, long long capacity,
+                                             const int32_t *table, int page_size, int n_pages) {
     if (n < 0 || n > src_stride || P < 0) return 2;
-    return ((long long)P + n > capacity) ? 1 : 0;
+    if ((long long)P + n > capacity) return 1;
+    if (table && n > 0) {
+        for (int pg = P / page_size; pg <= (P + n - 1) / page_size; ++pg) {
+            const int id = table[pg];
+            if (id < 0 || id >= n_pages) return 3;
+        }
+    }
+    return 0;
 }
 
 template <int D>
@@ -76,11 +88,11 @@ __global__ void __launch_bounds__(256) append_rows_kernel(const uint16_t *__rest
     constexpr int NC = D / 8;   // 16-byte chunks in a row
     const int b = blockIdx.x / n_kvh, kvh = blockIdx.x % n_kvh;
     const int n = n_append[b], P = prefix_lens[b];
-    if (append_status(n, P, src_stride, capacity) != 0 || n == 0) return;
+    const int32_t *table = block_table ? block_table + (size_t)b * max_pages : nullptr;
+    if (append_status(n, P, src_stride, capacity, table, page_size, n_pages) != 0 || n == 0) return;
     auto dst_off = [&](int p) -> size_t {  // element offset of cache row p of (b, kvh)
-        if (block_table) {
-            int pg = block_table[(size_t)b * max_pages + p / page_size];
-            pg = min(max(pg, 0), n_pages - 1);
+        if (table) {  // every page id in range: checked by append_status
+            const int pg = table[p / page_size];
             return (((size_t)pg * n_kvh + kvh) * page_size + p % page_size) * D;
         }
         return (((size_t)b * n_kvh + kvh) * page_size + p) * D;
@@ -114,12 +126,14 @@ __global__ void __launch_bounds__(256) append_rows_kernel(const uint16_t *__rest
 }
 
 __global__ void __launch_bounds__(256) append_lens_kernel(const int32_t *__restrict__ n_append, int32_t *prefix_lens,
-                                                          int32_t *status, int batch, int src_stride,
-                                                          long long capacity) {
+                                                          int32_t *status, const int32_t *__restrict__ block_table,
+                                                          int batch, int src_stride, long long capacity,
+                                                          int page_size, int max_pages, int n_pages) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= batch) return;
     const int n = n_append[b], P = prefix_lens[b];
-    const int s = append_status(n, P, src_stride, capacity);
+    const int s = append_status(n, P, src_stride, capacity,
+                                block_table ? block_table + (size_t)b * max_pages : nullptr, page_size, n_pages);
     if (s == 0) prefix_lens[b] = P + n;
     if (status) status[b] = s;
 }
@@ -173,7 +187,8 @@ hipError_t launch_append(const void *k_rows, const void *v_rows, int src_stride,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(append_lens_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, st, n_append,
-                       prefix_lens, status, batch, src_stride, capacity);
+                       prefix_lens, status, block_table, batch, src_stride, capacity, page_size, max_pages,
+                       n_pages);
     return hipGetLastError();
 }
 

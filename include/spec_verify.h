@@ -103,7 +103,13 @@ size_t spec_verify_attn_workspace_size(int dtype, int batch, int block, int pref
  *   k_new, v_new [batch][2*block][n_kvh][head_dim]   (response keys/values)
  *   k_cache, v_cache [batch][n_kvh][prefix_len][head_dim] (prompt KV, keys
  *          already rotated at positions 0..prefix_len-1; may be NULL when
- *          prefix_len == 0)
+ *          prefix_len == 0).  Head-major, so that one (sequence, kv head)
+ *          reads one contiguous stream; a caller that keeps its cache
+ *          position-major ([prefix_len][n_kvh][head_dim]) must transpose it
+ *          first, a copy of the whole cache (268 MB for 32 sequences of 2048
+ *          rows, 8 kv heads, head_dim 128) that this call's time does not
+ *          include -- or keep it in pages (spec_verify_attn_paged), which
+ *          the append keeps up to date in place.
  *   tau    [batch][block] int32, step labels 1..block
  *   out    [batch][2*block][n_qh][head_dim] in dtype
  * rope_theta > 0: q and k_new are raw and are rotated on the fly with the
@@ -265,7 +271,9 @@ int spec_verify_commit(const int32_t *out_tokens, int32_t *block_tokens, int bat
  * page_size, or the row stride page_size without a table).
  *   status [batch] (optional): 0 appended (or nothing to append), 1 the rows
  *   would pass the capacity (nothing written, length unchanged), 2 n_append[b]
- *   outside [0, src_stride] (nothing written).
+ *   outside [0, src_stride] (nothing written), 3 a block-table entry of a
+ *   page the rows would land in lies outside [0, n_pages) (nothing written,
+ *   length unchanged).
  * n_append and prefix_lens live on the device (n_append as spec_verify_commit
  * leaves it).  Pages shared by several sequences are the caller's to copy
  * before an append.  dtype SV_BF16, head_dim 64 or 128.
@@ -301,6 +309,11 @@ size_t spec_verify_accept_workspace_size(int batch, int block, int gamma, int64_
  *     itself when that sum is zero); -1 for every other slot
  *   alpha [batch][gamma] float32 (may be NULL): alpha_r of every step, in
  *     draft order
+ * Target logits may be -inf (masked or filtered vocabulary entries: they
+ * get probability 0); each verified slot's row needs at least one finite
+ * logit and no NaN or +inf -- a row without a finite logit has no target
+ * distribution: its alpha is NaN, its step is rejected and the resampled
+ * token is unspecified.
  */
 int spec_verify_accept(const float *target_logits, const float *draft_probs,
                        const int32_t *draft_tokens, const int32_t *tau, const float *uniforms,

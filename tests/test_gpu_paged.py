@@ -206,6 +206,44 @@ def test_kv_append(o, paged, theta, head_dim, ps):
     print(f"[result] append: lengths {lens.tolist()} -> {lens_o.tolist()}", flush=True)
 
 
+def test_kv_append_bad_page(o):
+    """A block-table entry outside [0, n_pages) where an append would land:
+    status 3, nothing written for that sequence and its length unchanged;
+    the other sequences append as usual."""
+    print("[case] append with planted bad page ids", flush=True)
+    _cuda()
+    case = BASE.with_(batch=6, ragged=True, prefix_len=200, page_size=64)
+    inp = synth.make_inputs(case, parts=("attn", "paged"))
+    B, S = case.block, 2 * case.block
+    kp, vp, table = inp["k_pages"], inp["v_pages"], inp["block_table"].copy()
+    ps, n_pages = case.page_size, kp.shape[0]
+    lens = inp["prefix_lens"].copy()
+    n_app = np.array([B, B, 5, 0, B, B], np.int32)
+    table[0, (lens[0] + B - 1) // ps] = n_pages      # last page of the rows: one past the end
+    table[2, lens[2] // ps] = -1                      # first page of the rows: negative
+    table[3, lens[3] // ps] = n_pages + 7             # nothing to append: not looked at
+    d = lambda a, dt=None: (lambda t: t.to(dt) if dt is not None else t)(torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    kr, vr = d(inp["k_new"], torch.bfloat16), d(inp["v_new"], torch.bfloat16)
+    kpd, vpd = d(kp, torch.bfloat16), d(vp, torch.bfloat16)
+    pl, na, tb = d(lens), d(n_app), d(table)
+    status = torch.full((6,), -9, dtype=torch.int32, device="cuda")
+    sv.spec_verify_kv_append(kr, vr, S, na, kpd, vpd, tb, pl, status, sv.SV_BF16, 6, ps, table.shape[1], n_pages,
+                             case.n_kvh, case.head_dim, case.theta)
+    torch.cuda.synchronize()
+    st = status.cpu().numpy()
+    assert st.tolist() == [3, 0, 3, 0, 0, 0], st
+    n_ok = n_app.copy()
+    n_ok[[0, 2]] = 0
+    kp_o, vp_o, lens_o, _ = o.kv_append(inp["k_new"], inp["v_new"], n_ok, kp, vp, table, lens, ps, case.theta)
+    assert np.array_equal(pl.cpu().numpy(), lens_o)
+    assert lens_o[0] == lens[0] and lens_o[2] == lens[2]
+    kg, vg = kpd.float().cpu().numpy(), vpd.float().cpu().numpy()
+    assert np.array_equal(vg, vp_o)
+    assert _bf16_close(kg, kp_o)
+    assert np.array_equal(kg[kp_o == kp], kp[kp_o == kp])   # nothing else written
+    print(f"[result] append bad pages: status {st.tolist()}", flush=True)
+
+
 def test_step_chain(o):
     """Verification, commit and append in a row on the GPU, then the next
     verification attention over the grown cache: each stage vs the oracle."""

@@ -147,6 +147,33 @@ def test_all_accepted_and_all_rejected(o):
     assert (res["L"] == 0).all()
 
 
+@pytest.mark.parametrize("vocab,run", [(20000, 5000), (151936, 9000), (1001, 1), (8191, 3000)])
+@pytest.mark.parametrize("temperature", [1.0, 0.7])
+def test_masked_logits(o, vocab, run, temperature):
+    """Target logits that are -inf (masked or filtered entries, probability
+    0): a leading run of `run` entries on even slots -- longer than one
+    round of a lane's loads on the 16-byte path, the first entry on the
+    scalar path -- and every 7th entry on odd slots; draft tokens that land
+    on a masked entry are rejected (alpha 0)."""
+    print(f"[case] masked logits vocab={vocab} run={run} T={temperature}", flush=True)
+    _cuda()
+    case = SMALL.with_(vocab=vocab, batch=4)
+    inp = synth.make_inputs(case, parts=("accept",))
+    lt = inp["target_logits"]
+    lt[:, ::2, :run] = -np.inf
+    lt[:, 1::2, ::7] = -np.inf
+    from diffusion_speculative_verification_amd.device import StepBuffers
+    buf = StepBuffers(case, inp, parts=("accept",))
+    buf.accept(temperature=None if temperature == 1.0 else temperature)
+    torch.cuda.synchronize()
+    L, tok, al = buf.accept_len.cpu().numpy(), buf.out_tokens.cpu().numpy(), buf.alpha.cpu().numpy()
+    assert np.isfinite(al).all(), al
+    ties = parity.check_accept(o, inp, case.gamma, L, tok, al, temperature=temperature)
+    masked = np.isneginf(np.take_along_axis(lt, inp["draft_tokens"][:, :, None], 2)[:, :, 0])
+    print(f"[result] masked logits: accept_len {L.tolist()}, draft tokens on masked entries {int(masked.sum())}, "
+          f"ties {ties}", flush=True)
+
+
 def test_standalone_rope(o):
     """spec_verify_rope, out of place and in place, against the oracle."""
     _cuda()

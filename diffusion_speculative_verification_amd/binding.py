@@ -16,7 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_E_NULL, SV_E_SHAPE, SV_E_UNSUPPORTED, SV_E_ALIGN, SV_E_WORKSPACE, SV_E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
-SV_E_INVALID_TAU = -7
+SV_E_INVALID_TAU, SV_E_SCRATCH = -7, -8
+SCRATCH_BYTES = 4 << 20   # SPEC_VERIFY_SCRATCH_BYTES
 SV_F32, SV_BF16 = 0, 1
 
 _lib = None
@@ -54,6 +55,8 @@ def load(path: str | None = None):
     lib.spec_verify_accept_workspace_size.argtypes = [I, I, I, I64]
     lib.spec_verify_accept.restype = I
     lib.spec_verify_accept.argtypes = [V, V, V, V, V, I, I, I, I64, V, V, V, V, SZ, V]
+    lib.spec_verify_accept_noalloc.restype = I
+    lib.spec_verify_accept_noalloc.argtypes = [V, V, V, V, V, I, I, I, I64, V, V, V, V]
     lib.spec_verify_accept_temperature.restype = I
     lib.spec_verify_accept_temperature.argtypes = [V, V, V, V, V, I, I, I, I64, F, V, V, V, V, SZ, V]
     lib.spec_verify_accept_coupled_workspace_size.restype = SZ
@@ -145,6 +148,13 @@ def spec_verify_accept(target_logits, draft_probs, draft_tokens, tau, uniforms, 
                                      _ptr(uniforms), batch, block, gamma, vocab, _ptr(accept_len),
                                      _ptr(out_tokens), _ptr(alpha), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream)))
+
+
+def spec_verify_accept_noalloc(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma, vocab,
+                               accept_len, out_tokens, alpha, stream=None) -> None:
+    _check(load().spec_verify_accept_noalloc(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(tau),
+                                             _ptr(uniforms), batch, block, gamma, vocab, _ptr(accept_len),
+                                             _ptr(out_tokens), _ptr(alpha), _stream(stream)))
 
 
 def spec_verify_accept_temperature(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma,

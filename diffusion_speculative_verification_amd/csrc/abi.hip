@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/spec_verify.h"
 #include "sv_internal.h"
 
@@ -48,6 +50,9 @@ const char *spec_verify_status_string(int status) {
         case SV_E_WORKSPACE: return "workspace missing or too small";
         case SV_E_LAUNCH: return "kernel launch failed";
         case SV_E_INVALID_TAU: return "tau is not a permutation of 1..block";
+        case SV_E_SCRATCH:
+            return "the sizes need more scratch than the library's static buffer holds "
+                   "(SPEC_VERIFY_SCRATCH_BYTES); use the call that takes a workspace";
         default: return "unknown status";
     }
 }
@@ -273,6 +278,66 @@ int spec_verify_accept_temperature(const float *target_logits, const float *draf
     if (!isfinite(inv_t)) return SV_E_SHAPE;
     return accept_impl(target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block, gamma, vocab, inv_t,
                        accept_len, out_tokens, alpha, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free verification epilogue.  Its scratch memory (the normaliser
+// partials, draft-token gathers, rejected-slot records and residual chunk
+// sums that spec_verify_accept keeps in the caller's workspace) is this
+// file-scope device array: every GPU the library runs on holds its own copy
+// from first use until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is taken
+// once per device with hipGetSymbolAddress and only that address is passed
+// to the kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SPEC_VERIFY_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];  // device address of `scratch` per device, NULL until taken
+
+// Device address of the current device's `scratch`, taken on the first call
+// on that device (with the device current); NULL if it cannot be obtained.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_accept_noalloc(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                               const int32_t *tau, const float *uniforms, int batch, int block, int gamma,
+                               int64_t vocab, int32_t *accept_len, int32_t *out_tokens, float *alpha, void *stream) {
+    // the same host checks as spec_verify_accept, before anything else
+    if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
+        vocab > (1ll << 21))
+        return SV_E_SHAPE;
+    if (!rows_ok(batch, block, vocab)) return SV_E_SHAPE;
+    if (!target_logits || !draft_probs || !draft_tokens || !tau || !uniforms || !accept_len || !out_tokens)
+        return SV_E_NULL;
+    if (!aligned16(target_logits) || !aligned16(draft_probs) || !aligned16(draft_tokens) || !aligned16(tau) ||
+        !aligned16(uniforms) || !aligned16(accept_len) || !aligned16(out_tokens) || (alpha && !aligned16(alpha)))
+        return SV_E_ALIGN;
+    const sv::AcceptPlan p = sv::accept_plan(batch, block, gamma, vocab);
+    if (p.ws_total > (size_t)SPEC_VERIFY_SCRATCH_BYTES) return SV_E_SCRATCH;
+    void *ws = device_scratch();
+    if (!ws) return SV_E_LAUNCH;
+    // every scratch entry a kernel reads is written earlier in the same call
+    // (the workspace variant gets uninitialised memory too): nothing to clear
+    return map_launch(sv::launch_accept(p, target_logits, draft_probs, draft_tokens, tau, uniforms, batch, block,
+                                        gamma, vocab, 1.0f, accept_len, out_tokens, alpha, ws, (hipStream_t)stream));
 }
 
 size_t spec_verify_accept_coupled_workspace_size(int batch, int block, int gamma, int64_t vocab) {

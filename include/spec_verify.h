@@ -56,7 +56,10 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 3
+#define SPEC_VERIFY_ABI_VERSION 4
+
+/* Size of the static device scratch buffer of spec_verify_accept_noalloc. */
+#define SPEC_VERIFY_SCRATCH_BYTES (4 << 20)
 
 enum {
     SV_OK = 0,
@@ -66,7 +69,8 @@ enum {
     SV_E_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned     */
     SV_E_WORKSPACE = -5,   /* workspace missing or smaller than required  */
     SV_E_LAUNCH = -6,      /* the HIP runtime refused a kernel launch     */
-    SV_E_INVALID_TAU = -7  /* validation only: tau not a permutation      */
+    SV_E_INVALID_TAU = -7, /* validation only: tau not a permutation      */
+    SV_E_SCRATCH = -8      /* sizes beyond the static scratch buffer      */
 };
 
 enum { SV_F32 = 0, SV_BF16 = 1 };
@@ -320,6 +324,28 @@ int spec_verify_accept(const float *target_logits, const float *draft_probs,
                        int batch, int block, int gamma, int64_t vocab, int32_t *accept_len,
                        int32_t *out_tokens, float *alpha, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * spec_verify_accept without a workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, outputs and results are
+ * those of spec_verify_accept with the workspace dropped.  Its scratch is a
+ * static device buffer of SPEC_VERIFY_SCRATCH_BYTES (4 MiB) inside the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends; the call itself allocates nothing.  Sizes whose
+ * spec_verify_accept_workspace_size exceeds SPEC_VERIFY_SCRATCH_BYTES
+ * return SV_E_SCRATCH before anything is enqueued (32 sequences of 32 slots
+ * over a 151936-token vocabulary need ~90 KB; 64 x 64 slots ~210 KB).
+ * Every call on one GPU shares that GPU's buffer: two calls whose work
+ * overlaps on one GPU (different streams without ordering, or different
+ * threads) race and give wrong results; calls on one stream, or ordered by
+ * events, are safe.  SV_E_LAUNCH if the buffer's device address cannot be
+ * obtained.
+ */
+int spec_verify_accept_noalloc(const float *target_logits, const float *draft_probs,
+                               const int32_t *draft_tokens, const int32_t *tau, const float *uniforms,
+                               int batch, int block, int gamma, int64_t vocab, int32_t *accept_len,
+                               int32_t *out_tokens, float *alpha, void *stream);
 
 /*
  * The same verification epilogue when target and draft sample at temperature

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
 
@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     hdr = open(HEADER).read()
     assert sv.spec_verify_abi_version() == int(re.search(r"#define SPEC_VERIFY_ABI_VERSION (\d+)", hdr).group(1))
-    for code in range(0, -7, -1):
+    for code in range(0, -9, -1):
         assert sv.spec_verify_status_string(code)
     assert sv.spec_verify_status_string(-99) == "unknown status"
 
@@ -278,3 +278,30 @@ def test_binding_raises(lib):
     with pytest.raises(sv.SpecVerifyError) as ei:
         sv.spec_verify_rope(None, A, A, A, 1, 1, 8, 4, 4, 64, 32, 1e4, stream=0)
     assert ei.value.status == sv.SV_E_NULL
+
+
+def test_accept_noalloc_argument_checks(lib):
+    """The allocation-free epilogue checks its arguments on the host like
+    spec_verify_accept, and refuses sizes beyond its static scratch buffer
+    before it touches a device."""
+    def call(**kw):
+        a = dict(l=A, p=A, x=A, tau=A, u=A, batch=2, block=8, gamma=8, vocab=1000, L=A, tok=A, alpha=None)
+        a.update(kw)
+        return lib.spec_verify_accept_noalloc(a["l"], a["p"], a["x"], a["tau"], a["u"], a["batch"], a["block"],
+                                              a["gamma"], a["vocab"], a["L"], a["tok"], a["alpha"], None)
+    assert call(l=None) == sv.SV_E_NULL
+    assert call(tok=None) == sv.SV_E_NULL
+    assert call(gamma=9) == sv.SV_E_SHAPE
+    assert call(block=65, gamma=1) == sv.SV_E_SHAPE
+    assert call(vocab=(1 << 21) + 1) == sv.SV_E_SHAPE
+    assert call(u=A + 4) == sv.SV_E_ALIGN
+    assert call(alpha=A + 8) == sv.SV_E_ALIGN
+    # 2^18 slots need ~8 MiB of partials: more than the 4 MiB buffer
+    big = dict(batch=1 << 12, block=64, gamma=64, vocab=1 << 14)
+    assert sv.spec_verify_accept_workspace_size(big["batch"], 64, 64, big["vocab"]) > sv.SCRATCH_BYTES
+    assert call(**big) == sv.SV_E_SCRATCH
+    # the headline and widest workloads fit
+    assert sv.spec_verify_accept_workspace_size(32, 32, 32, 151936) <= sv.SCRATCH_BYTES
+    assert sv.spec_verify_accept_workspace_size(64, 64, 64, 151936) <= sv.SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert sv.SCRATCH_BYTES == eval(re.search(r"#define SPEC_VERIFY_SCRATCH_BYTES \((.*)\)", hdr).group(1))

@@ -425,8 +425,8 @@ def main():
             e[4].record(stream)
 
     # the same-run peak microbenchmarks go first: after the idle time of the
-    # input generation they put the GPU under load long enough (~0.1 s) for
-    # its clocks to settle, so that even a short warmup ends in steady state
+    # input generation they put the GPU under load (~0.1 s) before the warmup
+    # steps, so that a short warmup starts closer to steady clocks
     peaks = measured_peaks(torch)
     for i in range(args.warmup):
         step(sets[i % n_sets])

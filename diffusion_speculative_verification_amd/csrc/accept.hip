@@ -205,6 +205,24 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double *wave_to
     return base + inc - v;
 }
 
+// The same for a pair of sums at once (both components scanned in the same
+// order, so each equals block_exclusive_scan of that component alone).
+__device__ __forceinline__ double2 block_exclusive_scan2(double2 v, double2 *wave_tot) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    double2 inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double tx = __shfl_up(inc.x, o), ty = __shfl_up(inc.y, o);
+        if (lane >= o) { inc.x += tx; inc.y += ty; }
+    }
+    if (lane == 63) wave_tot[w] = inc;
+    __syncthreads();
+    double bx = 0.0, by = 0.0;
+    for (int k = 0; k < w; ++k) { bx += wave_tot[k].x; by += wave_tot[k].y; }
+    __syncthreads();  // wave_tot may be reused by the caller
+    return make_double2(bx + inc.x - v.x, by + inc.y - v.y);
+}
+
 __device__ __forceinline__ int wave_min_int(int v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
@@ -374,6 +392,8 @@ __global__ void __launch_bounds__(256) accept_resid_kernel(
 // (ascending token order) crosses u * Z, then the token inside it.  Z is the
 // residual mass; when it is zero the target distribution is sampled instead.
 // If rounding leaves no crossing, the last entry with positive mass is taken.
+// VEC (vocab a multiple of 4): the chunk's entries arrive as 16-byte loads.
+template <bool VEC>
 __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restrict__ logits,
                                                             const float *__restrict__ probs,
                                                             const float *__restrict__ u,
@@ -383,6 +403,7 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
                                                             int n_chunk, float inv_t) {
     constexpr int CPT = kMaxChunks / 256;  // chunks per thread
     __shared__ double wave_tot[4];
+    __shared__ double2 wave_tot2[4];
     __shared__ double tot_s[2];
     __shared__ int sel_chunk;
     __shared__ double sel_base;
@@ -408,8 +429,8 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
         my_t += v[k].y;
     }
     if (tid == 0) { pick_first = 0x7fffffff; pick_last = -1; last_chunk = -1; sel_chunk = 0x7fffffff; sel_base = 0.0; }
-    const double ex_r = block_exclusive_scan(my_r, wave_tot);
-    const double ex_t = block_exclusive_scan(my_t, wave_tot);
+    const double2 ex = block_exclusive_scan2(make_double2(my_r, my_t), wave_tot2);
+    const double ex_r = ex.x, ex_t = ex.y;
     if (tid == 255) { tot_s[0] = ex_r + my_r; tot_s[1] = ex_t + my_t; }
     __syncthreads();
     const bool use_t = !(tot_s[0] > 0.0);
@@ -449,11 +470,24 @@ __global__ void __launch_bounds__(256) residual_pick_kernel(const float *__restr
     const float *pr = probs + row * vocab + v0;
     const double inv_sum = 1.0 / ri.s;
     float xl[kPickRun], xp[kPickRun];
+    if (VEC) {
+        // n and the chunk start are multiples of 4: whole float4 or nothing
+        static_assert(kPickRun % 4 == 0, "float4 runs");
 #pragma unroll
-    for (int k = 0; k < kPickRun; ++k) {  // every load in flight before any use
-        const int i = tid * kPickRun + k;
-        xl[k] = i < n ? lr[i] : 0.f;
-        xp[k] = i < n ? pr[i] : 0.f;
+        for (int q = 0; q < kPickRun / 4; ++q) {  // every load in flight before any use
+            const int i = tid * kPickRun + 4 * q;
+            const float4 a4 = i < n ? *reinterpret_cast<const float4 *>(lr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 p4 = i < n ? *reinterpret_cast<const float4 *>(pr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            xl[4 * q] = a4.x; xl[4 * q + 1] = a4.y; xl[4 * q + 2] = a4.z; xl[4 * q + 3] = a4.w;
+            xp[4 * q] = p4.x; xp[4 * q + 1] = p4.y; xp[4 * q + 2] = p4.z; xp[4 * q + 3] = p4.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPickRun; ++k) {  // every load in flight before any use
+            const int i = tid * kPickRun + k;
+            xl[k] = i < n ? lr[i] : 0.f;
+            xp[k] = i < n ? pr[i] : 0.f;
+        }
     }
     double mass[kPickRun], mine = 0.0;
     int lastpos = -1;
@@ -539,8 +573,12 @@ hipError_t launch_accept(const AcceptPlan &p, const float *logits, const float *
                            alpha, res, chunks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(residual_pick_kernel, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks, out_tokens,
-                       block, gamma, vocab, p.n_pick, inv_t);
+    if ((vocab & 3) == 0)
+        hipLaunchKernelGGL(residual_pick_kernel<true>, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks,
+                           out_tokens, block, gamma, vocab, p.n_pick, inv_t);
+    else
+        hipLaunchKernelGGL(residual_pick_kernel<false>, dim3(batch), dim3(256), 0, st, logits, probs, u, res, chunks,
+                           out_tokens, block, gamma, vocab, p.n_pick, inv_t);
     return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ import numpy as np
 
 TIE = 1e-6
 
+# running totals over the session (reported at the end of the test run)
+TOTALS = {"sequences": 0, "ties": 0}
+
 
 def attn_errors(gpu: np.ndarray, ref: np.ndarray):
     d = gpu.astype(np.float64) - ref
@@ -66,4 +69,6 @@ def check_accept(o, inp, gamma, L_g, tok_g, alpha_g, seqs=None, temperature=1.0)
             lo_b = cdf[v - 1] if v > 0 else 0.0
             assert lo_b - TIE * Z <= thr <= cdf[v] + TIE * Z, f"seq {b}: resampled {v} is not a tie"
             ties += 1
+    TOTALS["sequences"] += len(seqs)
+    TOTALS["ties"] += ties
     return ties

@@ -1,8 +1,10 @@
 """HIP path vs the CPU oracle, through the C-ABI, on the same seeded inputs.
 
 Small cases are compared element by element in full; the five workloads run
-at full size in the launch configuration the benchmark times, compared on
-sampled sequences (every head, row and slot of each sampled sequence)."""
+at full size in the launch configuration the benchmark times: the headline
+and long-prefix workloads on every sequence, the wide one on every
+sequence's acceptance and on sampled sequences' attention (every head, row
+and slot of each sampled sequence)."""
 import numpy as np
 import pytest
 
@@ -76,16 +78,17 @@ def test_small_bf16(o):
 
 
 def test_headline_bf16(o):
-    check_case(o, synth.config_by_name("headline"), attn_seqs=[0, 17, 31])
+    check_case(o, synth.config_by_name("headline"))
 
 
 def test_longprefix_bf16(o):
-    check_case(o, synth.config_by_name("longprefix"), attn_seqs=[2])
+    check_case(o, synth.config_by_name("longprefix"))
 
 
 def test_wide_bf16(o):
-    # sequence 7 uses tau = identity (the 2L view), 0 a random order
-    check_case(o, synth.config_by_name("wide"), attn_seqs=[0, 7], acc_seqs=range(0, 64, 4))
+    # sequences 7, 15, ... use tau = identity (the 2L view), the others a
+    # random order; acceptance on all 64
+    check_case(o, synth.config_by_name("wide"), attn_seqs=[0, 7, 20, 31, 47, 63])
 
 
 # --------------------------------------------------------------- edge cases

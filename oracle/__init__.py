@@ -96,6 +96,12 @@ class Oracle:
         lib.svo_tree_verify.argtypes = [P, P, P, P, P, P, i32, i32, i64, ctypes.c_float, P, P, P, P, P]
         lib.svo_commit.argtypes = [P, P, i32, i32, i32, P, P, P]
         lib.svo_kv_append.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, dbl, P, P, P]
+        lib.svo_confidence.argtypes = [P, i64]
+        lib.svo_confidence.restype = dbl
+        lib.svo_transition.argtypes = [P, P, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P]
+        lib.svo_state_walk.argtypes = [P, P, P, i32, i32, i32, P, P, P]
+        lib.svo_tree_states.argtypes = [P, P, P, P, i32, i32, i32, i64, ctypes.c_float, ctypes.c_float, P, P, P,
+                                        P, P]
         lib.svo_set_threads.argtypes = [i32]
         self.lib = lib
 
@@ -332,6 +338,56 @@ class Oracle:
                                            float(np.float32(temperature)), _p(L), _p(ot), _p(tt)))
         return L, ot, tt
 
+    def confidence(self, l) -> float:
+        """Confidence of one slot ("SPOT", 动态阈值解码): max_v softmax(l)_v in float64."""
+        l = _c(l, np.float32)
+        return float(self.lib.svo_confidence(_p(l), l.shape[0]))
+
+    def transition(self, logits, gumbel, state, temperature: float, threshold: float = 1.0):
+        """The target's own transition at one block state: logits/gumbel [L][V]
+        (gumbel None when T = 0), state [L] (-1 masked) -> (commit [L], conf [L]
+        float64, number committed).  threshold >= 1: the one-commit decoder."""
+        logits, state = _c(logits, np.float32), _c(state, np.int32)
+        L, V = logits.shape
+        inv_t = np.float32(1.0) / np.float32(temperature) if temperature > 0 else np.float32(0.0)
+        g = None if temperature == 0 or gumbel is None else _c(gumbel, np.float32)
+        if g is not None:
+            assert g.shape == (L, V)
+        commit = np.empty(L, np.int32)
+        conf = np.empty(L, np.float64)
+        n = self.lib.svo_transition(_p(logits), _p(g), _p(state), L, V, float(inv_t), float(np.float32(threshold)),
+                                    _p(commit), _p(conf))
+        return commit, conf, int(n)
+
+    def state_walk(self, parent, state, commit):
+        """The walk down trees of block states given every node's commit:
+        parent [n][N], state/commit [n][N][L] -> (path_len [n], path [n][N],
+        next_state [n][L])."""
+        parent, state, commit = _c(parent, np.int32), _c(state, np.int32), _c(commit, np.int32)
+        n, N, L = state.shape
+        pl, path, ns = np.empty(n, np.int32), np.empty((n, N), np.int32), np.empty((n, L), np.int32)
+        _check(self.lib.svo_state_walk(_p(parent), _p(state), _p(commit), n, N, L, _p(pl), _p(path), _p(ns)))
+        return pl, path, ns
+
+    def tree_states(self, logits, gumbel, parent, state, temperature: float, threshold: float = 1.0):
+        """Verification of trees of block states ("SPOT"): logits [n][N][L][V],
+        gumbel [n][L][V] (None when T = 0), parent [n][N], state [n][N][L] ->
+        (path_len [n], path [n][N], next_state [n][L], commit [n][N][L],
+        conf [n][N][L] float64)."""
+        logits, parent, state = _c(logits, np.float32), _c(parent, np.int32), _c(state, np.int32)
+        n, N, L, V = logits.shape
+        assert state.shape == (n, N, L) and parent.shape == (n, N)
+        g = None if temperature == 0 or gumbel is None else _c(gumbel, np.float32)
+        if g is not None:
+            assert g.shape == (n, L, V)
+        pl, path, ns = np.empty(n, np.int32), np.empty((n, N), np.int32), np.empty((n, L), np.int32)
+        commit = np.empty((n, N, L), np.int32)
+        conf = np.empty((n, N, L), np.float64)
+        _check(self.lib.svo_tree_states(_p(logits), _p(g), _p(parent), _p(state), n, N, L, V,
+                                        float(np.float32(temperature)), float(np.float32(threshold)), _p(pl),
+                                        _p(path), _p(ns), _p(commit), _p(conf)))
+        return pl, path, ns, commit, conf
+
     def route(self, probs, tau, gamma: int, estimator: str, param: float):
         """S2D2 verify-routing estimator of a batch: probs [n][B][V], tau [n][B];
         estimator "margin" (param = threshold) or "entropy" (param = beta).
@@ -364,6 +420,10 @@ def gather_prefix(*a, **k): return default().gather_prefix(*a, **k)
 def commit(*a, **k): return default().commit(*a, **k)
 def kv_append(*a, **k): return default().kv_append(*a, **k)
 def tree_verify(*a, **k): return default().tree_verify(*a, **k)
+def confidence(l): return default().confidence(l)
+def transition(*a, **k): return default().transition(*a, **k)
+def state_walk(*a, **k): return default().state_walk(*a, **k)
+def tree_states(*a, **k): return default().tree_states(*a, **k)
 def softmax(l): return default().softmax(l)
 def residual(l, pphi, u): return default().residual(l, pphi, u)
 def accept(*a, **k): return default().accept(*a, **k)

@@ -47,7 +47,10 @@
  *   (strict); alpha = 1 when the draft probability of the proposed token is
  *   zero; inverse-CDF resampling in ascending token order with u[gamma];
  *   Z = 0 falls back to the target distribution; a full accept emits no extra
- *   token.
+ *   token; the confidence that orders commit positions is max_v p_theta(v)
+ *   of the untempered model distribution at every temperature (the token at
+ *   the chosen position is the coupled choice); a state with no masked slot
+ *   commits nothing and ends a tree walk.
  */
 #include <math.h>
 #include <stdint.h>
@@ -712,4 +715,144 @@ int svo_tree_verify(const float *logits, const float *gumbel, const int32_t *par
         commit_tok[b] = tt[cur];
     }
     return SVO_OK;
+}
+
+/*
+ * Confidence of one slot ("SPOT", 前置知识 "块扩散语言模型": a decoding step
+ * commits the masked position of highest confidence; "动态阈值解码": the
+ * confidence is c_s = max_v p_theta,s(v)).  With p = softmax(l):
+ * max_v p_v = 1 / sum_v exp(l_v - max l).  All in float64.  The confidence
+ * reads the model's distribution p_theta itself at every temperature (the
+ * page's formula carries no temperature).
+ */
+double svo_confidence(const float *l, int64_t V) {
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v)
+        if ((double)l[v] > m) m = (double)l[v];
+    if (m == -INFINITY) return 0.0;  /* every entry masked: no mass anywhere */
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v) s += exp((double)l[v] - m);
+    return 1.0 / s;
+}
+
+/*
+ * The target's own transition at one block state ("SPOT", 方法步骤详情, 验证:
+ * Phi_0 at T = 0, Phi_G for the fixed noise table G at T > 0; with the rule
+ * of "动态阈值解码" for the set-commit decoder).
+ *   state[L]: the block, a token >= 0 at each decided slot, -1 where masked;
+ *   logits[L][V]: the target's logits at every slot of this state's copy
+ *     (rows of decided slots are not read);
+ *   gumbel[L][V]: the noise-table rows of the block's absolute positions
+ *     (NULL when inv_t <= 0);
+ *   threshold: every masked slot whose confidence exceeds it (strictly) is
+ *     committed; when none does, the single masked slot of highest
+ *     confidence is, the smallest slot among equal confidences.  A threshold
+ *     >= 1 can never be exceeded (c <= 1): the one-commit decoder.
+ * The token at a committed slot is the target's own choice there,
+ * svo_coupled_choice of its row (greedy when inv_t <= 0).
+ * Outputs: commit[L] = that token at each committed slot, -1 elsewhere;
+ *   conf[L] (may be NULL) = the confidence of each masked slot, -1 at
+ *   decided slots.  Returns the number of committed slots (0 when the state
+ *   has no masked slot).
+ */
+int svo_transition(const float *logits, const float *gumbel, const int32_t *state, int L, int64_t V, float inv_t,
+                   float threshold, int32_t *commit, double *conf) {
+    int best = -1, n = 0;
+    double bc = 0.0;
+    for (int s = 0; s < L; ++s) {
+        commit[s] = -1;
+        if (conf) conf[s] = -1.0;
+        if (state[s] >= 0) continue;
+        const double c = svo_confidence(logits + (size_t)s * V, V);
+        if (conf) conf[s] = c;
+        if (best < 0 || c > bc) { best = s; bc = c; }
+        if (c > (double)threshold) {
+            commit[s] = (int32_t)svo_coupled_choice(logits + (size_t)s * V, gumbel ? gumbel + (size_t)s * V : NULL,
+                                                    V, inv_t);
+            ++n;
+        }
+    }
+    if (n == 0 && best >= 0) {
+        commit[best] = (int32_t)svo_coupled_choice(logits + (size_t)best * V,
+                                                   gumbel ? gumbel + (size_t)best * V : NULL, V, inv_t);
+        n = 1;
+    }
+    return n;
+}
+
+/*
+ * The walk down a tree of block states given the target's own commit at
+ * every state ("SPOT", 核心方法, third step: state-equality checks edge by
+ * edge, the one prefix path that agrees with the target's own trajectory is
+ * accepted; 方法步骤详情, 验证: otherwise the target's own result is
+ * committed).  Per sequence, nodes 0..N-1, node 0 the root:
+ *   parent[N] (node 0's ignored; parent[n] in [0, n));
+ *   state[N][L]: each node's block (-1 masked);
+ *   commit[N][L]: the target's own commit at each node (svo_transition).
+ * From the root the walk moves to the child (smallest index if several)
+ * whose state equals the current state with the current commit applied; it
+ * stops at a node with no masked slot (a finished block has nothing left to
+ * commit) or where no child matches.  At most N - 1 edges.
+ * Outputs: path_len[b], path[b][N] (nodes of the walk, root first, -1
+ * after), next_state[b][L] = the last node's state with its commit applied.
+ */
+int svo_state_walk(const int32_t *parent, const int32_t *state, const int32_t *commit, int batch, int N, int L,
+                   int32_t *path_len, int32_t *path, int32_t *next_state) {
+    if (batch < 0 || N < 1 || L < 1) return SVO_BAD_ARG;
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *pb = parent + (size_t)b * N;
+        for (int n = 1; n < N; ++n)
+            if (pb[n] < 0 || pb[n] >= n) return SVO_BAD_ARG;
+        const int32_t *sb = state + (size_t)b * N * L, *cb = commit + (size_t)b * N * L;
+        int32_t *pa = path + (size_t)b * N;
+        for (int n = 0; n < N; ++n) pa[n] = -1;
+        int cur = 0, len = 0;
+        pa[0] = 0;
+        while (len < N - 1) {
+            const int32_t *y = sb + (size_t)cur * L, *cm = cb + (size_t)cur * L;
+            int open = 0;
+            for (int s = 0; s < L; ++s) open |= (y[s] < 0);
+            if (!open) break;
+            int next = -1;
+            for (int c = 1; c < N && next < 0; ++c) {
+                if (pb[c] != cur) continue;
+                const int32_t *z = sb + (size_t)c * L;
+                int eq = 1;
+                for (int s = 0; s < L && eq; ++s) eq = (z[s] == (cm[s] >= 0 ? cm[s] : y[s]));
+                if (eq) next = c;
+            }
+            if (next < 0) break;
+            cur = next;
+            pa[++len] = cur;
+        }
+        path_len[b] = len;
+        const int32_t *y = sb + (size_t)cur * L, *cm = cb + (size_t)cur * L;
+        for (int s = 0; s < L; ++s) next_state[(size_t)b * L + s] = cm[s] >= 0 ? cm[s] : y[s];
+    }
+    return SVO_OK;
+}
+
+/*
+ * Verification of a tree of block states: the target's own transition at
+ * every node (svo_transition) followed by the walk (svo_state_walk).
+ *   logits [batch][N][L][V]: the target's logits at every slot of every
+ *     node's copy; gumbel [batch][L][V]: the noise rows of the block's
+ *     absolute positions, shared by all copies (NULL when temperature == 0);
+ *   parent [batch][N], state [batch][N][L].
+ * Outputs as svo_state_walk, plus commit [batch][N][L] and conf
+ * [batch][N][L] (may be NULL) per node as svo_transition.
+ */
+int svo_tree_states(const float *logits, const float *gumbel, const int32_t *parent, const int32_t *state, int batch,
+                    int N, int L, int64_t V, float temperature, float threshold, int32_t *path_len, int32_t *path,
+                    int32_t *next_state, int32_t *commit, double *conf) {
+    if (batch < 0 || N < 1 || L < 1 || V < 1 || !(temperature >= 0.f) || threshold != threshold) return SVO_BAD_ARG;
+    const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.0f;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int b = 0; b < batch; ++b)
+        for (int n = 0; n < N; ++n) {
+            const size_t node = (size_t)b * N + n;
+            svo_transition(logits + node * L * V, gumbel ? gumbel + (size_t)b * L * V : NULL, state + node * L, L, V,
+                           inv_t, threshold, commit + node * L, conf ? conf + node * L : NULL);
+        }
+    return svo_state_walk(parent, state, commit, batch, N, L, path_len, path, next_state);
 }

@@ -838,6 +838,7 @@ def all_pins(o):
     all_copies_pins(o)
     all_cache_pins(o)
     all_tree_pins(o)
+    all_states_pins(o)
 
 
 # ---------------------------------------------------------------- paged cache, commit, append
@@ -1103,3 +1104,225 @@ def all_tree_pins(o):
     pin_tree_chain_is_coupled(o)
     pin_tree_bruteforce(o)
     pin_tree_rejects_bad_parent(o)
+
+
+# ---------------------------------------------------------------- trees of block states
+def _frac(x):
+    if isinstance(x, str):
+        a, b = x.split("/")
+        return int(a) / int(b)
+    return float(x)
+
+
+def pin_states_golden(o):
+    """The hand-worked fixture: confidences, per-node commits, walk and next
+    state at T = 0 (one-commit and threshold decoders) and at T = 1, and the
+    strict threshold comparison."""
+    g = json.load(open(os.path.join(GOLDEN, "tree_states_tiny.json")))
+    w = np.array(g["weights"], np.float64)
+    lt = np.log(w).astype(np.float32)[None]
+    noise = np.array(g["noise"], np.float32)[None]
+    parent, state = np.array([g["parent"]], np.int32), np.array([g["state"]], np.int32)
+    conf_ref = np.array([[_frac(x) for x in row] for row in g["conf"]])
+    for c in g["cases"]:
+        pl, path, ns, commit, conf = o.tree_states(lt, noise, parent, state, c["temperature"], c["threshold"])
+        assert int(pl[0]) == c["path_len"] and path[0].tolist() == c["path"], (c, pl, path)
+        assert ns[0].tolist() == c["next_state"], (c, ns)
+        assert commit[0].tolist() == c["commit"], (c, commit)
+        assert np.allclose(conf[0], conf_ref, rtol=1e-6, atol=0), (conf[0], conf_ref)
+    s = g["strict"]
+    for c in s["cases"]:
+        commit, conf, n = o.transition(np.array(s["logits"], np.float32), None, np.array(s["state"]), 0.0,
+                                       c["threshold"])
+        assert commit.tolist() == c["commit"], (c, commit, conf)
+        assert n == sum(t >= 0 for t in c["commit"])
+
+
+def pin_confidence_closed_forms(o):
+    """max_v softmax(l)_v: 1/V for a constant row; 1 when one entry is finite
+    and the rest -inf; unchanged by a constant shift of the row (also a large
+    one); equal to the largest probability of a softmax summed exactly."""
+    import math
+    r = np.random.default_rng(130)
+    for V in (1, 2, 7, 1000):
+        assert abs(o.confidence(np.full(V, 3.25, np.float32)) - 1.0 / V) <= 1e-15
+        row = np.full(V, -np.inf, np.float32)
+        row[V // 2] = 0.5
+        assert o.confidence(row) == 1.0
+    for _ in range(30):
+        V = int(r.integers(2, 300))
+        l = (r.standard_normal(V) * r.choice([0.5, 3.0, 20.0])).astype(np.float32)
+        e = [math.exp(float(x) - float(l.max())) for x in l]
+        ref = max(e) / math.fsum(e)
+        c = o.confidence(l)
+        assert abs(c - ref) <= 1e-13 * ref, (c, ref)
+        for shift in (1000.0, -1000.0, 37.0):   # exact in float32 for these rows
+            ls = (l.astype(np.float64) + shift).astype(np.float32)
+            if np.array_equal(ls.astype(np.float64) - shift, l.astype(np.float64)):
+                assert abs(o.confidence(ls) - c) <= 1e-12 * c
+
+
+def _check_transition_rule(commit, conf, state, lt, gum, T, threshold, o):
+    L = state.shape[0]
+    masked = [s for s in range(L) if state[s] < 0]
+    assert all(commit[s] == -1 and conf[s] == -1.0 for s in range(L) if state[s] >= 0)
+    if not masked:
+        assert (commit == -1).all()
+        return
+    above = [s for s in masked if conf[s] > np.float64(np.float32(threshold))]
+    if above:
+        chosen = above
+    else:
+        top = max(conf[s] for s in masked)
+        chosen = [min(s for s in masked if conf[s] == top)]
+    assert sorted(s for s in range(L) if commit[s] >= 0) == chosen, (chosen, commit, conf)
+    for s in chosen:
+        assert commit[s] == o.coupled_choice(lt[s], gum[s] if T > 0 else None, T)
+
+
+def pin_transition_rule(o):
+    """Random states (several identical rows to make exact ties): decided
+    slots are never committed; the committed set is every masked slot above
+    the threshold, or else the first masked slot of highest confidence, each
+    with the target's own (coupled) token; a threshold of 1 or more commits
+    exactly one slot, a negative one every masked slot; the confidences
+    agree with an exactly summed softmax."""
+    import math
+    r = np.random.default_rng(131)
+    for trial in range(400):
+        L, V = int(r.integers(1, 7)), int(r.integers(1, 6))
+        lt = (r.standard_normal((L, V)) * r.choice([0.3, 2.0, 6.0])).astype(np.float32)
+        for s in range(1, L):
+            if r.random() < 0.3:
+                lt[s] = lt[int(r.integers(0, s))]
+        gum = (-np.log(-np.log(r.random((L, V))))).astype(np.float32)
+        state = np.where(r.random(L) < 0.4, r.integers(0, V, L), -1).astype(np.int32)
+        T = float(r.choice([0.0, 1.0, 0.6]))
+        threshold = float(r.choice([1.0, 1.5, 0.5, 0.3, 0.9, -0.1]))
+        commit, conf, n = o.transition(lt, gum, state, T, threshold)
+        _check_transition_rule(commit, conf, state, lt, gum, T, threshold, o)
+        masked = int((state < 0).sum())
+        assert n == int((commit >= 0).sum())
+        if threshold >= 1.0:
+            assert n == min(1, masked)
+        if threshold < 0:
+            assert n == masked
+        for s in range(L):
+            if state[s] < 0:
+                e = [math.exp(float(x) - float(lt[s].max())) for x in lt[s]]
+                assert abs(conf[s] - max(e) / math.fsum(e)) <= 1e-13
+
+
+def pin_state_walk_bruteforce(o):
+    """Random trees and commits: the walk visits exactly the nodes whose every
+    edge from the root equals its parent with the parent's commit applied,
+    never leaving a node without masked slots -- the smallest index where
+    siblings are equal -- and applies the last node's commit."""
+    r = np.random.default_rng(132)
+    for trial in range(400):
+        N, L, V = int(r.integers(1, 9)), int(r.integers(1, 5)), int(r.integers(1, 4))
+        st = [np.where(r.random(L) < 0.3, r.integers(0, V, L), -1).astype(np.int32)]
+        par, commits = [-1], []
+        for n in range(N):
+            y = st[n]
+            masked = np.flatnonzero(y < 0)
+            c = np.full(L, -1, np.int32)
+            if len(masked):                    # any nonempty set of masked slots
+                k = int(r.integers(1, len(masked) + 1))
+                c[r.choice(masked, k, replace=False)] = r.integers(0, V, k)
+            commits.append(c)
+            if n + 1 < N:                      # the next node: a child of an earlier one
+                p = int(r.integers(0, n + 1))
+                yp = st[p]
+                if r.random() < 0.6:           # its parent plus the parent's commit
+                    z = np.where(commits[p] >= 0, commits[p], yp)
+                else:                          # a random commit, or none at all
+                    z = yp.copy()
+                    mp = np.flatnonzero(yp < 0)
+                    if len(mp) and r.random() < 0.9:
+                        z[r.choice(mp)] = int(r.integers(0, V))
+                st.append(z.astype(np.int32))
+                par.append(p)
+        S, C = np.stack(st), np.stack(commits)
+        pl, path, ns = o.state_walk(np.array([par], np.int32), S[None], C[None])
+        ok = [True] + [False] * (N - 1)
+        for n in range(1, N):
+            p = par[n]
+            applied = np.where(C[p] >= 0, C[p], S[p])
+            ok[n] = ok[p] and bool((S[p] < 0).any()) and np.array_equal(S[n], applied)
+        walk, cur = [0], 0
+        while True:
+            kids = [n for n in range(1, N) if par[n] == cur and ok[n]]
+            if not kids:
+                break
+            cur = kids[0]
+            walk.append(cur)
+        assert path[0, :pl[0] + 1].tolist() == walk and (path[0, pl[0] + 1:] == -1).all(), (trial, walk, path)
+        assert ns[0].tolist() == np.where(C[cur] >= 0, C[cur], S[cur]).tolist()
+
+
+def pin_states_one_commit_is_tree_verify(o):
+    """With the one-commit decoder every edge is one (position, token) commit:
+    trees of states verify exactly as the (separately pinned) draft-tree
+    verification given each node's commit position and its row there."""
+    r = np.random.default_rng(133)
+    compared = 0
+    for trial in range(150):
+        N, L, V = int(r.integers(2, 9)), int(r.integers(2, 6)), int(r.integers(2, 5))
+        T = float(r.choice([0.0, 0.8]))
+        lt = (r.standard_normal((N, L, V)) * 2).astype(np.float32)
+        gum = (-np.log(-np.log(r.random((L, V))))).astype(np.float32)
+        root = np.where(r.random(L) < 0.3, r.integers(0, V, L), -1).astype(np.int32)
+        root[int(r.integers(0, L))] = -1
+        states, parent, commits = [root], [-1], []
+        for n in range(N):
+            commits.append(o.transition(lt[n], gum, states[n], T, 1.0)[0])
+            if n + 1 == N:
+                break
+            open_nodes = [p for p in range(n + 1) if (states[p] < 0).sum() >= 2]
+            if not open_nodes:                 # every child must keep a masked slot
+                break
+            p = int(r.choice(open_nodes))
+            y = states[p]
+            if r.random() < 0.6:
+                z = np.where(commits[p] >= 0, commits[p], y)
+            else:
+                z = y.copy()
+                z[r.choice(np.flatnonzero(y < 0))] = int(r.integers(0, V))
+            parent.append(p)
+            states.append(z.astype(np.int32))
+        N = len(states)
+        S = np.stack(states)
+        pl, path, ns, commit, conf = o.tree_states(lt[None, :N], gum[None], np.array([parent]), S[None], T, 1.0)
+        node_pos, node_tok = np.full(N, -1, np.int32), np.full(N, -1, np.int32)
+        for n in range(1, N):
+            d = np.flatnonzero(S[n] != S[parent[n]])
+            node_pos[n], node_tok[n] = d[0], S[n, d[0]]
+        tpos = np.array([int(np.flatnonzero(commit[0, n] >= 0)[0]) for n in range(N)], np.int32)
+        rows = np.stack([lt[n, tpos[n]] for n in range(N)])[None]
+        grow = np.stack([gum[tpos[n]] for n in range(N)])[None]
+        pl2, path2, cp2, ct2, tt2 = o.tree_verify(rows, grow if T > 0 else None, np.array([parent]),
+                                                  node_pos[None], node_tok[None], tpos[None], T)
+        assert pl[0] == pl2[0] and np.array_equal(path, path2), (trial, path, path2)
+        assert ns[0, cp2[0]] == ct2[0] and commit[0, path[0, pl[0]], cp2[0]] == ct2[0]
+        assert (commit[0] >= 0).sum(axis=1).tolist() == [1] * N
+        compared += 1
+    assert compared == 150
+
+
+def pin_states_reject_bad_parent(o):
+    try:
+        o.tree_states(np.zeros((1, 3, 2, 2), np.float32), None, np.array([[-1, 2, 0]]),
+                      np.full((1, 3, 2), -1), 0.0)
+    except oracle_error():
+        return
+    raise AssertionError("a parent after its child was accepted")
+
+
+def all_states_pins(o):
+    pin_states_golden(o)
+    pin_confidence_closed_forms(o)
+    pin_transition_rule(o)
+    pin_state_walk_bruteforce(o)
+    pin_states_one_commit_is_tree_verify(o)
+    pin_states_reject_bad_parent(o)

@@ -73,6 +73,26 @@ MUTANTS = [
     ("resample row untempered", "ob[rs] = (int32_t)svo_residual(z, pk,",
      "ob[rs] = (int32_t)svo_residual(logits + ((size_t)b * B + rs) * V, pk,"),
     ("coupled verifies every slot", "if (tb[k] > gamma) continue;   /* not verified in this call */", ";"),
+    ("confidence without the max shift", "for (int64_t v = 0; v < V; ++v) s += exp((double)l[v] - m);\n    return 1.0 / s;",
+     "for (int64_t v = 0; v < V; ++v) s += exp((double)l[v]);\n    return 1.0 / s;"),
+    ("confidence as the sum", "for (int64_t v = 0; v < V; ++v) s += exp((double)l[v] - m);\n    return 1.0 / s;",
+     "for (int64_t v = 0; v < V; ++v) s += exp((double)l[v] - m);\n    return s;"),
+    ("threshold not strict", "if (c > (double)threshold) {", "if (c >= (double)threshold) {"),
+    ("confidence ties to the larger slot", "if (best < 0 || c > bc) { best = s; bc = c; }",
+     "if (best < 0 || c >= bc) { best = s; bc = c; }"),
+    ("lowest confidence first", "if (best < 0 || c > bc) { best = s; bc = c; }",
+     "if (best < 0 || c < bc) { best = s; bc = c; }"),
+    ("decided slots compete", "if (state[s] >= 0) continue;\n        const double c", ";\n        const double c"),
+    ("no fallback commit", "if (n == 0 && best >= 0) {", "if (0) {"),
+    ("walk leaves finished blocks", "if (!open) break;", ";"),
+    ("walk compares positions only", "eq = (z[s] == (cm[s] >= 0 ? cm[s] : y[s]));",
+     "eq = ((z[s] >= 0) == ((cm[s] >= 0 ? cm[s] : y[s]) >= 0));"),
+    ("walk ignores the commit", "eq = (z[s] == (cm[s] >= 0 ? cm[s] : y[s]));", "eq = (z[s] == y[s] || cm[s] >= 0);"),
+    ("walk takes any later node", "if (pb[c] != cur) continue;\n                const int32_t *z", "if (pb[c] < cur) continue;\n                const int32_t *z"),
+    ("next state from the root", "const int32_t *y = sb + (size_t)cur * L, *cm = cb + (size_t)cur * L;\n        for (int s = 0; s < L; ++s) next_state",
+     "const int32_t *y = sb, *cm = cb;\n        for (int s = 0; s < L; ++s) next_state"),
+    ("state tree ignores the temperature", "const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.0f;\n#pragma omp parallel for schedule(dynamic, 1) collapse(2)",
+     "const float inv_t = 0.0f;\n#pragma omp parallel for schedule(dynamic, 1) collapse(2)"),
 ]
 
 

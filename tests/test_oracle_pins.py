@@ -181,3 +181,27 @@ def test_tree_bruteforce(o):
 
 def test_tree_rejects_bad_parent(o):
     pins.pin_tree_rejects_bad_parent(o)
+
+
+def test_states_golden(o):
+    pins.pin_states_golden(o)
+
+
+def test_confidence_closed_forms(o):
+    pins.pin_confidence_closed_forms(o)
+
+
+def test_transition_rule(o):
+    pins.pin_transition_rule(o)
+
+
+def test_state_walk_bruteforce(o):
+    pins.pin_state_walk_bruteforce(o)
+
+
+def test_states_one_commit_is_tree_verify(o):
+    pins.pin_states_one_commit_is_tree_verify(o)
+
+
+def test_states_reject_bad_parent(o):
+    pins.pin_states_reject_bad_parent(o)

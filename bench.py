@@ -34,8 +34,11 @@ entropy adds S2D2's verify-routing estimate (spec_verify_route, parameter
 verification step instead: attention over C copies of the block (the root
 state and D = C - 1 draft states, spec_verify_attn_copies) followed by
 shared-noise (or, with --verify greedy, greedy) verification of the D draft
-steps; gamma = D.  --copies C --tree verifies a draft tree of the C states
-instead of a chain (spec_verify_tree).  --paged PS keeps the prompt caches in pages of PS rows
+steps; gamma = D.  --copies C --tree verifies a tree of the C block states
+instead of a chain (spec_verify_tree_states: the target's own next commit at
+every state from the logits of every slot of every copy, C * B rows per
+sequence; --threshold t < 1 commits every slot whose confidence exceeds t,
+the dynamic-threshold decoder).  --paged PS keeps the prompt caches in pages of PS rows
 (spec_verify_attn_paged; --ragged gives each sequence its own prompt length)
 and ends each step with the commit step and the cache append of finished
 blocks (spec_verify_commit, spec_verify_kv_append); the prompt lengths and the
@@ -111,12 +114,15 @@ def coupled_bytes(c, greedy: bool) -> float:
     return rows * (1 if greedy else 2) + small
 
 
-def tree_bytes(c, greedy: bool) -> float:
-    """Algorithmic HBM bytes of one draft-tree verification call: the float32
-    target row of every node once, its noise row once (not read when greedy),
-    plus the tree arrays and the outputs."""
-    rows = 4.0 * c.batch * c.n_copies * c.vocab
-    return rows * (1 if greedy else 2) + c.batch * (c.n_copies * 4 * 6 + 12)
+def states_bytes(c, state, greedy: bool) -> float:
+    """Algorithmic HBM bytes of one verification of trees of block states:
+    the float32 logits row of every masked slot of every copy once, the
+    noise row of every slot masked in at least one copy once (shared by the
+    copies; not read when greedy), plus the states, parents and outputs."""
+    masked = state < 0                                   # [batch][N][B]
+    rows = 4.0 * c.vocab * int(masked.sum())
+    noise = 0.0 if greedy else 4.0 * c.vocab * int(masked.any(axis=1).sum())
+    return rows + noise + c.batch * (c.n_copies * (c.block + 2) * 4 + c.block * 4 + 4)
 
 
 def route_bytes(c) -> float:
@@ -181,7 +187,7 @@ def oracle_agreement(o, inp, gamma, temperature, L_o, tok_o, al_o, rs_o, gpu) ->
 
 
 def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
-                 paged=False, tree=False, attn_budget_s=20.0, gpu_accept=None) -> dict:
+                 paged=False, tree=False, attn_budget_s=20.0, gpu_accept=None, threshold=1.0) -> dict:
     """The CPU oracle on this host over the same workload (one step).  The
     attention is timed over the first sequences of the batch until
     `attn_budget_s` has passed and scaled to the whole batch.  With
@@ -221,8 +227,8 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     t_attn = (time.perf_counter() - t) * case.batch / n_seq
     t = time.perf_counter()
     if tree:
-        o.tree_verify(inp["tree_logits"], inp["tree_gumbel"] if temperature > 0 else None, inp["parent"],
-                      inp["node_pos"], inp["node_tok"], inp["target_pos"], temperature)
+        o.tree_states(inp["st_logits"], inp["st_gumbel"] if temperature > 0 else None, inp["st_parent"],
+                      inp["st_state"], temperature, threshold)
         out_tokens = None
     elif verify == "rejection":
         acc_o = o.accept(inp["target_logits"], inp["draft_probs"], inp["draft_tokens"], inp["tau"],
@@ -307,7 +313,9 @@ def main():
                     help="prompt caches in pages of PS rows, plus the commit step and the cache append")
     ap.add_argument("--ragged", action="store_true", help="with --paged: per-sequence prompt lengths")
     ap.add_argument("--tree", action="store_true",
-                    help="with --copies: verify a draft tree of the C states instead of a chain")
+                    help="with --copies: verify a tree of the C block states instead of a chain")
+    ap.add_argument("--threshold", type=float, default=1.0,
+                    help="with --tree: commit every slot whose confidence exceeds it (>= 1: one commit per step)")
     ap.add_argument("--copies", type=int, default=0,
                     help="SPOT multi-copy verification over C copies of the block (root + C-1 draft states)")
     ap.add_argument("--temperature", type=float, default=1.0,
@@ -363,13 +371,15 @@ def main():
     T = 0.0 if verify == "greedy" else args.temperature
     parts = ("attn", "accept") if verify == "rejection" else ("attn", "coupled")
     if copies:
-        parts = ("copies", "tree") if tree else ("copies", "coupled")
+        parts = ("copies", "states") if tree else ("copies", "coupled")
     if paged:
         parts = parts + ("paged",)
     route = args.route
     rparam = args.route_param if args.route_param is not None else (0.05 if route == "margin" else 1.0)
     if verify != "rejection":
         case = case.with_(temperature=T)
+    if tree:
+        case = case.with_(threshold=args.threshold)
     gen_parts = parts + (("accept",) if route != "none" and "accept" not in parts else ())
     inp = synth.make_inputs(case, parts=gen_parts)
     if route != "none":
@@ -399,7 +409,7 @@ def main():
 
     def epilogue(s):
         if tree:
-            s.tree(temperature=T)
+            s.tree_states(details=False)
         elif verify == "rejection":
             s.accept(temperature=None if T == 1.0 else T)
         else:
@@ -458,7 +468,7 @@ def main():
     ms_step = total_ms / K
     attn_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
     acc_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
-    L = (sets[0].path_len if tree else sets[0].accept_len if verify == "rejection" else sets[0].cpl_accept_len).cpu()
+    L = (sets[0].st_path_len if tree else sets[0].accept_len if verify == "rejection" else sets[0].cpl_accept_len).cpu()
     n_rej = int((L < case.gamma).sum())
     slots = case.batch * case.gamma
     value = slots / (ms_step * 1e-3)
@@ -467,7 +477,7 @@ def main():
     a_bytes, a_flops = attn_bytes(case, copies, prompt_rows), attn_flops(case, copies, prompt_rows)
     attn_call = "spec_verify_attn_copies" if copies else "spec_verify_attn_paged" if paged else "spec_verify_attn"
     if tree:
-        c_bytes, acc_call = tree_bytes(case, T == 0), "spec_verify_tree"
+        c_bytes, acc_call = states_bytes(case, inp["st_state"], T == 0), "spec_verify_tree_states"
     else:
         c_bytes = accept_bytes(case, n_rej) if verify == "rejection" else coupled_bytes(case, T == 0)
         acc_call = "spec_verify_accept" if verify == "rejection" else "spec_verify_accept_coupled"
@@ -559,7 +569,8 @@ def main():
         if verify == "rejection" and not tree and not paged:
             # the GPU's outputs of the inputs in `inp` (every input set holds them)
             gpu_acc = (sets[0].accept_len.cpu().numpy(), sets[0].out_tokens.cpu().numpy())
-        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree, gpu_accept=gpu_acc)
+        cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree, gpu_accept=gpu_acc,
+                           threshold=case.threshold)
 
     out = {
         "metric": METRIC,
@@ -575,7 +586,10 @@ def main():
         "dtype": case.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{case.name} SPOT multi-copy verify step: {copies} copies (root + D={copies - 1} "
-                                f"draft states" + (" in a draft tree" if tree else "") + "), gamma=D"
+                                f"draft states" + (" in a tree of block states" +
+                                                   (f", commit threshold {case.threshold:g}"
+                                                    if case.threshold < 1 else ", one commit per step")
+                                                   if tree else "") + "), gamma=D"
                                 if copies else f"{case.name} verify step") +
                                f": batch {case.batch}, prefix {case.prefix_len}, "
                                f"B={case.block}, gamma={case.gamma}, {case.n_qh}/{case.n_kvh} heads, "
@@ -591,6 +605,7 @@ def main():
                    "route": None if route == "none" else {"estimator": route, "param": rparam},
                    "verify": verify, "temperature": None if verify == "rejection" and T == 1.0 else T,
                    "copies": copies or None, "tree": tree if copies else None,
+                   "threshold": case.threshold if tree else None,
                    "page_size": case.page_size if paged else None, "ragged": bool(case.ragged) if paged else None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,

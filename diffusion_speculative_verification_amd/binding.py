@@ -76,6 +76,10 @@ def load(path: str | None = None):
     lib.spec_verify_tree_workspace_size.argtypes = [I, I, I64]
     lib.spec_verify_tree.restype = I
     lib.spec_verify_tree.argtypes = [V, V, V, V, V, V, I, I, I64, F, V, V, V, V, V, V, SZ, V]
+    lib.spec_verify_tree_states_workspace_size.restype = SZ
+    lib.spec_verify_tree_states_workspace_size.argtypes = [I, I, I, I64]
+    lib.spec_verify_tree_states.restype = I
+    lib.spec_verify_tree_states.argtypes = [V, V, V, V, I, I, I, I64, F, F, V, V, V, V, V, V, SZ, V]
     lib.spec_verify_check_tau.restype = I
     lib.spec_verify_check_tau.argtypes = [V, I, I, V, V]
     lib.spec_verify_commit.restype = I
@@ -244,6 +248,19 @@ def spec_verify_check_tau(tau, batch, block, bad, stream=None) -> None:
 
 def spec_verify_tree_workspace_size(batch, n_nodes, vocab) -> int:
     return int(load().spec_verify_tree_workspace_size(batch, n_nodes, vocab))
+
+
+def spec_verify_tree_states_workspace_size(batch, n_nodes, block, vocab) -> int:
+    return int(load().spec_verify_tree_states_workspace_size(batch, n_nodes, block, vocab))
+
+
+def spec_verify_tree_states(target_logits, gumbel, parent, state, batch, n_nodes, block, vocab, temperature,
+                            threshold, path_len, path, next_state, commit, confidence, workspace, workspace_bytes,
+                            stream=None) -> None:
+    _check(load().spec_verify_tree_states(_ptr(target_logits), _ptr(gumbel), _ptr(parent), _ptr(state), batch,
+                                          n_nodes, block, int(vocab), float(temperature), float(threshold),
+                                          _ptr(path_len), _ptr(path), _ptr(next_state), _ptr(commit),
+                                          _ptr(confidence), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def spec_verify_tree(target_logits, gumbel, parent, node_pos, node_tok, target_pos, batch, n_nodes, vocab,

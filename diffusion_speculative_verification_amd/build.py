@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["attn.hip", "accept.hip", "coupled.hip", "route.hip", "commit.hip", "abi.hip"]
+SOURCES = ["attn.hip", "accept.hip", "coupled.hip", "states.hip", "route.hip", "commit.hip", "abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -403,6 +403,34 @@ int spec_verify_tree(const float *target_logits, const float *gumbel, const int3
                                       commit_tok, target_tok, workspace, (hipStream_t)stream));
 }
 
+size_t spec_verify_tree_states_workspace_size(int batch, int n_nodes, int block, int64_t vocab) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || block < 1 || block > 64 || vocab < 1 || vocab > (1ll << 21) ||
+        !rows_ok(batch, n_nodes * block, vocab))
+        return 0;
+    return sv::states_plan(batch, n_nodes, block, vocab).ws_total;
+}
+
+int spec_verify_tree_states(const float *target_logits, const float *gumbel, const int32_t *parent,
+                            const int32_t *state, int batch, int n_nodes, int block, int64_t vocab, float temperature,
+                            float threshold, int32_t *path_len, int32_t *path, int32_t *next_state, int32_t *commit,
+                            float *confidence, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || block < 1 || block > 64 || vocab < 1 || vocab > (1ll << 21))
+        return SV_E_SHAPE;
+    if (!rows_ok(batch, n_nodes * block, vocab)) return SV_E_SHAPE;
+    if (!(temperature >= 0.f) || !isfinite(temperature) || isnan(threshold)) return SV_E_SHAPE;
+    if (!target_logits || !parent || !state || !path_len || !path || !next_state) return SV_E_NULL;
+    if (temperature > 0.f && !gumbel) return SV_E_NULL;
+    if (!aligned16(target_logits) || (gumbel && !aligned16(gumbel))) return SV_E_ALIGN;
+    const sv::StatesPlan p = sv::states_plan(batch, n_nodes, block, vocab);
+    if (!workspace || workspace_bytes < p.ws_total) return SV_E_WORKSPACE;
+    if (!aligned16(workspace)) return SV_E_ALIGN;
+    const float inv_t = temperature > 0.f ? 1.0f / temperature : 0.f;
+    if (temperature > 0.f && !isfinite(inv_t)) return SV_E_SHAPE;
+    return map_launch(sv::launch_states(p, target_logits, temperature > 0.f ? gumbel : nullptr, parent, state, batch,
+                                        n_nodes, block, vocab, inv_t, threshold, path_len, path, next_state, commit,
+                                        confidence, workspace, (hipStream_t)stream));
+}
+
 size_t spec_verify_route_workspace_size(int batch, int block, int gamma, int64_t vocab) {
     if (batch < 1 || block < 1 || block > 64 || gamma < 1 || gamma > block || vocab < 1 ||
         vocab > (1ll << 21) || !rows_ok(batch, block, vocab))

@@ -102,6 +102,19 @@ hipError_t launch_tree(const CoupledPlan &p, const float *logits, const float *n
                        int n_nodes, int64_t vocab, float inv_t, int32_t *path_len, int32_t *path, int32_t *commit_pos,
                        int32_t *commit_tok, int32_t *target_tok, void *ws, hipStream_t st);
 
+struct StatesPlan {
+    long long rows;  // batch * n_nodes * block logits rows
+    int n_vsplit;    // vocab splits of the streaming pass
+    size_t ws_total;
+};
+
+StatesPlan states_plan(int batch, int n_nodes, int block, int64_t vocab);
+
+hipError_t launch_states(const StatesPlan &p, const float *logits, const float *noise, const int32_t *parent,
+                         const int32_t *state, int batch, int n_nodes, int block, int64_t vocab, float inv_t,
+                         float threshold, int32_t *path_len, int32_t *path, int32_t *next_state, int32_t *commit,
+                         float *conf, void *ws, hipStream_t st);
+
 hipError_t launch_check_tau(const int32_t *tau, int batch, int block, int32_t *bad, hipStream_t st);
 
 hipError_t launch_commit(const int32_t *out_tokens, int32_t *block_tokens, int batch, int block, int gamma,

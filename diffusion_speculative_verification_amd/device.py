@@ -101,6 +101,19 @@ class StepBuffers:
             n = sv.spec_verify_tree_workspace_size(c.batch, N, c.vocab)
             self.tree_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self.tree_ws_bytes = n
+        if "states" in parts:
+            N = c.n_copies
+            self.st_logits = up(inputs["st_logits"])
+            self.st_gumbel = up(inputs["st_gumbel"])
+            self.st_parent, self.st_state = up(inputs["st_parent"]), up(inputs["st_state"])
+            self.st_path_len = torch.empty(c.batch, dtype=torch.int32, device=device)
+            self.st_path = torch.empty((c.batch, N), dtype=torch.int32, device=device)
+            self.st_next = torch.empty((c.batch, c.block), dtype=torch.int32, device=device)
+            self.st_commit = torch.empty((c.batch, N, c.block), dtype=torch.int32, device=device)
+            self.st_conf = torch.empty((c.batch, N, c.block), dtype=torch.float32, device=device)
+            n = sv.spec_verify_tree_states_workspace_size(c.batch, N, c.block, c.vocab)
+            self.st_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self.st_ws_bytes = n
         if "route" in parts:
             if not hasattr(self, "draft_probs"):
                 self.draft_probs = up(inputs["draft_probs"])
@@ -203,6 +216,18 @@ class StepBuffers:
                             self.node_tok, self.target_pos, c.batch, c.n_copies, c.vocab, T, self.path_len,
                             self.path, self.commit_pos, self.commit_tok, self.tree_target_tok, self.tree_ws,
                             self.tree_ws_bytes, stream)
+
+    def tree_states(self, temperature=None, threshold=None, details=True, stream=None):
+        """Verification of the case's tree of block states ("SPOT"): the
+        target's own transition from every copy's logits, then the walk.
+        details=False leaves the optional per-node outputs unwritten."""
+        c = self.case
+        T = c.temperature if temperature is None else temperature
+        thr = c.threshold if threshold is None else threshold
+        sv.spec_verify_tree_states(self.st_logits, self.st_gumbel if T > 0 else None, self.st_parent, self.st_state,
+                                   c.batch, c.n_copies, c.block, c.vocab, T, thr, self.st_path_len, self.st_path,
+                                   self.st_next, self.st_commit if details else None,
+                                   self.st_conf if details else None, self.st_ws, self.st_ws_bytes, stream)
 
     def route(self, estimator: str, param: float, stream=None):
         """S2D2 verify-routing estimate K of every sequence (margin or entropy)."""

@@ -40,6 +40,19 @@ numpy default_rng(SeedSequence([s, t, b]))):
       synthetic drafter: a child commits at its parent's target position the
       draft's own Gumbel-max token (draft logits = target + N(0,1)) with
       probability 3/4, otherwise another (position, token); siblings differ
+  t=17 tree of block states of case.n_copies nodes (root = node 0): the
+      root block has a uniform number in [B/2, B] of masked slots (-1), the
+      others hold uniform tokens; node k's parent is one of the three nodes
+      before it that still has a masked slot (else the root).  Per node, the
+      logits of every masked slot are iid N(0, var_t) in float32 (rows of
+      decided slots are NaN: they must never be read), and the generator
+      plants peaks: one masked slot gets +16 at a uniform token (with a
+      threshold below 1: 1-3 slots get +18, and with probability 1/2 one
+      more gets +13), unless logit_model is "iid".  The synthetic drafter's
+      child of a node is, with probability 3/4, the node with its planted
+      slots set to their planted tokens, otherwise the node with 1 (with a
+      threshold: 1-3) uniform masked slots set to uniform tokens.  Noise
+      rows [B][V] as t=10, shared by every node.
   t=15 (one stream for the batch) the page permutation of a paged cache: the
       sequences' page tables take consecutive runs of a random permutation of
       all pages, with one spare page per sequence that no table names
@@ -88,6 +101,7 @@ class Case:
     n_copies: int = 9          # multi-copy verification: root + 8 draft states
     page_size: int = 64        # paged prompt cache: rows per page
     ragged: bool = False       # paged inputs: per-sequence prompt lengths
+    threshold: float = 1.0     # trees of block states: commit threshold (>= 1: one commit per step)
 
     @property
     def rows(self) -> int:
@@ -278,7 +292,69 @@ def make_inputs(case: Case, parts=("attn", "accept"), seqs=None, threads: int | 
         _paged(case, out, seqs)
     if "tree" in parts:
         _tree(case, out, seqs, threads)
+    if "states" in parts:
+        _states(case, out, seqs, threads)
     return out
+
+
+def _states(case: Case, out: dict, seqs, threads: int) -> None:
+    """Trees of block states (tensor id 17): st_parent [n][N], st_state
+    [n][N][B], st_logits [n][N][B][V], st_gumbel [n][B][V], N = case.n_copies."""
+    n, N, B, V = len(seqs), case.n_copies, case.block, case.vocab
+    sets, plant = case.threshold < 1.0, case.logit_model != "iid"
+    sd = np.float32(np.sqrt(case.target_var))
+    out["st_parent"] = np.full((n, N), -1, np.int32)
+    out["st_state"] = np.full((n, N, B), -1, np.int32)
+    out["st_logits"] = np.empty((n, N, B, V), np.float32)
+    out["st_gumbel"] = np.empty((n, B, V), np.float32)
+
+    def fill(i):
+        r = _rng(case, 17, seqs[i])
+        u = np.maximum(r.random((B, V)), np.finfo(np.float64).tiny)
+        out["st_gumbel"][i] = (-np.log(-np.log(u))).astype(np.float32)
+        st = out["st_state"][i]
+        root = r.integers(0, V, B).astype(np.int32)
+        root[r.choice(B, int(r.integers(max(1, B // 2), B + 1)), replace=False)] = -1
+        st[0] = root
+        planted = []
+        for k in range(N):
+            if k > 0:
+                cand = [q for q in range(max(0, k - 3), k) if (st[q] < 0).any()] or [0]
+                p = int(cand[int(r.integers(0, len(cand)))])
+                y = st[p].copy()
+                if r.random() < 0.75 and planted[p]:
+                    for s_, v_ in planted[p].items():
+                        y[s_] = v_
+                else:
+                    m = np.flatnonzero(y < 0)
+                    j = min(len(m), int(r.integers(1, 4)) if sets else 1)
+                    y[r.choice(m, j, replace=False)] = r.integers(0, V, j)
+                out["st_parent"][i, k] = p
+                st[k] = y
+            lg = out["st_logits"][i, k]
+            masked = np.flatnonzero(st[k] < 0)
+            lg[st[k] >= 0] = np.nan
+            for s_ in masked:
+                lg[s_] = r.standard_normal(V, dtype=np.float32) * sd
+            pk = {}
+            if plant and len(masked):
+                if sets:
+                    hi = r.choice(masked, min(len(masked), int(r.integers(1, 4))), replace=False)
+                    for s_ in hi:
+                        pk[int(s_)] = int(r.integers(0, V))
+                        lg[s_, pk[int(s_)]] += np.float32(18.0)
+                    rest = [q for q in masked if q not in pk]
+                    if rest and r.random() < 0.5:
+                        q = int(rest[int(r.integers(0, len(rest)))])
+                        lg[q, int(r.integers(0, V))] += np.float32(13.0)
+                else:
+                    s_ = int(masked[int(r.integers(0, len(masked)))])
+                    pk[s_] = int(r.integers(0, V))
+                    lg[s_, pk[s_]] += np.float32(16.0)
+            planted.append(pk)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(n)))
 
 
 def _tree(case: Case, out: dict, seqs, threads: int) -> None:

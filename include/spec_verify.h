@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 4
+#define SPEC_VERIFY_ABI_VERSION 5
 
 /* Size of the static device scratch buffer of spec_verify_accept_noalloc. */
 #define SPEC_VERIFY_SCRATCH_BYTES (4 << 20)
@@ -230,6 +230,60 @@ int spec_verify_tree(const float *target_logits, const float *gumbel, const int3
                      const int32_t *node_tok, const int32_t *target_pos, int batch, int n_nodes, int64_t vocab,
                      float temperature, int32_t *path_len, int32_t *path, int32_t *commit_pos, int32_t *commit_tok,
                      int32_t *target_tok, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace spec_verify_tree_states needs for these sizes (0 when
+ * the sizes are out of range). */
+size_t spec_verify_tree_states_workspace_size(int batch, int n_nodes, int block, int64_t vocab);
+
+/*
+ * Verification of a tree of block states, the target's own transition
+ * computed from its logits ("SPOT: Enhancing Speculative Decoding for
+ * Diffusion Language Models via Commit-Order Prediction": 前置知识
+ * "块扩散语言模型", a decoding step commits the masked position of highest
+ * confidence; 前置知识 "动态阈值解码", confidence c_s = max_v p_theta,s(v), every
+ * masked position above a threshold committed, else the single highest;
+ * 核心方法 third step and 方法步骤详情 验证, one forward over the root and all
+ * draft copies gives the target's own next transition at every state, Phi_0
+ * at T = 0 and Phi_G for the fixed noise table at T > 0, edges whose child
+ * equals it are accepted, otherwise the target's own result is committed).
+ * Per sequence, nodes 0..n_nodes-1, node 0 the root (the copies of
+ * spec_verify_attn_copies):
+ *   target_logits [batch][n_nodes][block][vocab] float32: the target's
+ *     logits at every slot of every node's copy; rows of decided slots are
+ *     never read.  -inf entries have probability 0.
+ *   gumbel [batch][block][vocab] float32: the noise-table rows of the
+ *     block's absolute positions, shared by every copy (NULL allowed when
+ *     temperature == 0).
+ *   parent [batch][n_nodes]: node n's parent, in [0, n) (node 0's is
+ *     ignored; a node whose parent lies outside that range is never
+ *     entered).
+ *   state [batch][n_nodes][block]: each node's block, a token >= 0 at every
+ *     decided slot, -1 where masked.
+ *   threshold: the dynamic-threshold rule; any value >= 1 gives the
+ *     one-commit decoder (no confidence exceeds 1).
+ * At every node: c_s = 1 / sum_v exp(l_v - max l) per masked slot (the
+ * untempered distribution at every temperature; normaliser in float64), the
+ * commit set is every masked slot with c_s > threshold (compared in
+ * float64), else the masked slot of highest c_s (the smallest slot among
+ * equal values), and the token at a committed slot is argmax_v fmaf(l_v,
+ * 1/T, g_v) in float32 (T == 0: argmax_v l_v), the smallest v among equal
+ * scores.  From the root the walk moves to the child (smallest index if
+ * several) whose state equals the current state with the current commit
+ * applied; it stops at a node without masked slots or where no child
+ * matches.
+ * Outputs: path_len [batch] = accepted edges; path [batch][n_nodes] = the
+ * nodes of the walk, root first, -1 after; next_state [batch][block] = the
+ * last node's state with its commit applied (the block after this step);
+ * commit [batch][n_nodes][block] (optional) = each node's commit, token or
+ * -1; confidence [batch][n_nodes][block] float32 (optional) = c_s at masked
+ * slots, -1 at decided ones.
+ * 1 <= n_nodes <= 64, 1 <= block <= 64, 1 <= vocab <= 2^21, temperature >= 0
+ * finite, threshold not NaN; logits and gumbel 16-byte aligned.
+ */
+int spec_verify_tree_states(const float *target_logits, const float *gumbel, const int32_t *parent,
+                            const int32_t *state, int batch, int n_nodes, int block, int64_t vocab, float temperature,
+                            float threshold, int32_t *path_len, int32_t *path, int32_t *next_state, int32_t *commit,
+                            float *confidence, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Validation of the step labels ("SimSD: Simple Speculative Decoding in

@@ -24,3 +24,6 @@ def pytest_terminal_summary(terminalreporter):
     if t["sequences"]:
         terminalreporter.write_line(f"acceptance parity: {t['sequences']} sequences compared with the oracle, "
                                     f"{t['ties']} counted ties")
+    if t.get("tree_sequences"):
+        terminalreporter.write_line(f"state-tree parity: {t['tree_sequences']} sequences compared with the oracle, "
+                                    f"{t['tree_ties']} counted ties")

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
 
@@ -213,6 +213,38 @@ def test_paged_argument_checks(lib):
     assert call(kp=None) == sv.SV_E_NULL
     assert call(o=A + 4) == sv.SV_E_ALIGN
     assert call(wb=0) == sv.SV_E_WORKSPACE
+
+
+def test_tree_states_argument_checks(lib):
+    f = lib.spec_verify_tree_states
+    ok = dict(l=A, g=A, par=A, st=A, b=32, n=9, L=32, V=151936, T=1.0, thr=1.0, pl=A, path=A, ns=A, cm=A, cf=A,
+              ws=A, wb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["l"], a["g"], a["par"], a["st"], a["b"], a["n"], a["L"], a["V"], a["T"], a["thr"], a["pl"],
+                 a["path"], a["ns"], a["cm"], a["cf"], a["ws"], a["wb"], None)
+    ws = sv.spec_verify_tree_states_workspace_size(32, 9, 32, 151936)
+    assert ws >= 32 * 9 * 32 * 24
+    assert sv.spec_verify_tree_states_workspace_size(32, 65, 32, 151936) == 0
+    assert sv.spec_verify_tree_states_workspace_size(32, 9, 65, 151936) == 0
+    assert sv.spec_verify_tree_states_workspace_size(32, 9, 32, (1 << 21) + 1) == 0
+    assert call(n=65) == sv.SV_E_SHAPE
+    assert call(L=0) == sv.SV_E_SHAPE
+    assert call(L=65) == sv.SV_E_SHAPE
+    assert call(T=-1.0) == sv.SV_E_SHAPE
+    assert call(T=float("nan")) == sv.SV_E_SHAPE
+    assert call(thr=float("nan")) == sv.SV_E_SHAPE
+    assert call(T=1e-45) == sv.SV_E_SHAPE          # 1/T overflows float32
+    assert call(b=(1 << 14) + 1, n=64, L=64, V=4) == sv.SV_E_SHAPE  # more than 2^26 rows
+    assert call(g=None) == sv.SV_E_NULL            # T > 0 needs the noise rows
+    assert call(st=None) == sv.SV_E_NULL
+    assert call(ns=None) == sv.SV_E_NULL
+    assert call(l=A + 4) == sv.SV_E_ALIGN
+    assert call(g=A + 8) == sv.SV_E_ALIGN
+    assert call(wb=ws - 1) == sv.SV_E_WORKSPACE
+    assert call(ws=A + 4, wb=ws) == sv.SV_E_ALIGN
 
 
 def test_tree_argument_checks(lib):

@@ -18,10 +18,13 @@
 //                          the max logit, the normaliser sum exp(l - max) in
 //                          float64, and the argmax of the coupled score
 //                          fmaf(l, 1/T, g) (l alone when greedy) with its
-//                          smallest index.  16-byte non-temporal loads of the
-//                          logits (read once), 4 in flight per lane; the
-//                          noise rows are read with ordinary loads, because
-//                          the copies of one slot read the same row.
+//                          smallest index (a lane takes the best score of
+//                          each round of 16 entries first and looks for its
+//                          index only when it beats the running best).
+//                          16-byte non-temporal loads of the logits (read
+//                          once), 4 in flight per lane; the noise rows are
+//                          read with ordinary loads, because the copies of
+//                          one slot read the same row.
 //   states_walk_kernel     one workgroup per sequence: a wave per node turns
 //                          its slots' partials into confidences (1 / sum, in
 //                          float64) and applies the threshold rule with
@@ -117,20 +120,31 @@ __global__ void __launch_bounds__(256) states_partial_kernel(const float *__rest
                 if (m != -INFINITY) sum *= (double)__builtin_amdgcn_exp2f((m - gm) * kLog2e);
                 m = gm;
             }
-            // while every entry so far is -inf, so is m: subtracting 0 keeps
-            // exp(-inf - m) at 0 rather than NaN
             const float mu = (m == -INFINITY) ? 0.f : m;
             float ps = 0.f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (i + 256 * u >= c1) break;
-                const int32_t v = (int32_t)(4 * (i + 256 * u));
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ps += __builtin_amdgcn_exp2f((x[u][e] - mu) * kLog2e);
-                    const float sc = GREEDY ? x[u][e] : fmaf(x[u][e], inv_t, g[u][e]);
-                    if (st_better(sc, v + e, bs, bi)) { bs = sc; bi = v + e; }
-                }
+                for (int e = 0; e < 4; ++e) ps += __builtin_amdgcn_exp2f((x[u][e] - mu) * kLog2e);
+            // the coupled argmax: the round's best score first, its first
+            // index only when it beats the running best (entries ascend)
+            st_f4 sc[4];
+            float gs = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[u][e] = GREEDY ? x[u][e] : fmaf(x[u][e], inv_t, g[u][e]);
+                gs = fmaxf(gs, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+            }
+            if (gs > bs) {
+                int32_t idx = INT32_MAX;
+#pragma unroll
+                for (int u = 3; u >= 0; --u)
+#pragma unroll
+                    for (int e = 3; e >= 0; --e)
+                        if (sc[u][e] == gs) idx = (int32_t)(4 * (i + 256 * u)) + e;
+                bs = gs;
+                bi = idx;
             }
             sum += (double)ps;
         }
@@ -175,42 +189,47 @@ __device__ __forceinline__ double wave_max_f64(double v) {
     return v;
 }
 
-constexpr int kWalkThreads = 256;
+constexpr int kWalkThreads = 1024;
+constexpr int kWalkWaves = kWalkThreads / 64;
 constexpr int kMaxStateCells = 64 * 64;  // n_nodes * block
 
+// Every global load of a sequence's tree is issued before any of its values
+// is used (one round trip of latency): the parents, and per node wave the
+// states and vocab-split partials of its slots, the partials read whether or
+// not the slot is masked (a decided slot's partial is never written, and its
+// value is discarded).
 __global__ void __launch_bounds__(kWalkThreads) states_walk_kernel(
     const SPart *__restrict__ parts, const int32_t *__restrict__ parent, const int32_t *__restrict__ state,
     int n_nodes, int block, int n_vsplit, double threshold, int32_t *path_len, int32_t *path, int32_t *next_state,
     int32_t *commit_out, float *conf_out) {
     __shared__ int32_t st[kMaxStateCells];   // every node's block
     __shared__ int32_t cm[kMaxStateCells];   // every node's commit (token or -1)
+    __shared__ int32_t par[64];
     __shared__ uint8_t open[64], match[64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t b = blockIdx.x;
     const bool in_slot = lane < block;
+    if (threadIdx.x < n_nodes) par[threadIdx.x] = parent[b * n_nodes + threadIdx.x];
     // 1. per node (one wave each): confidences and the threshold rule, lane = slot
-    for (int n = w; n < n_nodes; n += kWalkThreads / 64) {
+    for (int n = w; n < n_nodes; n += kWalkWaves) {
         const size_t row = ((size_t)b * n_nodes + n) * block + (in_slot ? lane : 0);
         const int y = in_slot ? state[row] : 0;
-        const bool masked = in_slot && y < 0;
-        double c = -1.0;
-        int32_t x = -1;
-        if (masked) {
-            float m = -INFINITY, bs = -INFINITY;
-            double sum = 0.0;
-            int32_t bi = INT32_MAX;
-            for (int i = 0; i < n_vsplit; ++i) {
-                const SPart p = parts[row * n_vsplit + i];
-                lse_merge(m, sum, p.m, p.s);
-                if (st_better(p.bs, p.bi, bs, bi)) { bs = p.bs; bi = p.bi; }
-            }
-            c = sum > 0.0 ? 1.0 / sum : 0.0;
-            x = bi;
+        float m = -INFINITY, bs = -INFINITY;
+        double sum = 0.0;
+        int32_t bi = INT32_MAX;
+#pragma unroll 4
+        for (int i = 0; i < n_vsplit; ++i) {
+            const SPart q = parts[row * n_vsplit + i];
+            lse_merge(m, sum, q.m, q.s);
+            if (st_better(q.bs, q.bi, bs, bi)) { bs = q.bs; bi = q.bi; }
         }
+        const bool masked = in_slot && y < 0;
+        const double c = masked ? (sum > 0.0 ? 1.0 / sum : 0.0) : -1.0;
+        const int32_t x = (bi == INT32_MAX) ? 0 : bi;  // every entry -inf: the smallest index
         const unsigned long long any = __ballot(masked);
         unsigned long long take = __ballot(masked && c > threshold);
         if (take == 0 && any != 0) {
-            const double top = wave_max_f64(masked ? c : -1.0);
+            const double top = wave_max_f64(c);
             const unsigned long long tops = __ballot(masked && c == top);
             take = tops & (~tops + 1);  // the smallest slot of highest confidence
         }
@@ -225,8 +244,8 @@ __global__ void __launch_bounds__(kWalkThreads) states_walk_kernel(
     }
     __syncthreads();
     // 2. per node: does it equal its parent with the parent's commit applied?
-    for (int n = w; n < n_nodes; n += kWalkThreads / 64) {
-        const int p = (n > 0) ? parent[b * n_nodes + n] : -1;
+    for (int n = w; n < n_nodes; n += kWalkWaves) {
+        const int p = (n > 0) ? par[n] : -1;
         const bool valid = p >= 0 && p < n;  // parents come before their children
         bool eq = true;
         if (valid && in_slot) {
@@ -240,12 +259,12 @@ __global__ void __launch_bounds__(kWalkThreads) states_walk_kernel(
     // 3. the walk from the root (wave 0, lane = node)
     if (w == 0) {
         const bool in_node = lane < n_nodes;
-        const int par = (in_node && lane > 0) ? parent[b * n_nodes + lane] : -1;
+        const int pn = (in_node && lane > 0) ? par[lane] : -1;
         const bool ok = in_node && lane > 0 && match[lane];
         int cur = 0, len = 0;
         for (; len < n_nodes - 1; ++len) {
             if (!open[cur]) break;  // a finished block commits nothing more
-            const unsigned long long kids = __ballot(ok && par == cur);
+            const unsigned long long kids = __ballot(ok && pn == cur);
             if (!kids) break;
             cur = __ffsll((long long)kids) - 1;
             if (lane == 0) path[b * n_nodes + len + 1] = cur;
@@ -267,7 +286,7 @@ __global__ void __launch_bounds__(kWalkThreads) states_walk_kernel(
 StatesPlan states_plan(int batch, int n_nodes, int block, int64_t vocab) {
     StatesPlan p{};
     p.rows = (long long)batch * n_nodes * block;
-    long long vs = (2048 + p.rows - 1) / p.rows;
+    long long vs = (16384 + p.rows - 1) / p.rows;  // about 8 workgroups per CU slot
     long long cap = vocab / 16384;
     if (cap < 1) cap = 1;
     if (vs > cap) vs = cap;

@@ -14,10 +14,13 @@ float32 logits.  Two copies of the inputs live in HBM and steps alternate
 between them, so a step never finds the previous step's data in the 256 MB
 last-level cache.
 
-Prints ONE JSON line (rank 0, N = 1).  After W untimed steps, K steps are
-timed with events only at their two ends (value, ms_per_step); the same K
-steps then run again with HIP events on the launch stream around every call,
-which gives the per-call durations.  `roofline` is the step's: every call at
+Prints ONE JSON line (rank 0, N = 1).  Every call is launched from Python
+(--launch graph instead captures each input set's step once in a HIP graph
+and replays it: the same time, since the step is GPU-bound).  After W
+untimed steps, K steps are timed with events only at their two ends
+(value, ms_per_step); the same K steps then run again, launched call by call
+with HIP events on the launch stream around every call, which gives the
+per-call durations.  `roofline` is the step's: every call at
 its bound (HBM bytes at 8 TB/s, or bf16 MFMA flops at 2.5 PFLOP/s when they
 take longer) against the timed step; `roofline.dominant_kernel` gives the
 dominant call's own rate against its bound.  Same-run peak microbenchmarks
@@ -324,6 +327,9 @@ def main():
                     help="add the S2D2 verify-routing estimate in front of each step")
     ap.add_argument("--route-param", type=float, default=None,
                     help="margin threshold (default 0.05) or entropy beta (default 1.0)")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="launch every call from Python (default), or replay each input set's step captured in a "
+                         "HIP graph (the same time at every workload measured: the step is GPU-bound)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -434,12 +440,38 @@ def main():
         if e:
             e[4].record(stream)
 
+    # one graph per input set: the step's calls captured once (every call
+    # allocates nothing, sets no memory with memset and never synchronises),
+    # after an eager step on a side stream as capture requires
+    graphs = None
+    if args.launch == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for s_ in sets:
+                step(s_)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for s_ in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s_)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if graphs is not None:
+            graphs[i % n_sets].replay()
+        else:
+            step(sets[i % n_sets])
+
     # the same-run peak microbenchmarks go first: after the idle time of the
     # input generation they put the GPU under load (~0.1 s) before the warmup
     # steps, so that a short warmup starts closer to steady clocks
     peaks = measured_peaks(torch)
     for i in range(args.warmup):
-        step(sets[i % n_sets])
+        run_step(i)
     torch.cuda.synchronize()
 
     # timed pass: K steps with events only at its two ends (an event between
@@ -450,7 +482,7 @@ def main():
     wall0 = time.perf_counter()
     t_begin.record(stream)
     for i in range(K):
-        step(sets[i % n_sets])
+        run_step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -609,7 +641,7 @@ def main():
                    "page_size": case.page_size if paged else None, "ragged": bool(case.ragged) if paged else None,
                    "batch": case.batch, "prefix_len": case.prefix_len, "block": case.block, "gamma": case.gamma,
                    "n_qh": case.n_qh, "n_kvh": case.n_kvh, "head_dim": case.head_dim, "vocab": case.vocab,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "launch": args.launch},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": {

@@ -104,3 +104,45 @@ def test_graph_copies_and_tree():
     buf = StepBuffers(case, inp, parts=("copies", "tree"))
     _graph_check(buf, lambda: (buf.attn_copies(), buf.tree(temperature=1.0)),
                  [buf.out_c, buf.path_len, buf.path, buf.commit_pos, buf.commit_tok, buf.tree_target_tok])
+
+
+def test_graph_tree_states():
+    print("[case] graph: multi-copy attention + verification of a tree of block states", flush=True)
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_speculative_verification_amd.device import StepBuffers
+    for T, thr in ((1.0, 1.0), (0.0, 0.9)):
+        case = synth.config_by_name("small").with_(n_copies=5, gamma=4, temperature=T, threshold=thr, vocab=20000)
+        inp = synth.make_inputs(case, parts=("copies", "states"))
+        buf = StepBuffers(case, inp, parts=("copies", "states"))
+        _graph_check(buf, lambda: (buf.attn_copies(), buf.tree_states()),
+                     [buf.out_c, buf.st_path_len, buf.st_path, buf.st_next, buf.st_commit, buf.st_conf])
+
+
+def test_graph_paged_step_with_restore():
+    """The benchmark's paged step as one graph: the commit and append, then
+    the two device copies that restore the prompt lengths and the block."""
+    print("[case] graph: paged step with the restoring copies inside the graph", flush=True)
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_speculative_verification_amd.device import StepBuffers
+    case = synth.config_by_name("small").with_(page_size=64, ragged=True)
+    inp = synth.make_inputs(case, parts=("attn", "accept", "paged"))
+    buf = StepBuffers(case, inp, parts=("attn", "accept", "paged"))
+
+    def step():
+        buf.attn_paged()
+        buf.accept()
+        buf.commit(buf.out_tokens)
+        buf.kv_append(buf.k_new, buf.v_new, 2 * case.block)
+        buf.prefix_lens.copy_(buf.prefix_lens0)
+        buf.block_tokens.copy_(buf.block_tokens0)
+
+    def restore():   # the clobbered state back before each replay; the graph's own copies restore it after
+        buf.prefix_lens.copy_(buf.prefix_lens0)
+        buf.block_tokens.copy_(buf.block_tokens0)
+
+    # after a replay the block and the prompt lengths must hold the restored
+    # values (the in-graph copies ran after the commit and the append)
+    _graph_check(buf, step, [buf.out_paged, buf.accept_len, buf.out_tokens, buf.block_tokens, buf.prefix_lens,
+                             buf.remaining, buf.state, buf.n_append], restore=restore)

@@ -627,6 +627,8 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
                                          char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
                                          double *__restrict__ invf, int *__restrict__ klab) {
     constexpr int NS = D / 16, NTH = 64 * NW;
+    // one thread per entry of the paired layout's key-label table below
+    static_assert(NTH > 2 * kMaxBlock, "the key-label table needs 2 * kMaxBlock + 1 threads");
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)
@@ -970,9 +972,13 @@ AttnPlan attn_plan(const AttnShape &s) {
     p.n_split = 1;
     p.tiles_per_split = p.n_tiles;
     if (s.dtype == 1) {
-        // aim for about one workgroup per compute unit (256 CUs)
+        // aim for about one workgroup per compute unit (256 CUs) -- unless
+        // a workgroup would stream only a few tiles anyway: at 9 tiles (a
+        // 512-key prompt) the merge launch and the float32 partials cost
+        // more than the idle compute units (24.7 us unsplit vs 26.4 us in
+        // three splits, batch 8)
         const long units = (long)s.batch * s.n_kvh * p.n_rb;
-        if (units < 256 && p.n_tiles >= 4) {
+        if (units < 256 && p.n_tiles > 12) {
             int want = (int)((256 + units - 1) / units);
             want = want < p.n_tiles / 2 ? want : p.n_tiles / 2;
             if (want > 1) {

@@ -1,7 +1,9 @@
 """A seeded sweep of random shapes through the calls that stream a
 vocabulary -- rejection sampling (at T = 1 and at another temperature),
-shared-noise or greedy verification, the routing estimate (both estimators)
-and draft-tree verification -- against the CPU oracle through the C-ABI:
+shared-noise or greedy verification, the routing estimate (both estimators),
+draft-tree verification and the verification of a tree of block states (the
+target's own transition at one-commit and dynamic thresholds) -- against the
+CPU oracle through the C-ABI:
 batch, block, gamma, node counts and vocabulary sizes (multiples of 4 and
 not, one vocabulary split and several) drawn within the documented limits.
 Integer results must be identical (ties of the rejection sampler counted),
@@ -102,5 +104,17 @@ def test_vocab_sweep(o, sh):
     assert np.array_equal(buf.tree_target_tok.cpu().numpy(), tt)
     assert np.array_equal(buf.path_len.cpu().numpy(), pl) and np.array_equal(buf.path.cpu().numpy(), path)
     assert np.array_equal(buf.commit_pos.cpu().numpy(), cp) and np.array_equal(buf.commit_tok.cpu().numpy(), ct)
+    # a tree of block states: every masked slot of every copy streams the
+    # vocabulary (node count capped to keep the logits within 160 MB)
+    ns = max(1, min(sh["nodes"], 40_000_000 // (case.batch * case.block * case.vocab)))
+    thr = float(np.random.default_rng(sh["seed"]).choice([1.0, 0.9, 0.5]))
+    scase = case.with_(n_copies=ns, threshold=thr)
+    sinp = synth.make_inputs(scase, parts=("states",))
+    sbuf = StepBuffers(scase, sinp, parts=("states",))
+    sbuf.tree_states(temperature=T, threshold=thr)
+    torch.cuda.synchronize()
+    g = [t.cpu().numpy() for t in (sbuf.st_path_len, sbuf.st_path, sbuf.st_next, sbuf.st_commit, sbuf.st_conf)]
+    st_ties = parity.check_states(o, sinp, T, thr, *g)
     print(f"[result] ok: accept_len {buf.accept_len.cpu().numpy().tolist()[:6]}, "
-          f"tree edges {pl.tolist()[:6]}", flush=True)
+          f"tree edges {pl.tolist()[:6]}, state-tree edges {g[0].tolist()[:6]} ({ns} nodes, threshold {thr}, "
+          f"ties {st_ties})", flush=True)

@@ -77,12 +77,16 @@ __global__ void __launch_bounds__(256) states_partial_kernel(const float *__rest
     __shared__ float red_m[4], red_bs[4];
     __shared__ double red_s[4];
     __shared__ int32_t red_bi[4];
-    // Workgroups go round-robin over the 8 XCDs: workgroup i takes task
-    // (i % 8) * per + i / 8, so each XCD runs one contiguous range of tasks
-    // and the copies of one (slot, vocab split) -- adjacent tasks, reading
-    // the same noise chunk -- run together on one XCD and share its L2.
-    const long long per = (long long)(gridDim.x >> 3);
-    const long long task = (long long)(blockIdx.x & 7) * per + (long long)(blockIdx.x >> 3);
+    // Workgroups go round-robin over the 8 XCDs (workgroup i to XCD i % 8).
+    // Tasks come in groups of n_nodes -- the copies of one (slot, vocab
+    // split), which read the same noise chunk -- and the groups are dealt
+    // round-robin over the XCDs: the j-th workgroup an XCD receives takes
+    // copy j % n_nodes of that XCD's (j / n_nodes)-th group, so a group's
+    // copies run one after another on one XCD and share its L2, while every
+    // XCD gets groups from every sequence (equal shares of the masked rows;
+    // whole sequences per XCD left the XCDs up to 2x apart in work).
+    const long long j = (long long)(blockIdx.x >> 3);
+    const long long task = (8 * (j / n_nodes) + (blockIdx.x & 7)) * n_nodes + j % n_nodes;
     if (task >= n_tasks) return;
     const int n = (int)(task % n_nodes);
     long long t = task / n_nodes;
@@ -302,7 +306,8 @@ hipError_t launch_states(const StatesPlan &p, const float *logits, const float *
                          float *conf, void *ws, hipStream_t st) {
     SPart *parts = (SPart *)ws;
     const long long n_tasks = p.rows * p.n_vsplit;
-    const dim3 g1((unsigned)((n_tasks + 7) / 8 * 8));
+    const long long unit = 8LL * n_nodes;  // whole groups for every XCD
+    const dim3 g1((unsigned)((n_tasks + unit - 1) / unit * unit));
     const bool vec = (vocab & 3) == 0, greedy = !(inv_t > 0.f);
     if (vec && greedy)
         hipLaunchKernelGGL((states_partial_kernel<true, true>), g1, dim3(256), 0, st, logits, noise, state, parts,

@@ -12,7 +12,8 @@
 // output position, shared by all copies).
 //
 // Two launches on the caller's stream:
-//   states_partial_kernel  one streaming pass over the float32 logits of
+//   states_partial_kernel (or states_partial_noise_kernel, below)
+//                          one streaming pass over the float32 logits of
 //                          every masked slot of every copy (rows of decided
 //                          slots are skipped): per (node, slot, vocab split)
 //                          the max logit, the normaliser sum exp(l - max) in
@@ -24,7 +25,10 @@
 //                          16-byte non-temporal loads of the logits (read
 //                          once), 4 in flight per lane; the noise rows are
 //                          read with ordinary loads, because the copies of
-//                          one slot read the same row.
+//                          one slot read the same row.  At T > 0 on the
+//                          16-byte path, states_partial_noise_kernel streams
+//                          two copies of a slot per workgroup, so each noise
+//                          load serves both.
 //   states_walk_kernel     one workgroup per sequence: a wave per node turns
 //                          its slots' partials into confidences (1 / sum, in
 //                          float64) and applies the threshold rule with
@@ -187,6 +191,138 @@ __global__ void __launch_bounds__(256) states_partial_kernel(const float *__rest
     }
 }
 
+struct RowAcc {
+    float m, bs;
+    double sum;
+    int32_t bi;
+};
+
+// One copy's running state in the shared-noise pass, and one round of 16
+// entries of its row (as in states_partial_kernel's 16-byte path)
+__device__ __forceinline__ void acc_round(RowAcc &A, const st_f4 (&x)[4], const st_f4 (&g)[4], float inv_t,
+                                          int64_t i) {
+    float gm = A.m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gm = fmaxf(gm, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+    if (gm > A.m) {
+        if (A.m != -INFINITY) A.sum *= (double)__builtin_amdgcn_exp2f((A.m - gm) * kLog2e);
+        A.m = gm;
+    }
+    const float mu = (A.m == -INFINITY) ? 0.f : A.m;
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += __builtin_amdgcn_exp2f((x[u][e] - mu) * kLog2e);
+    st_f4 sc[4];
+    float gs = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[u][e] = fmaf(x[u][e], inv_t, g[u][e]);
+        gs = fmaxf(gs, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+    }
+    if (gs > A.bs) {
+        int32_t idx = INT32_MAX;
+#pragma unroll
+        for (int u = 3; u >= 0; --u)
+#pragma unroll
+            for (int e = 3; e >= 0; --e)
+                if (sc[u][e] == gs) idx = (int32_t)(4 * (i + 256 * u)) + e;
+        A.bs = gs;
+        A.bi = idx;
+    }
+    A.sum += (double)ps;
+}
+
+__device__ __forceinline__ void acc_merge_write(RowAcc A, SPart *dst) {
+    __shared__ float red_m[4], red_bs[4];
+    __shared__ double red_s[4];
+    __shared__ int32_t red_bi[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(A.m, o), bs2 = __shfl_xor(A.bs, o);
+        const double s2 = __shfl_xor(A.sum, o);
+        const int32_t bi2 = __shfl_xor(A.bi, o);
+        lse_merge(A.m, A.sum, m2, s2);
+        if (st_better(bs2, bi2, A.bs, A.bi)) { A.bs = bs2; A.bi = bi2; }
+    }
+    __syncthreads();
+    if (lane == 0) { red_m[w] = A.m; red_s[w] = A.sum; red_bs[w] = A.bs; red_bi[w] = A.bi; }
+    __syncthreads();
+    if (tid == 0) {
+        for (int k = 1; k < 4; ++k) {
+            lse_merge(A.m, A.sum, red_m[k], red_s[k]);
+            if (st_better(red_bs[k], red_bi[k], A.bs, A.bi)) { A.bs = red_bs[k]; A.bi = red_bi[k]; }
+        }
+        *dst = SPart{A.m, A.bs, A.bi, 0, A.sum};
+    }
+}
+
+// The shared-noise pass (T > 0, vocabulary a multiple of 4): NC copies of
+// one (slot, vocab split) per workgroup, each 16-byte noise load serving all
+// of them (two copies: 728 -> 682 us at the headline tree against one copy
+// per workgroup; three tie with two, four lose occupancy).  Task groups and
+// their XCD dealing as in states_partial_kernel, a group being the
+// ceil(n_nodes / NC) workgroups of one (slot, vocab split).
+template <int NC>
+__global__ void __launch_bounds__(256) states_partial_noise_kernel(const float *__restrict__ logits,
+                                                                   const float *__restrict__ noise,
+                                                                   const int32_t *__restrict__ state, SPart *parts,
+                                                                   int n_nodes, int block, int64_t vocab,
+                                                                   int n_vsplit, long long n_tasks, float inv_t) {
+    const int G = (n_nodes + NC - 1) / NC;
+    const long long j = (long long)(blockIdx.x >> 3);
+    const long long task = (8 * (j / G) + (blockIdx.x & 7)) * G + j % G;
+    if (task >= n_tasks) return;
+    const int k = (int)(task % G);
+    long long t = task / G;
+    const int sp = (int)(t % n_vsplit);
+    t /= n_vsplit;
+    const int s = (int)(t % block);
+    const long long b = t / block;
+    size_t row[NC];
+    bool act[NC];
+    bool any = false;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int n = NC * k + c;
+        row[c] = ((size_t)b * n_nodes + (n < n_nodes ? n : NC * k)) * block + s;
+        act[c] = n < n_nodes && state[row[c]] < 0;
+        any |= act[c];
+    }
+    if (!any) return;
+    const size_t nrow = (size_t)b * block + s;
+    const int tid = threadIdx.x;
+    RowAcc A[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) A[c] = RowAcc{-INFINITY, -INFINITY, 0.0, INT32_MAX};
+    const int64_t n4 = vocab >> 2;
+    const int64_t c0 = n4 * sp / n_vsplit, c1 = n4 * (sp + 1) / n_vsplit;
+    const st_f4 *gsrc = reinterpret_cast<const st_f4 *>(noise + nrow * vocab);
+    for (int64_t i = c0 + tid; i < c1; i += 256 * 4) {
+        st_f4 x[NC][4], g[4];
+        const st_f4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = i + 256 * u < c1;
+            g[u] = ok ? gsrc[i + 256 * u] : st_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                x[c][u] = (ok && act[c])
+                    ? __builtin_nontemporal_load(reinterpret_cast<const st_f4 *>(logits + row[c] * vocab) + i + 256 * u)
+                    : ninf;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (act[c]) acc_round(A[c], x[c], g, inv_t, i);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        if (act[c]) acc_merge_write(A[c], parts + row[c] * n_vsplit + sp);
+}
+
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
@@ -312,9 +448,13 @@ hipError_t launch_states(const StatesPlan &p, const float *logits, const float *
     if (vec && greedy)
         hipLaunchKernelGGL((states_partial_kernel<true, true>), g1, dim3(256), 0, st, logits, noise, state, parts,
                            n_nodes, block, vocab, p.n_vsplit, n_tasks, inv_t);
-    else if (vec)
-        hipLaunchKernelGGL((states_partial_kernel<true, false>), g1, dim3(256), 0, st, logits, noise, state, parts,
-                           n_nodes, block, vocab, p.n_vsplit, n_tasks, inv_t);
+    else if (vec) {
+        constexpr int NC = 2;  // copies per workgroup sharing the noise loads
+        const long long gsz = (n_nodes + NC - 1) / NC, n_tasks2 = n_tasks / n_nodes * gsz, unit2 = 8 * gsz;
+        const dim3 g2((unsigned)((n_tasks2 + unit2 - 1) / unit2 * unit2));
+        hipLaunchKernelGGL(states_partial_noise_kernel<NC>, g2, dim3(256), 0, st, logits, noise, state, parts,
+                           n_nodes, block, vocab, p.n_vsplit, n_tasks2, inv_t);
+    }
     else if (greedy)
         hipLaunchKernelGGL((states_partial_kernel<false, true>), g1, dim3(256), 0, st, logits, noise, state, parts,
                            n_nodes, block, vocab, p.n_vsplit, n_tasks, inv_t);

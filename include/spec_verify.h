@@ -277,8 +277,17 @@ size_t spec_verify_tree_states_workspace_size(int batch, int n_nodes, int block,
  * commit [batch][n_nodes][block] (optional) = each node's commit, token or
  * -1; confidence [batch][n_nodes][block] float32 (optional) = c_s at masked
  * slots, -1 at decided ones.
- * 1 <= n_nodes <= 64, 1 <= block <= 64, 1 <= vocab <= 2^21, temperature >= 0
- * finite, threshold not NaN; logits and gumbel 16-byte aligned.
+ * 1 <= n_nodes <= 64, 1 <= block <= 64, 1 <= vocab <= 2^21, batch * n_nodes *
+ * block <= 2^26 rows and rows * vocab <= 2^40, temperature >= 0 finite,
+ * threshold not NaN; logits and gumbel 16-byte aligned.  Status: SV_E_SHAPE
+ * for sizes out of range, a negative, NaN or infinite temperature (or one
+ * whose 1/T overflows float32) or a NaN threshold; SV_E_NULL for a missing
+ * input or output (gumbel is required when temperature > 0; commit and
+ * confidence may be NULL); SV_E_ALIGN; SV_E_WORKSPACE when the workspace is
+ * missing or smaller than spec_verify_tree_states_workspace_size (24 bytes
+ * per (node, slot, vocabulary part), written before it is read within the
+ * call's two launches).  A parent array that is not a tree gives a wrong path
+ * but the call still ends (a walk has at most n_nodes - 1 edges).
  */
 int spec_verify_tree_states(const float *target_logits, const float *gumbel, const int32_t *parent,
                             const int32_t *state, int batch, int n_nodes, int block, int64_t vocab, float temperature,

@@ -124,3 +124,44 @@ def test_states_repeat_bit_identical(o):
                                                        buf.st_conf)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_states_irregular_trees(o):
+    """Trees the synthetic drafter never builds: a chain of 16 single commits
+    from a fully masked root, each node its parent with the target's own
+    commit applied, ending in a finished block; a child of that finished
+    node identical to it (the walk stops at a finished block); a child equal
+    to its parent (no commit: never an edge); and a sibling equal to a chain
+    node but with a larger index (the smaller index is taken).  At threshold
+    1 the walk must run the whole chain; at 0.5 it is checked against the
+    oracle only."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    case = BASE.with_(batch=4, n_copies=20, block=16, vocab=3000, temperature=0.0)
+    inp = synth.make_inputs(case, parts=("states",))
+    st, par, lt = inp["st_state"], inp["st_parent"], inp["st_logits"]
+    r = np.random.default_rng(77)
+
+    def fresh_rows(b, n):   # N(0, 3) rows at the masked slots, NaN at the decided ones
+        lt[b, n] = (r.standard_normal((case.block, case.vocab)) * np.sqrt(3.0)).astype(np.float32)
+        lt[b, n][st[b, n] >= 0] = np.nan
+
+    for b in range(case.batch):
+        st[b, 0] = -1
+        fresh_rows(b, 0)
+        for n in range(1, 17):   # the chain 0 -> 1 -> ... -> 16
+            par[b, n] = n - 1
+            commit, _, _ = o.transition(lt[b, n - 1], None, st[b, n - 1], 0.0, 1.0)
+            st[b, n] = np.where(commit >= 0, commit, st[b, n - 1])
+            fresh_rows(b, n)
+        assert (st[b, 16] >= 0).all()           # 16 commits fill the block
+        par[b, 17], st[b, 17] = 16, st[b, 16]   # a finished node's identical child
+        par[b, 18], st[b, 18] = 3, st[b, 3]     # a child equal to its parent
+        par[b, 19], st[b, 19] = 15, st[b, 16]   # equal to node 16, a larger index
+        for n in (17, 18, 19):
+            fresh_rows(b, n)
+    for thr in (1.0, 0.5):
+        g = run(o, case, inp, 0.0, thr)
+        if thr == 1.0:
+            assert (g[0] == 16).all() and (g[1][:, :17] == np.arange(17)).all() and (g[1][:, 17:] == -1).all()
+            assert np.array_equal(g[2], st[:, 16])

@@ -504,6 +504,9 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 #pragma unroll
             for (int x = 0; x < 16; ++x) sacc[qb][kb][x] = 0.f;
     constexpr int KSTEP = NS / NL;  // S MFMAs between two refill loads
+    // refill load i goes out after S MFMA i * KSTEP + 1 of the 2 * NS: all
+    // 2 * NL of them only when KSTEP divides evenly and is at least 2
+    static_assert(NS % NL == 0 && KSTEP >= 2, "every refill load must be issued between the S MFMAs");
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll

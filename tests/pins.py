@@ -448,6 +448,29 @@ def pin_accept_special_cases(o):
     assert used and abs(Z - 1) < 1e-12 and cdf[tok] > 0.5 and (tok == 0 or cdf[tok - 1] <= 0.5)
 
 
+def pin_residual_boundaries(o):
+    """The inverse CDF at the ends of the uniform's range, on a row whose
+    residual (p_theta - p_phi)^+ is positive at tokens 1 and 4 only: u = 0
+    takes the first token with mass; a u just below 1 crosses at token 4,
+    the last one with mass; at u = 1 (one past the documented range) no
+    running sum exceeds u * Z and the rule falls back to the last token
+    with positive mass -- still 4, not the later zero-mass tokens 5..7.
+    With p_phi >= p_theta everywhere the target itself is sampled, and the
+    fallback then skips tokens whose target mass is 0 (-inf logits)."""
+    lt = np.log(np.arange(1, 9, dtype=np.float64)).astype(np.float32)
+    pt, _, _ = o.softmax(lt)
+    pd = np.where(np.isin(np.arange(8), [1, 4]), 0.5 * pt, 1.5 * pt).astype(np.float32)
+    for u, want in ((0.0, 1), (float(np.float32(1.0 - 2 ** -24)), 4), (1.0, 4)):
+        tok, cdf, Z, used = o.residual(lt, pd, u)
+        assert not used and tok == want, (u, tok, want)
+        assert Z > 0 and cdf[-1] == cdf[4] == Z and cdf[0] == 0.0
+    lt2 = lt.copy()
+    lt2[6:] = -np.inf
+    pt2, _, _ = o.softmax(lt2)
+    tok, cdf, Z, used = o.residual(lt2, (1.5 * pt2).astype(np.float32), 1.0)
+    assert used and tok == 5 and abs(Z - 1.0) < 1e-12, (tok, Z)
+
+
 def pin_accept_assembly(o, seed=34):
     """Output layout: tokens of steps 1..L are the draft tokens, the slot of
     step L+1 holds the resample, slots of later steps and of steps > gamma
@@ -536,6 +559,7 @@ def all_accept_pins(o, exact=True):
     pin_softmax(o)
     pin_accept_tv_identity(o)
     pin_accept_special_cases(o)
+    pin_residual_boundaries(o)
     pin_accept_assembly(o)
     pin_accept_energy(o)
     pin_accept_tempered(o)

@@ -150,6 +150,42 @@ def test_all_accepted_and_all_rejected(o):
     assert (res["L"] == 0).all()
 
 
+@pytest.mark.parametrize("vocab", [151936, 100003])
+def test_resample_uniform_boundaries(o, vocab):
+    """The resample's uniform at the ends of its range, every sequence
+    rejecting (step uniforms 0.9999) and the last three target logits -inf
+    (no residual mass there): u = 0 takes the first token with residual
+    mass, u = 1 - 2^-24 crosses at (about) the last, and u = 1 -- one past
+    the documented range -- falls back on both sides to the last token with
+    positive residual mass, before the tail.  Then draft probabilities 1.5x
+    the target's (an empty residual: the target itself is sampled): u = 1
+    falls back to V - 4, the last token with target mass."""
+    print(f"[case] resample uniform boundaries vocab={vocab}", flush=True)
+    _cuda()
+    case = SMALL.with_(vocab=vocab, batch=6)
+    inp = synth.make_inputs(case, parts=("accept",))
+    lt = inp["target_logits"]
+    lt[:, :, -3:] = -np.inf
+    u_end = np.array([0.0, 1.0 - 2.0 ** -24, 1.0], np.float32)
+    inp["uniforms"][:, :case.gamma] = np.float32(0.9999)
+    inp["uniforms"][:, case.gamma] = u_end[np.arange(case.batch) % 3]
+    res = run(case, inp, parts=("accept",))
+    ties = parity.check_accept(o, inp, case.gamma, res["L"], res["tok"], res["alpha"])
+    assert (res["L"] < case.gamma).all()
+    rs = np.array([np.nonzero(inp["tau"][b] == res["L"][b] + 1)[0][0] for b in range(case.batch)])
+    picked = res["tok"][np.arange(case.batch), rs]
+    assert (picked[1::3] <= vocab - 4).all() and (picked[2::3] <= vocab - 4).all(), picked   # never the -inf tail
+    p = np.exp(lt.astype(np.float64) - lt.max(axis=2, keepdims=True))
+    inp["draft_probs"] = (1.5 * p / p.sum(axis=2, keepdims=True)).astype(np.float32)
+    inp["uniforms"][:, case.gamma] = np.float32(1.0)
+    res2 = run(case, inp, parts=("accept",))
+    ties += parity.check_accept(o, inp, case.gamma, res2["L"], res2["tok"], res2["alpha"])
+    assert (res2["L"] == 0).all()
+    first = np.array([np.nonzero(inp["tau"][b] == 1)[0][0] for b in range(case.batch)])
+    assert (res2["tok"][np.arange(case.batch), first] == vocab - 4).all(), res2["tok"]
+    print(f"[result] resample boundaries: ties {ties}", flush=True)
+
+
 @pytest.mark.parametrize("vocab,run", [(20000, 5000), (151936, 9000), (1001, 1), (8191, 3000)])
 @pytest.mark.parametrize("temperature", [1.0, 0.7])
 def test_masked_logits(o, vocab, run, temperature):

@@ -35,6 +35,8 @@ MUTANTS = [
     ("residual operands swapped", "const double r = pt - (double)pphi[v];", "const double r = (double)pphi[v] - pt;"),
     ("resample mass operands swapped", "double mass = use_t ? pt : pt - (double)pphi[v];", "double mass = use_t ? pt : (double)pphi[v] - pt;"),
     ("resample at wrong slot", "rs = o[L + 1];", "rs = o[L > 0 ? L : 1];"),
+    ("resample fallback to the last token", "if (pick < 0) pick = last_pos;", "if (pick < 0) pick = V - 1;"),
+    ("resample fallback ignores zero mass", "if (mass > 0) last_pos = v;", "last_pos = v;"),
     ("resample uses step uniform", "(double)ub[gamma], NULL", "(double)ub[0], NULL"),
     ("coupled noise subtracted", "? fmaf(l[v], inv_t, g[v]) : l[v];", "? fmaf(l[v], inv_t, -g[v]) : l[v];"),
     ("coupled ties to the largest index", "if (sc > bs) { bs = sc; best = v; }", "if (sc >= bs) { bs = sc; best = v; }"),

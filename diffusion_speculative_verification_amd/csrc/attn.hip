@@ -126,7 +126,7 @@ struct BfArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
     const int32_t *tau;
     uint16_t *out;
-    float *ws_o;    // split partials [split][batch][n_resp][Hq][D]
+    uint16_t *ws_o;  // split partials [split][batch][n_resp][Hq][D], unnormalised, bf16 (RNE)
     float2 *ws_ml;  // [split][batch][n_resp][Hq] (running max in log2 units, sum)
     int batch, block, prefix, n_qh, n_kvh, n_rb, n_split, tiles_per_split;
     int n_resp;  // response rows (and keys) per sequence: 2B, or copies * block
@@ -834,14 +834,19 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
                 }
         } else {
             const size_t prow = (size_t)split * a.batch * R2 * a.n_qh + row;
-            float *op = a.ws_o + prow * D + 4 * h;
+            // the merge weights are non-negative and sum to one over the
+            // splits, so rounding each partial to bf16 adds at most one
+            // bf16 rounding (2^-9 relative) to the merged row
+            uint16_t *op = a.ws_o + prow * D + 4 * h;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const f32x16 &o = st.oacc[qb][db];
-                    *reinterpret_cast<float4 *>(op + db * 32 + 8 * jj) =
-                        make_float4(o[4 * jj + 0], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]);
+                    uint2 pk;
+                    pk.x = pack_bf16x2(o[4 * jj + 0], o[4 * jj + 1]);
+                    pk.y = pack_bf16x2(o[4 * jj + 2], o[4 * jj + 3]);
+                    *reinterpret_cast<uint2 *>(op + db * 32 + 8 * jj) = pk;
                 }
             if (h == 0) a.ws_ml[prow] = make_float2(st.m_run[qb], l_tot);
         }
@@ -853,7 +858,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 // independent loads (unrolled, so many are in flight), and the 32 threads of
 // a row read the same (m, l) entries as one broadcast.
 template <typename T>
-__global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ ws_o,
+__global__ void __launch_bounds__(256) attn_combine_kernel(const uint16_t *__restrict__ ws_o,
                                                            const float2 *__restrict__ ws_ml, T *out,
                                                            int n_split, size_t rows_total, int d) {
     const int d4 = d >> 2;
@@ -870,7 +875,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
     for (int s = 0; s < n_split; ++s) {
         const float2 ml = ws_ml[s * rows_total + row];
         if (ml.x == -INFINITY) continue;  // no visible key in this split (or an empty split)
-        const float4 o = *reinterpret_cast<const float4 *>(ws_o + (s * rows_total + row) * d + e);
+        const uint2 pk = *reinterpret_cast<const uint2 *>(ws_o + (s * rows_total + row) * d + e);
+        const float4 o = make_float4(__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
+                                     __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u));
         const float f = __builtin_amdgcn_exp2f(ml.x - M);
         den += f * ml.y;
         num.x += f * o.x;
@@ -977,9 +984,9 @@ AttnPlan attn_plan(const AttnShape &s) {
     if (s.dtype == 1) {
         // aim for about one workgroup per compute unit (256 CUs) -- unless
         // a workgroup would stream only a few tiles anyway: at 9 tiles (a
-        // 512-key prompt) the merge launch and the float32 partials cost
+        // 512-key prompt) the merge launch and the partials cost
         // more than the idle compute units (24.7 us unsplit vs 26.4 us in
-        // three splits, batch 8)
+        // three splits with float32 partials, batch 8)
         const long units = (long)s.batch * s.n_kvh * p.n_rb;
         if (units < 256 && p.n_tiles > 12) {
             int want = (int)((256 + units - 1) / units);
@@ -991,7 +998,7 @@ AttnPlan attn_plan(const AttnShape &s) {
         }
         if (p.n_split > 1) {
             const size_t rows = (size_t)p.n_split * s.batch * s.n_resp * s.n_qh;
-            p.ws_partial_o = align_up(rows * s.head_dim * sizeof(float));
+            p.ws_partial_o = align_up(rows * s.head_dim * sizeof(uint16_t));
             p.ws_partial_ml = align_up(rows * sizeof(float2));
         }
     } else {
@@ -1044,7 +1051,7 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         a.v_cache = (const uint16_t *)v_cache;
         a.tau = tau;
         a.out = (uint16_t *)out;
-        a.ws_o = p.n_split > 1 ? (float *)ws : nullptr;
+        a.ws_o = p.n_split > 1 ? (uint16_t *)ws : nullptr;
         a.ws_ml = p.n_split > 1 ? (float2 *)((char *)ws + p.ws_partial_o) : nullptr;
         a.batch = s.batch;
         a.block = s.block;
@@ -1081,7 +1088,7 @@ hipError_t launch_attn(const AttnShape &s, const AttnPlan &p, const void *q, con
         const size_t rows_total = (size_t)s.batch * R2 * s.n_qh;
         const size_t threads = rows_total * (size_t)(s.head_dim / 4);
         hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           st, (const float *)a.ws_o, (const float2 *)a.ws_ml, (uint16_t *)out, p.n_split,
+                           st, (const uint16_t *)a.ws_o, (const float2 *)a.ws_ml, (uint16_t *)out, p.n_split,
                            rows_total, s.head_dim);
         return hipGetLastError();
     }

@@ -28,7 +28,7 @@ struct AttnPlan {
     int n_tiles;         // key tiles over prefix + n_resp keys (the longest prompt)
     int n_split;         // prefix splits (1 = no combine pass)
     int tiles_per_split;
-    size_t ws_partial_o;   // bytes of split partial outputs (float32)
+    size_t ws_partial_o;   // bytes of split partial outputs (bf16)
     size_t ws_partial_ml;  // bytes of split (max, sum) pairs
     size_t ws_rope;        // bytes of rotated q/k copies (float32 path)
     size_t ws_total;

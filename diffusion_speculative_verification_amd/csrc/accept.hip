@@ -10,7 +10,7 @@
 //   lse_partial_kernel   vocab-parallel softmax normaliser of every verified
 //                        slot: a streaming pass over the float32 target
 //                        logits (16-byte coalesced non-temporal loads -- the
-//                        logits are read once -- 4 in flight per lane),
+//                        logits are read once -- 8 in flight per lane),
 //                        per-lane running (max, sum) with the sum kept
 //                        in float64, merged per workgroup into one (m, s)
 //                        partial per (slot, vocab split).  The first split of
@@ -108,11 +108,14 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
         const int64_t n4 = vocab >> 2;
         const int64_t c0 = n4 * sp / n_vsplit, c1 = n4 * (sp + 1) / n_vsplit;
         const float4 *src = reinterpret_cast<const float4 *>(logits + (size_t)row * vocab);
-        for (int64_t i = c0 + tid; i < c1; i += 256 * 4) {
-            float4 x[4];
-            bool ok[4];
+        // 8 loads in flight per lane: the small and long-prompt workloads
+        // (few slots) are bound by dependent load rounds, which this halves
+        constexpr int U = 8;
+        for (int64_t i = c0 + tid; i < c1; i += 256 * U) {
+            float4 x[U];
+            bool ok[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < U; ++u) {
                 ok[u] = i + 256 * u < c1;
                 if (ok[u]) {
                     const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(src + i + 256 * u));
@@ -124,7 +127,7 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
             }
             float gm = m;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < U; ++u)
                 gm = fmaxf(gm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
             if (gm > m) {
                 if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - gm) * kLog2e);
@@ -134,15 +137,17 @@ __global__ void __launch_bounds__(256) lse_partial_kernel(const float *__restric
             // and so are the entries of this round: subtracting 0 instead
             // keeps exp(-inf - m) at 0 rather than NaN
             const float mu = (m == -INFINITY) ? 0.f : m;
-            float ps = 0.f;
+            // float32 partial sums of 16 terms each, added in float64
+            float ps[U / 4] = {};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ps += __builtin_amdgcn_exp2f((x[u].x - mu) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].y - mu) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].z - mu) * kLog2e);
-                ps += __builtin_amdgcn_exp2f((x[u].w - mu) * kLog2e);
+            for (int u = 0; u < U; ++u) {
+                ps[u / 4] += __builtin_amdgcn_exp2f((x[u].x - mu) * kLog2e);
+                ps[u / 4] += __builtin_amdgcn_exp2f((x[u].y - mu) * kLog2e);
+                ps[u / 4] += __builtin_amdgcn_exp2f((x[u].z - mu) * kLog2e);
+                ps[u / 4] += __builtin_amdgcn_exp2f((x[u].w - mu) * kLog2e);
             }
-            s += (double)ps;
+#pragma unroll
+            for (int k = 0; k < U / 4; ++k) s += (double)ps[k];
         }
     } else {
         const int64_t c0 = vocab * sp / n_vsplit, c1 = vocab * (sp + 1) / n_vsplit;

@@ -983,12 +983,12 @@ AttnPlan attn_plan(const AttnShape &s) {
     p.tiles_per_split = p.n_tiles;
     if (s.dtype == 1) {
         // aim for about one workgroup per compute unit (256 CUs) -- unless
-        // a workgroup would stream only a few tiles anyway: at 9 tiles (a
-        // 512-key prompt) the merge launch and the partials cost
-        // more than the idle compute units (24.7 us unsplit vs 26.4 us in
-        // three splits with float32 partials, batch 8)
+        // a workgroup would stream only a few tiles anyway, where the merge
+        // launch and the partials cost more than the idle compute units: 64
+        // units of 5 tiles (a 256-key prompt) take 19.1 us unsplit and 20.5
+        // split, of 7 tiles 22.0 and 20.2 us
         const long units = (long)s.batch * s.n_kvh * p.n_rb;
-        if (units < 256 && p.n_tiles > 12) {
+        if (units < 256 && p.n_tiles > 6) {
             int want = (int)((256 + units - 1) / units);
             want = want < p.n_tiles / 2 ? want : p.n_tiles / 2;
             if (want > 1) {

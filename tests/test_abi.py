@@ -1,7 +1,6 @@
 """The C-ABI library: it loads, exports every symbol the header declares, and
 its host-side argument checks return the documented status codes without
 touching a GPU (CPU only)."""
-import ctypes
 import os
 import re
 

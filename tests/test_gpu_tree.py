@@ -6,7 +6,6 @@ import numpy as np
 import pytest
 
 import oracle
-from diffusion_speculative_verification_amd import binding as sv
 from diffusion_speculative_verification_amd import synth
 
 pytestmark = pytest.mark.gpu

@@ -2,7 +2,6 @@
 and check that at least one pin fails for each: the pins would catch a
 dropped term, a wrong comparison, sign, index or operand order."""
 import os
-import shutil
 import subprocess
 
 import pytest

@@ -1,7 +1,6 @@
 """Plant plausible mistakes in copies of the oracle's C source (on the CPU)
 and check that at least one pin fails for each: the pins would catch a
 dropped term, a wrong comparison, sign, index or operand order."""
-import os
 import subprocess
 
 import pytest

@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(kWalkThreads) states_walk_kernel(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t b = blockIdx.x;
     const bool in_slot = lane < block;
-    if (threadIdx.x < n_nodes) par[threadIdx.x] = parent[b * n_nodes + threadIdx.x];
+    if ((int)threadIdx.x < n_nodes) par[threadIdx.x] = parent[b * n_nodes + threadIdx.x];
     // 1. per node (one wave each): confidences and the threshold rule, lane = slot
     for (int n = w; n < n_nodes; n += kWalkWaves) {
         const size_t row = ((size_t)b * n_nodes + n) * block + (in_slot ? lane : 0);

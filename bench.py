@@ -190,13 +190,16 @@ def oracle_agreement(o, inp, gamma, temperature, L_o, tok_o, al_o, rs_o, gpu) ->
 
 
 def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", rparam=0.0, copies=0,
-                 paged=False, tree=False, attn_budget_s=20.0, gpu_accept=None, threshold=1.0) -> dict:
+                 paged=False, tree=False, attn_budget_s=20.0, gpu_accept=None, threshold=1.0,
+                 gpu_attn=None) -> dict:
     """The CPU oracle on this host over the same workload (one step).  The
     attention is timed over the first sequences of the batch until
     `attn_budget_s` has passed and scaled to the whole batch.  With
     `gpu_accept` (the GPU's accept_len and out_tokens of the same inputs) the
     oracle's acceptance outputs are also compared with the GPU's
-    (oracle_agreement), outside the timed part."""
+    (oracle_agreement), and with `gpu_attn` (the GPU's attention output of
+    the same inputs, one entry per sequence) the oracle's attention rows of
+    the timed sequences are compared with it, both outside the timed part."""
     import oracle
     o = oracle.Oracle()
     threads = o.max_threads()
@@ -212,18 +215,21 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     t_route = time.perf_counter() - t
     t = time.perf_counter()
     n_seq = 0
+    attn_o = []
     for b in range(case.batch):
         if paged:
             sl = slice(b, b + 1)
-            o.attention_paged(inp["q"][sl], inp["k_new"][sl], inp["v_new"][sl], inp["k_pages"], inp["v_pages"],
+            ref = o.attention_paged(inp["q"][sl], inp["k_new"][sl], inp["v_new"][sl], inp["k_pages"], inp["v_pages"],
                               inp["block_table"][sl], inp["prefix_lens"][sl], inp["tau"][sl], case.page_size,
-                              case.theta)
+                              case.theta)[0]
         elif copies:
-            o.attention_copies(inp["q_c"][b], inp["k_new_c"][b], inp["v_new_c"][b], inp["k_cache"][b],
+            ref = o.attention_copies(inp["q_c"][b], inp["k_new_c"][b], inp["v_new_c"][b], inp["k_cache"][b],
                                inp["v_cache"][b], copies, case.theta)
         else:
-            o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
-                        inp["tau"][b], case.theta)
+            ref = o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b], inp["v_cache"][b],
+                              inp["tau"][b], case.theta)
+        if gpu_attn is not None:
+            attn_o.append(ref)
         n_seq += 1
         if time.perf_counter() - t > attn_budget_s:
             break
@@ -252,6 +258,17 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
     agreement = None
     if gpu_accept is not None and verify == "rejection" and not tree:
         agreement = oracle_agreement(o, inp, case.gamma, temperature, *acc_o, gpu_accept)
+    attn_agreement = None
+    if gpu_attn is not None:
+        import numpy as np
+        mx = err2 = ref2 = 0.0
+        for b, ref in enumerate(attn_o):
+            d = gpu_attn[b].astype(np.float64) - ref
+            mx = max(mx, float(np.abs(d).max()))
+            err2 += float((d * d).sum())
+            ref2 += float((ref * ref).sum())
+        attn_agreement = {"sequences": n_seq, "max_abs_err": mx,
+                          "rel_rms_err": (err2 / ref2) ** 0.5 if ref2 > 0 else 0.0}
     attn_what = (f"attention {t_attn:.2f} s" if n_seq == case.batch else
                  f"attention {t_attn:.2f} s (timed on {n_seq} of {case.batch} sequences, scaled)")
     return {"value": case.batch * case.gamma / total, "unit": "slots/s", "cores": threads, "kind": "oracle",
@@ -262,7 +279,7 @@ def cpu_baseline(case, inp, verify="rejection", temperature=1.0, route="none", r
                       + (f" + commit and append {t_commit:.2f} s" if paged else "") +
                       f" on {threads} OpenMP threads "
                       f"(host reports {os.cpu_count()} CPUs); input generation excluded",
-            "agreement": agreement}
+            "agreement": agreement, "attn_agreement": attn_agreement}
 
 
 def measured_peaks(torch, keep: list) -> dict:
@@ -606,8 +623,10 @@ def main():
         if verify == "rejection" and not tree and not paged:
             # the GPU's outputs of the inputs in `inp` (every input set holds them)
             gpu_acc = (sets[0].accept_len.cpu().numpy(), sets[0].out_tokens.cpu().numpy())
+        # the GPU's attention output of the same inputs
+        gpu_out = sets[0].out_c if copies else sets[0].out_paged if paged else sets[0].out
         cpu = cpu_baseline(case, inp, verify, T, route, rparam, copies, paged, tree, gpu_accept=gpu_acc,
-                           threshold=case.threshold)
+                           threshold=case.threshold, gpu_attn=gpu_out.float().cpu().numpy())
 
     out = {
         "metric": METRIC,
@@ -666,6 +685,9 @@ def main():
             # acceptance outputs of the GPU against the oracle on the same inputs
             # (counted ties are decisions within 1e-6 of their threshold)
             "oracle_agreement": cpu["agreement"] if cpu else None,
+            # attention rows of the oracle's timed sequences against the GPU's
+            # (max abs and relative RMS error)
+            "attn_oracle_agreement": cpu["attn_agreement"] if cpu else None,
         },
     }
     print(json.dumps(out))

@@ -77,3 +77,22 @@ def test_refusals_before_gpu_work(argv, needle):
     assert r.returncode == 2
     assert needle in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_attention_agreement():
+    """The CPU leg's attention comparison: zero against the oracle's own rows,
+    and the planted error's size when one element is moved."""
+    import oracle
+    c = synth.config_by_name("tiny")
+    inp = synth.make_inputs(c, parts=("attn", "accept"))
+    o = oracle.Oracle()
+    ref = np.stack([o.attention(inp["q"][b], inp["k_new"][b], inp["v_new"][b], inp["k_cache"][b],
+                                inp["v_cache"][b], inp["tau"][b], c.theta) for b in range(c.batch)])
+    same = bench.cpu_baseline(c, inp, gpu_attn=ref.copy())
+    assert same["attn_agreement"] == {"sequences": c.batch, "max_abs_err": 0.0, "rel_rms_err": 0.0}
+    moved = ref.copy()
+    moved[c.batch - 1, 3, 1, 2] += 0.25
+    got = bench.cpu_baseline(c, inp, gpu_attn=moved)["attn_agreement"]
+    assert abs(got["max_abs_err"] - 0.25) < 1e-12
+    assert abs(got["rel_rms_err"] - 0.25 / np.linalg.norm(ref)) < 1e-12
+    assert bench.cpu_baseline(c, inp)["attn_agreement"] is None

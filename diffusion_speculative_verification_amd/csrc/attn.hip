@@ -370,10 +370,41 @@ __device__ __forceinline__ int2 map_row(int rho, int R2, int B, int g) {
 
 template <int QB>
 struct RowInfo {
-    int t_row[QB];     // step label of each row's slot (copies: the row's copy)
-    bool is_data[QB];  // D row (true) or D~ row
-    int c_lo, c_hi;    // copies: the range of copies this wave's rows belong to
+    // paired layout: the row's label threshold, the step label of its slot
+    // plus one for a D row (clamped to 0 .. B + 1); a D key is visible to the
+    // row iff its label is below the threshold, a D~ key iff it is not.
+    // Copies: the row's copy.
+    int lab[QB];
+    int c_lo, c_hi;  // copies: the range of copies this wave's rows belong to
 };
+
+// Bits of a 64-key window of a row's keys: bit j is the visibility of response
+// key off + j.  m0 / m1 hold the visibility of response keys 0..63 / 64..127;
+// keys before the first response key are prompt keys (visible), keys from 128
+// on are padding (hidden).  off lies in -63 .. 131.
+__device__ __forceinline__ uint64_t key_window(int off, uint64_t m0, uint64_t m1) {
+    const int q = off >> 6, r = off & 63;  // q in -1 .. 2
+    const uint64_t lo = q < 0 ? ~0ull : q == 0 ? m0 : q == 1 ? m1 : 0ull;
+    const uint64_t hi = q < 0 ? m0 : q == 0 ? m1 : 0ull;
+    return r == 0 ? lo : ((lo >> r) | (hi << (64 - r)));
+}
+
+// the n lowest bits, n in 0 .. 64
+__device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : (1ull << n) - 1; }
+
+// max of x over lanes l and l ^ 32.  The 8-wave kernel exchanges the two
+// 32-lane halves with v_permlane32_swap, a VALU op (no LDS round trip queued
+// behind the tile reads; each lane ends with its own value and its peer's);
+// the 4-wave kernel keeps the LDS permute, which measured faster there.
+template <int NW>
+__device__ __forceinline__ float pair_max(float x) {
+    if constexpr (NW == 8) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    } else {
+        return fmaxf(x, __shfl_xor(x, 32));
+    }
+}
 
 // Loop-invariant LDS byte offsets of this lane's MFMA operand reads.  The
 // K swizzle depends on row & 15 and the V swizzle on row & 3 only, and each
@@ -428,7 +459,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                                           const RowInfo<QB> &ri, const LdsOffs<D> &lo_, const bf16x8 (*qop)[D / 16],
                                           RowState<D, QB> &st, char *__restrict__ kt, char *__restrict__ vt,
                                           char *__restrict__ kn, char *__restrict__ vn,
-                                          const float2 *__restrict__ cs, const int *__restrict__ klab,
+                                          const float2 *__restrict__ cs, const uint64_t *__restrict__ below,
                                           const char *v_stage0, const LoadOffs<D, NW> &ldo, size_t unit_off,
                                           const TileMap<MASK> &tm, int jend) {
     using T = Tile<D, false>;
@@ -518,26 +549,33 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                 sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][s], sacc[qb][kb], 0, 0, 0);
         }
     }
-    // ---- temporal-causal mask, only where response / padding keys occur;
-    // klab[c] = (step label << 1) | is_data of response key c, and -1 past
-    // the last response key
+    // ---- temporal-causal mask, only where response / padding keys occur.
+    // This lane's 32 scores belong to response keys off + j (negative: prompt
+    // keys), j = 32 kb + 8 (x >> 2) + (x & 3) < 64, so one 64-bit window of
+    // the row's key visibility covers them.
     if (base + kTileKeys > P) {
+        const int off = base - P + 4 * h;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int c = base + kb * 32 + 8 * (x >> 2) + 4 * h + (x & 3) - P;  // < 0: prompt key
-                const int lab = klab[max(0, min(c, MASK == 0 ? 2 * kMaxBlock : kMaxResp))];
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    // bitwise, so that the select stays a select (no branches);
-                    // copies: a key is visible to the rows of its own copy
-                    const bool vis = MASK == 0
-                        ? ((c < 0) | ((lab >= 0) & visible(ri.t_row[qb], ri.is_data[qb], lab >> 1, lab & 1)))
-                        : ((c < 0) | (lab == ri.t_row[qb]));
-                    sacc[qb][kb][x] = vis ? sacc[qb][kb][x] : -INFINITY;
-                }
+        for (int qb = 0; qb < QB; ++qb) {
+            uint64_t win;
+            if constexpr (MASK == 0) {
+                // response keys 0..B-1 are D keys, B..2B-1 their D~ keys
+                const uint64_t dk = below[ri.lab[qb]];
+                const uint64_t mk = ~dk & low_bits(B);
+                win = key_window(off, B == 64 ? dk : (dk | (mk << B)), B == 64 ? mk : (mk >> (64 - B)));
+            } else {
+                // copies: the prompt keys and the keys of the row's own copy
+                const int k0 = ri.lab[qb] * B - off;
+                win = low_bits(min(max(-off, 0), 64)) |
+                      (low_bits(min(max(k0 + B, 0), 64)) & ~low_bits(min(max(k0, 0), 64)));
             }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int j = 32 * kb + 8 * (x >> 2) + (x & 3);
+                    sacc[qb][kb][x] = ((win >> j) & 1) ? sacc[qb][kb][x] : -INFINITY;
+                }
         }
     }
     // ---- online softmax (log2 domain); each lane owns its queries' scores
@@ -551,7 +589,7 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[qb][kb][x]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair_max<NW>(mx);
         // lazy rescale: the running max moves only when the tile max exceeds
         // it by more than 8 (log2 units); otherwise P = 2^(s - m_run) <= 2^8
         // and the accumulators keep their scale (exact after normalisation)
@@ -628,10 +666,9 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
                                          uint4 (*raw)[D / 16], const bool *rvalid, const int *pos_idx,
                                          bf16x8 (*qop)[D / 16], char *__restrict__ k0, char *__restrict__ v0,
                                          char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
-                                         double *__restrict__ invf, int *__restrict__ klab) {
+                                         double *__restrict__ invf, uint64_t *__restrict__ below) {
     constexpr int NS = D / 16, NTH = 64 * NW;
     // one thread per entry of the paired layout's key-label table below
-    static_assert(NTH > 2 * kMaxBlock, "the key-label table needs 2 * kMaxBlock + 1 threads");
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)
@@ -648,12 +685,12 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
         }
     }
     if constexpr (MASK == 0) {
-        // key labels of the 2B response keys: (tau << 1) | is_data; -1 past them
-        const int tk = __shfl(tau_v, tid % B);  // tau of slot tid mod B
-        if (tid <= 2 * kMaxBlock) klab[tid] = (tid < 2 * B) ? ((tk << 1) | (tid < B ? 1 : 0)) : -1;
-    } else {
-        // copies: the copy index of each response key; -1 past them
-        for (int c = tid; c <= kMaxResp; c += NTH) klab[c] = (c < a.n_resp) ? c / B : -1;
+        // below[t]: the slots whose step label is below t, one bit per slot
+        // (lane k < B of every wave holds the label of slot k)
+        for (int t = w; t <= B + 1; t += NW) {
+            const uint64_t bits = __ballot(lane < B && tau_v < t);
+            if (lane == 0) below[t] = bits;
+        }
     }
     ring_barrier();
 #pragma unroll
@@ -687,7 +724,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     __shared__ __attribute__((aligned(1024))) char v_st0[T::BYTES], v_st1[T::BYTES], v_st2[T::BYTES];
     __shared__ __attribute__((aligned(16))) float2 cs_lds[kMaxBlock * kCsStride<D>];
     __shared__ double invf_lds[D / 2];
-    __shared__ int klab_lds[kMaxResp + 1];
+    __shared__ uint64_t below_lds[MASK == 0 ? kMaxBlock + 2 : 1];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int B = a.block, R2 = a.n_resp, g = a.n_qh / a.n_kvh, R = g * R2;
@@ -760,17 +797,14 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
     const int jend = min(a.prefix + R2, (tm(t1 - 1) + 1) * kTileKeys);  // end of this workgroup's keys
     bf16x8 qop[QB][NS];
     prologue<D, NW, QB, MASK, NT>(a, b, kvh, t0, tm, jend, tau_v, raw, rvalid, pos_idx, qop, k_st0, v_st0, k_st1, v_st1, cs_lds,
-                        invf_lds, klab_lds);
+                        invf_lds, below_lds);
     RowInfo<QB> ri;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        if constexpr (MASK == 0) {
-            ri.t_row[qb] = __shfl(tau_v, pos_idx[qb]);
-            ri.is_data[qb] = rrow[qb] < B;
-        } else {
-            ri.t_row[qb] = rrow[qb] / B;  // the row's copy
-            ri.is_data[qb] = false;
-        }
+        if constexpr (MASK == 0)
+            ri.lab[qb] = min(max(__shfl(tau_v, pos_idx[qb]), 0), B) + (rrow[qb] < B ? 1 : 0);
+        else
+            ri.lab[qb] = rrow[qb] / B;  // the row's copy
     }
     ri.c_lo = 0;
     ri.c_hi = R2 / B - 1;
@@ -802,13 +836,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bf16_kernel(BfArgs a) {
 
     for (int it = 0; it < nt; it += 3) {
         tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it, wave_active, ri, offs, qop, st, k_st0, v_st0, k_st2, v_st2,
-                             cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
+                             cs_lds, below_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 1 < nt)
             tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it + 1, wave_active, ri, offs, qop, st, k_st1, v_st1, k_st0,
-                                 v_st0, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
+                                 v_st0, cs_lds, below_lds, v_st0, ldo, unit_off, tm, jend);
         if (it + 2 < nt)
             tile_step<D, NW, QB, MASK, NT>(a, b, kvh, t0, nt, it + 2, wave_active, ri, offs, qop, st, k_st2, v_st2, k_st1,
-                                 v_st1, cs_lds, klab_lds, v_st0, ldo, unit_off, tm, jend);
+                                 v_st1, cs_lds, below_lds, v_st0, ldo, unit_off, tm, jend);
     }
     wait_vmcnt<0>();  // no direct load may still target this workgroup's LDS when it exits
 

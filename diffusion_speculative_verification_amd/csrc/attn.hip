@@ -25,9 +25,12 @@
 //     XOR-swizzled for the 64-bank LDS;
 //   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on MFMA rows, queries
 //     on columns): each lane then owns one query's scores, so the row
-//     max/sum need one cross-lane exchange (lane ^ 32) per tile;
-//   - the mask is evaluated in registers from the step labels, only on
-//     tiles that reach the response keys; prompt tiles take the unmasked path;
+//     max/sum need one cross-lane exchange (lane ^ 32) per tile; in the
+//     8-wave kernel the K operand reads run four MFMAs ahead;
+//   - the mask is evaluated in registers, only on tiles that reach the
+//     response keys (prompt tiles take the unmasked path): each row holds a
+//     64-key window of its key visibility built from the step labels, one
+//     bit test per score;
 //   - online softmax in the log2 domain, P rounded to bf16 and fed straight
 //     from the S^T accumulators as the B operand of O^T = V^T P^T (same lane
 //     ownership, no shuffle); V^T comes from the row-major V tile through
@@ -44,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -538,16 +543,42 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // refill load i goes out after S MFMA i * KSTEP + 1 of the 2 * NS: all
     // 2 * NL of them only when KSTEP divides evenly and is at least 2
     static_assert(NS % NL == 0 && KSTEP >= 2, "every refill load must be issued between the S MFMAs");
+    auto s_phase = [&](auto with_refill) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+        for (int s = 0; s < NS; ++s) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (prompt_refill && (2 * s + kb) % KSTEP == 1) refill((2 * s + kb) / KSTEP);
-            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + lo_.k[s] + kb * 32 * T::ROW_BYTES);
+            for (int kb = 0; kb < 2; ++kb) {
+                if (with_refill && (2 * s + kb) % KSTEP == 1) refill((2 * s + kb) / KSTEP);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + lo_.k[s] + kb * 32 * T::ROW_BYTES);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][s], sacc[qb][kb], 0, 0, 0);
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[qb][s], sacc[qb][kb], 0, 0, 0);
+            }
         }
+        if constexpr (NW == 8 && QB == 1) {
+            // each K operand read issued four MFMAs ahead of its use (masks:
+            // 0x100 LDS reads, 0x008 MFMAs)
+            constexpr int kAhead = 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NS - kAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        }
+    };
+    // The 8-wave kernel picks the version with or without refill loads once,
+    // so that each is a single basic block over which the reads above can be
+    // scheduled ahead; the 4-wave kernel, faster with the plain loop by
+    // measurement, tests the condition at each load.
+    if constexpr (NW == 8) {
+        if (prompt_refill)
+            s_phase(std::true_type{});
+        else
+            s_phase(std::false_type{});
+    } else {
+        s_phase(prompt_refill);
     }
     // ---- temporal-causal mask, only where response / padding keys occur.
     // This lane's 32 scores belong to response keys off + j (negative: prompt

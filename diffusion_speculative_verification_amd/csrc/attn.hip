@@ -609,6 +609,19 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
                 }
         }
     }
+    // ---- the V^T operands of the first PV k-step, read before the softmax so
+    // that their LDS latency passes under it (layout: see the PV product)
+    const uint32_t vt_off = (uint32_t)(vt - v_stage0);  // 0, 1 or 2 tile sizes
+    auto vt_operand = [&](int s, int db) {
+        const uint32_t o0 = lo_.v[db] + vt_off + 16 * s * T::ROW_BYTES;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)o0);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)(o0 + 8 * T::ROW_BYTES));
+        const v4i16 cat[2] = {lo, hi};
+        return __builtin_bit_cast(bf16x8, cat);
+    };
+    bf16x8 va0[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) va0[db] = vt_operand(0, db);
     // ---- online softmax (log2 domain); each lane owns its queries' scores
     bf16x8 pop[QB][4];
     bool rescale = false;
@@ -666,17 +679,11 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
     // row-major V tile through the transposing LDS read: in 16-lane group gq,
     // lane j = 4k + c reads row key(k) at dims dim0 + 4c, and lane i receives
     // the four keys of dim dim0 + i.
-    const uint32_t vt_off = (uint32_t)(vt - v_stage0);  // 0, 1 or 2 tile sizes
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const uint32_t o0 = lo_.v[db] + vt_off + 16 * s * T::ROW_BYTES;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)o0);
-            const v4i16 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((SV_LDS v4i16 *)(uintptr_t)(o0 + 8 * T::ROW_BYTES));
-            const v4i16 cat[2] = {lo, hi};
-            const bf16x8 va = __builtin_bit_cast(bf16x8, cat);
+            const bf16x8 va = s == 0 ? va0[db] : vt_operand(s, db);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qb][s], st.oacc[qb][db], 0, 0, 0);
@@ -685,8 +692,8 @@ __device__ __forceinline__ void tile_step(const BfArgs &a, int b, int kvh, int t
 }
 
 // Prologue: start the first tile's direct loads, build the RoPE table while
-// they and the query loads are in flight, then the key-label table (which
-// needs tau), rotate this lane's query rows, and only then start the second
+// they and the query loads are in flight, then the label-threshold table
+// (which needs tau), rotate this lane's query rows, and only then start the second
 // tile.  The compiler cannot see the direct loads, so its wait for the query
 // registers is a full vmcnt(0): issuing the second tile after that wait
 // keeps it out of the chip-wide burst that every workgroup waits on before
@@ -699,7 +706,6 @@ __device__ __forceinline__ void prologue(const BfArgs &a, int b, int kvh, int t0
                                          char *__restrict__ k1, char *__restrict__ v1, float2 *__restrict__ cs,
                                          double *__restrict__ invf, uint64_t *__restrict__ below) {
     constexpr int NS = D / 16, NTH = 64 * NW;
-    // one thread per entry of the paired layout's key-label table below
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int B = a.block, P = a.prefix;
     // the first tile (every split has at least one)

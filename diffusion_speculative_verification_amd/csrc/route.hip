@@ -152,12 +152,15 @@ __global__ void __launch_bounds__(64) route_scan_kernel(const int32_t *__restric
     if (lane == 0) khat[b] = (float)sum;
 }
 
+// Vocabulary parts per verified row, as for the normaliser pass: about 2048
+// workgroups, no part shorter than 32768 entries (128 verified rows at
+// vocabulary 151936: 4 parts, 18.5 us per call against 20.3 us with 9).
 RoutePlan route_plan(int batch, int block, int gamma, int64_t vocab) {
     RoutePlan p{};
     p.rows = batch * block;
     const long active = (long)batch * gamma;
     long vs = (2048 + active - 1) / active;
-    long cap = vocab / 16384;
+    long cap = vocab / 32768;
     if (cap < 1) cap = 1;
     if (vs > cap) vs = cap;
     if (vs < 1) vs = 1;
